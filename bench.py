@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the submanifold 3x3x3 convolution on one MI355X.
+
+One step = the whole path on one synthetic batch: build the neighbour map of
+the coordinate set (pack, radix sort, resolve, status read-back), then run the
+forward pass on it (4 forward passes reusing the map for the 4-grid workload).
+Inputs are resident in device memory before the timed region starts.
+
+Prints ONE JSON line.  `value` is forward active voxels per second (N divided
+by the mean forward kernel time from HIP events on the launch stream);
+`ms_per_step` is the wall time of a whole step (map build + forward).
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--dtype f32|bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SubMConv3d fwd active-voxels/s + TFLOP/s at 128^3/128ch; map-build ms"
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+CONV_SRC = os.path.join(ROOT, "submanifold_sparse_convolution_submconv3d_amd", "csrc", "conv.hip")
+MAP_SRCS = [os.path.join(ROOT, "submanifold_sparse_convolution_submconv3d_amd", "csrc", f)
+            for f in ("mapbuild.hip", "sort_scan.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+BOUND = {1: "hbm", 2: "mfma", 3: "mfma", 4: "mfma", 5: "hbm"}
+
+
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, dtype: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = data.get("%s/%s/%s" % (workload, dtype, kernel))
+    if not entry:
+        return None
+    srcs = [CONV_SRC] if kernel == "forward" else MAP_SRCS
+    if entry.get("source_hash") != src_hash(srcs):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def algorithmic(n, p, cin, cout, dtype):
+    s = 4 if dtype == "f32" else 2
+    flops = 2.0 * cin * cout * p
+    bytes_ = n * (cin * s + cout * s + 27 * 4) + 27 * cin * cout * s + 4 * cout
+    return flops, float(bytes_)
+
+
+def cpu_baseline(coords, feats, weight, bias, res, batch, budget_s):
+    """The oracle (C, dense volume, fp64) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+
+    oracle.build_oracle(force=False)
+    t0 = time.perf_counter()
+    nbr = oracle.dense.neighbor_table(coords, res, batch)
+    t_map = time.perf_counter() - t0
+    n = len(coords)
+    f64, w64 = feats.astype(np.float64), weight.astype(np.float64)
+    probe = min(n, 256)
+    t0 = time.perf_counter()
+    oracle.dense.forward(f64, w64, bias, nbr, rows=(0, probe))
+    per_row = max((time.perf_counter() - t0) / probe, 1e-9)
+    rows = int(min(n, max(probe, (budget_s - t_map) / per_row)))
+    t0 = time.perf_counter()
+    oracle.dense.forward(f64, w64, bias, nbr, rows=(0, rows))
+    t_fwd = time.perf_counter() - t0
+    return {
+        "value": rows / t_fwd, "unit": "voxels/s", "cores": oracle.dense.num_threads(), "kind": "oracle",
+        "sample": "C dense-volume oracle, fp64: neighbour table of all %d voxels (%.2f s), forward of the "
+                  "first %d rows (%.2f s)" % (n, t_map, rows, t_fwd),
+        "map_build_s": t_map,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--dtype", default=None, choices=[None, "f32", "bf16"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "generic", "lowc", "mfma"])
+    ap.add_argument("--shuffled", action="store_true", help="seeded random row order")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the second dtype and the cold-cache pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import submanifold_sparse_convolution_submconv3d_amd as sc
+
+    variant = {"auto": sc.KERNEL_AUTO, "generic": sc.KERNEL_GENERIC, "lowc": sc.KERNEL_LOWC,
+               "mfma": sc.KERNEL_MFMA}[args.variant]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sc.load_library()
+    w, coords = synth.workload(args.config)
+    dtype = args.dtype or w.dtypes[0]
+    subdivide_ms = None
+    if w.subdivide_parent:                       # the set is the device subdivision of the parent shell
+        parent = torch.from_numpy(coords).to(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kids, _ = sc.submconv_subdivide(parent)
+        e1.record()
+        torch.cuda.synchronize()
+        subdivide_ms = e0.elapsed_time(e1)
+        tc = kids
+        coords = kids.cpu().numpy()
+    else:
+        tc = torch.from_numpy(coords).to(dev)
+    n = len(coords)
+    feats, weight, bias = synth.make_values(n, w.cin, w.cout, w.value_seed, w.weight_std, w.bias)
+    if args.shuffled:
+        p = synth.shuffle_rows(n, 1000 + args.config)
+        coords, feats = np.ascontiguousarray(coords[p]), np.ascontiguousarray(feats[p])
+        tc = torch.from_numpy(coords).to(dev)
+
+    def dev_values(dt):
+        if dt == "f32":
+            return torch.from_numpy(feats).to(dev), torch.from_numpy(weight).to(dev)
+        fb, wb = synth.bf16_bits(feats), synth.bf16_bits(weight)
+        return (torch.from_numpy(fb.view(np.int16)).view(torch.bfloat16).to(dev),
+                torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(dev).reshape(weight.shape))
+
+    tb = torch.from_numpy(bias).to(dev)
+    reps = 4 if args.config == 4 else 1
+    stream = torch.cuda.current_stream()
+
+    def run(dt, steps, warmup, flush=None):
+        tf, tw = dev_values(dt)
+        out = torch.empty((n, w.cout), dtype=tf.dtype, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + reps)] for _ in range(steps)]
+        taps = None
+        for _ in range(warmup):
+            rb = sc.submconv_build_map(tc, w.res, w.batch)
+            for _ in range(reps):
+                sc.submconv_forward(tf, tw, tb, rb, out=out, variant=variant)
+            taps = rb.taps_present
+            rb.free()
+        torch.cuda.synchronize()
+        wall = 0.0
+        for s in range(steps):
+            if flush is not None:
+                flush.fill_(s)                 # evict caches (outside the timed events and wall time)
+                torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e = ev[s]
+            e[0].record(stream)
+            rb = sc.submconv_build_map(tc, w.res, w.batch)
+            e[1].record(stream)
+            for r in range(reps):
+                sc.submconv_forward(tf, tw, tb, rb, out=out, variant=variant)
+                e[2 + r].record(stream)
+            taps = rb.taps_present
+            rb.free()
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+        t_map = [e[0].elapsed_time(e[1]) for e in ev]
+        t_fwd = [e[1 + r].elapsed_time(e[2 + r]) for e in ev for r in range(reps)]
+        return dict(t_map=t_map, t_fwd=t_fwd, wall_ms=wall * 1e3 / steps, taps=taps, out=out)
+
+    torch.cuda.synchronize()
+    res = run(dtype, args.steps, args.warmup)
+    p = res["taps"]
+    fwd_ms = float(np.mean(res["t_fwd"]))
+    map_ms = float(np.mean(res["t_map"]))
+    flops, abytes = algorithmic(n, p, w.cin, w.cout, dtype)
+    bound = BOUND[args.config]
+    if bound == "mfma":
+        achieved, peak, unit = flops / (fwd_ms * 1e-3) / 1e12, PEAK_TFLOPS[dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = abytes / (fwd_ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+    kname = "forward"
+    traffic = load_traffic(w.name + ("_shuffled" if args.shuffled else ""), dtype, kname)
+    rec = {
+        "metric": METRIC,
+        "value": n / (fwd_ms * 1e-3),
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["wall_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "grid": "%d^3" % w.res, "batch": w.batch, "n_voxels": n, "taps_present": p,
+            "cin": w.cin, "cout": w.cout, "geometry": w.note,
+            "row_order": "seeded shuffle" if args.shuffled else ("parent-major subdivide" if w.subdivide_parent
+                                                                   else "C order"),
+            "forward_calls_per_step": reps, "kernel": args.variant,
+        },
+        "fwd_ms": fwd_ms,
+        "fwd_ms_min": float(np.min(res["t_fwd"])),
+        "fwd_tflops": flops / (fwd_ms * 1e-3) / 1e12,
+        "fwd_tflops_dense27": 2.0 * w.cin * w.cout * 27 * n / (fwd_ms * 1e-3) / 1e12,
+        "fwd_algorithmic_GBps": abytes / (fwd_ms * 1e-3) / 1e9,
+        "map_build_ms": map_ms,
+        "map_build_ms_min": float(np.min(res["t_map"])),
+        "map_algorithmic_GBps": n * 124.0 / (map_ms * 1e-3) / 1e9,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": traffic, "kernel": "forward (%s)" % args.variant,
+                     "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
+    }
+    if subdivide_ms is not None:
+        rec["subdivide_ms"] = subdivide_ms
+    if not args.no_extra:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB > 4x the 256 MB MALL
+        cold = run(dtype, max(3, args.steps // 4), 1, flush)
+        cf = float(np.mean(cold["t_fwd"]))
+        rec["cold"] = {"fwd_ms": cf, "map_build_ms": float(np.mean(cold["t_map"])),
+                       "voxels_per_s": n / (cf * 1e-3), "fwd_tflops": flops / (cf * 1e-3) / 1e12,
+                       "fwd_algorithmic_GBps": abytes / (cf * 1e-3) / 1e9}
+        del flush
+        for other in w.dtypes:
+            if other == dtype:
+                continue
+            o = run(other, args.steps, args.warmup)
+            of = float(np.mean(o["t_fwd"]))
+            ofl, oby = algorithmic(n, p, w.cin, w.cout, other)
+            rec[other] = {"fwd_ms": of, "voxels_per_s": n / (of * 1e-3), "fwd_tflops": ofl / (of * 1e-3) / 1e12,
+                          "map_build_ms": float(np.mean(o["t_map"])),
+                          "roofline": {"bound": "mfma", "achieved": ofl / (of * 1e-3) / 1e12,
+                                       "peak": PEAK_TFLOPS[other], "unit": "TFLOP/s",
+                                       "frac": ofl / (of * 1e-3) / 1e12 / PEAK_TFLOPS[other],
+                                       "hbm_frac": oby / (of * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+    if args.no_cpu_baseline:
+        rec["cpu_baseline"] = None
+    else:
+        rec["cpu_baseline"] = cpu_baseline(coords, feats, weight, bias, w.res, w.batch, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,193 @@
+/*
+ * submconv.h -- C ABI of the MI355X (gfx950) submanifold 3x3x3 sparse
+ * convolution library (SubMConv3d).
+ *
+ * The operation (lato.2_mrp_mlx working notes, commit summary and section
+ * "Key facts"): a sparse tensor is a set of N active voxels with integer
+ * coordinates (b, z, y, x) and a feature row each.  The submanifold
+ * convolution keeps the output set equal to the input set (stride 1, no
+ * dilation of the set) and computes, for every active voxel i,
+ *
+ *     out[i] = bias + sum over the 27 offsets d in {-1,0,1}^3 of W[d] . feats[j]
+ *
+ * where j is the active voxel at coords[i] + d in the same batch entry (taps
+ * with no active voxel there contribute nothing).  Weights use the KRSC layout
+ * [Cout, kz, ky, kx, Cin] of the upstream sparse library.  The neighbour lookup
+ * is done once per coordinate set and reused by every convolution on that set
+ * (same page, commit summary: a map cached per coordinate set).
+ *
+ * Conventions fixed here where the pages are silent:
+ *   - tap k <-> offset (dz, dy, dx) = (k/9 - 1, (k/3)%3 - 1, k%3 - 1), i.e. C
+ *     order over the kernel's (kz, ky, kx); kernel axis a pairs with coordinate
+ *     column a+1; k = 13 is the centre.
+ *   - orientation: correlation by default (the neighbour at c + d is weighted by
+ *     W[kz,ky,kx] with (kz,ky,kx) = d + 1); flip = 1 selects the mirrored kernel,
+ *     W at 1 - d (the pages leave the orientation open, "Unresolved" section).
+ *   - neighbours outside [0, res)^3 or in another batch entry do not exist.
+ *
+ * Memory: every tensor pointer is a DEVICE pointer owned by the caller unless
+ * stated otherwise; rows are contiguous, row-major.  A rulebook and its device
+ * memory are owned by the library from submconv_build_map until
+ * submconv_rulebook_free.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = null stream).  All
+ * work is enqueued on it.  Only calls that must return a device-computed value
+ * (build_map's validity status, output row counts) synchronise that stream.
+ *
+ * Errors: every call returns a status (0 = success, < 0 = error); no call aborts
+ * or throws.  Host-side argument checks run before any HIP call.
+ * submconv_status_string names a status; submconv_last_error gives the detail
+ * of the last failure on the calling thread.
+ */
+#ifndef SUBMCONV_H
+#define SUBMCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SUBMCONV_OK 0
+#define SUBMCONV_E_INVALID_ARG (-1) /* null pointer, bad size, misaligned pointer, ... */
+#define SUBMCONV_E_COORD_RANGE (-2) /* a coordinate outside [0,res) or batch outside [0,batch) */
+#define SUBMCONV_E_DUPLICATE (-3)   /* two rows with the same (b, z, y, x) */
+#define SUBMCONV_E_UNSUPPORTED (-4) /* channel count / dtype / grid size not supported */
+#define SUBMCONV_E_ALIAS (-5)       /* an output buffer overlaps an input buffer */
+#define SUBMCONV_E_OOM (-6)         /* device allocation failed */
+#define SUBMCONV_E_HIP (-7)         /* a HIP runtime call or kernel launch failed */
+
+/* Element types of feature, weight and output tensors (bias is always fp32). */
+#define SUBMCONV_F32 0
+#define SUBMCONV_BF16 1
+
+/* Forward kernel selection (submconv_forward_variant). */
+#define SUBMCONV_KERNEL_AUTO 0    /* pick by (Cin, Cout, dtype) */
+#define SUBMCONV_KERNEL_GENERIC 1 /* one thread per output element, any channel counts */
+#define SUBMCONV_KERNEL_LOWC 2    /* narrow channels (<= 32), wave shuffles, no matrix cores */
+#define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128} */
+
+typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
+
+/*
+ * Build the neighbour map ("rulebook") of a coordinate set.
+ *
+ *   coords : device int32 [n,4], rows (b, z, y, x), 16-byte aligned; any row order.
+ *   n      : number of rows, 0 <= n < 2^31 (n = 0 gives an empty rulebook).
+ *   res    : grid extent per spatial axis (cubic grid), 1 <= res.
+ *   batch  : number of batch entries; every b must satisfy 0 <= b < batch.
+ *            (3 * bits(res-1) + bits(batch-1) must not exceed 64.)
+ *   stream : hipStream_t.
+ *   out_rb : receives the rulebook on success, NULL on failure.
+ *
+ * The table computed is nbr int32 [n,27]: nbr[i,k] = row of the voxel at
+ * coords[i] + offset(k), or -1.  It is exact (integer work).  Synchronises
+ * `stream` once to read the validity status: E_COORD_RANGE if a coordinate is
+ * out of range, E_DUPLICATE if two rows are equal (no rulebook is returned).
+ * Device memory is taken from the device's stream-ordered pool.
+ */
+int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t batch,
+                       void *stream, submconv_rulebook **out_rb);
+
+/* Device pointer to the rulebook's nbr table int32 [n,27] (owned by the
+ * rulebook, valid until it is freed) and its row count. */
+int submconv_rulebook_neighbors(const submconv_rulebook *rb, const int32_t **nbr, int64_t *n);
+
+/* Copy the rulebook's nbr table into caller memory dst (device int32 [n,27]),
+ * enqueued on `stream`. */
+int submconv_rulebook_copy_neighbors(const submconv_rulebook *rb, int32_t *dst, void *stream);
+
+/* Host-side facts of a rulebook: rows, grid, batch count, and P = number of
+ * entries of nbr that are not -1 (centre taps included). */
+int submconv_rulebook_info(const submconv_rulebook *rb, int64_t *n, int32_t *res, int32_t *batch,
+                           int64_t *taps_present);
+
+/* Release a rulebook; its memory returns to the pool in order on `stream`
+ * (work already queued on other streams that uses it must be ordered first).
+ * NULL is accepted. */
+int submconv_rulebook_free(submconv_rulebook *rb, void *stream);
+
+/*
+ * Submanifold convolution forward pass on a rulebook's coordinate set.
+ *
+ *   feats  : device [n, cin] of dtype, row i = voxel of coords row i.
+ *   weight : device KRSC [cout, 3, 3, 3, cin] of dtype.
+ *   bias   : device fp32 [cout], or NULL for none (added once).
+ *   out    : device [n, cout] of dtype; must not overlap feats or weight (E_ALIAS).
+ *   cin, cout : 1..1024; the matrix-core path takes {32, 64, 128}, the rest
+ *            runs on the generic kernels.
+ *   dtype  : SUBMCONV_F32 or SUBMCONV_BF16; accumulation is fp32, bf16 output is
+ *            one round-to-nearest-even of the fp32 sum.
+ *   flip   : 0 = correlation, 1 = mirrored kernel (weight tap 26 - k for tap k).
+ *
+ * Pointers must be aligned to 16 bytes.  Asynchronous: never synchronises and
+ * allocates nothing.
+ */
+int submconv_forward(const void *feats, const void *weight, const float *bias,
+                     const submconv_rulebook *rb, void *out, int32_t cin, int32_t cout,
+                     int32_t dtype, int32_t flip, void *stream);
+
+/* submconv_forward with an explicit kernel choice (SUBMCONV_KERNEL_*), for
+ * A/B measurement; E_UNSUPPORTED if that kernel does not take these sizes. */
+int submconv_forward_variant(const void *feats, const void *weight, const float *bias,
+                             const submconv_rulebook *rb, void *out, int32_t cin, int32_t cout,
+                             int32_t dtype, int32_t flip, int32_t variant, void *stream);
+
+/*
+ * Subdivide (lato.2_mrp_mlx working notes, "Key facts": upsampling is
+ * coords*2 + unit cube with features replicated): parent i -> children
+ * 8i + q, q = 4 dz + 2 dy + dx (C order), coords (b, 2z+dz, 2y+dy, 2x+dx),
+ * feats row copied.  coords device int32 [n,4] with 0 <= z,y,x < 2^30;
+ * feats [n,c] of dtype or NULL (then out_feats is ignored);
+ * out_coords [8n,4]; out_feats [8n,c].  Asynchronous.
+ */
+int submconv_subdivide(const int32_t *coords, const void *feats, int64_t n, int32_t c,
+                       int32_t dtype, int32_t *out_coords, void *out_feats, void *stream);
+
+/*
+ * Sparse space-to-depth with factor 2 (trellis_sparse_mrp_mlx commits, the
+ * spatial2channel commit): each fine voxel goes to coarse voxel
+ * (b, z/2, y/2, x/2), slot s = (z%2) + 2 (y%2) + 4 (x%2) (axis 0 fastest).
+ *
+ *   coords [n,4], feats [n,c]: fine set, validated like submconv_build_map
+ *            against res and batch (E_COORD_RANGE, E_DUPLICATE).
+ *   out_coords : [capacity >= n, 4] -> coarse coords, ascending (b, z, y, x).
+ *   out_feats  : [capacity >= n, 8c] -> slot s at channels [s c, (s+1) c);
+ *            slots with no fine voxel are zero.
+ *   out_mask   : uint8 [capacity >= n, 8] -> 1 where the slot is occupied; may be NULL.
+ *   out_m      : host int64, receives M, the number of coarse voxels.
+ * Synchronises `stream` to read M and the status.
+ */
+int submconv_space_to_depth(const int32_t *coords, const void *feats, int64_t n, int32_t c,
+                            int32_t dtype, int32_t res, int32_t batch, int32_t *out_coords,
+                            void *out_feats, uint8_t *out_mask, int64_t *out_m, void *stream);
+
+/*
+ * Inverse of submconv_space_to_depth: coarse voxel m emits child slot s
+ * (s ascending; child (b, 2z + s%2, 2y + (s/2)%2, 2x + s/4)) with features
+ * coarse_feats[m, s c : (s+1) c] -- every slot when mask is NULL, else only the
+ * slots with mask[m,s] != 0 (the masked channel2spatial of the same commit).
+ *   coarse_coords [m,4], coarse_feats [m, 8c], mask uint8 [m,8] or NULL,
+ *   out_coords [capacity >= 8m, 4], out_feats [capacity >= 8m, c],
+ *   out_n : host int64, receives the number of children written.
+ * With a mask it synchronises `stream` to read the count; without, it does not.
+ */
+int submconv_depth_to_space(const int32_t *coarse_coords, const void *coarse_feats,
+                            const uint8_t *mask, int64_t m, int32_t c, int32_t dtype,
+                            int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream);
+
+/* Name of a status code (static string). */
+const char *submconv_status_string(int status);
+
+/* Detail of the last failing call on this thread (static thread-local string). */
+const char *submconv_last_error(void);
+
+/* Library version string. */
+const char *submconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SUBMCONV_H */

@@ -1,0 +1,307 @@
+"""MI355X (gfx950) submanifold 3x3x3 sparse convolution: Python binding.
+
+A thin ctypes binding over the C ABI in include/submconv.h.  It only
+marshals arguments (torch tensors -> device pointers, the current HIP stream,
+status codes -> exceptions); every step of the computation runs in the HIP
+library `_lib/libsubmconv.so`.  PyTorch provides device memory and streams.
+
+If the library has not been built, every call raises: there is no CPU or
+PyTorch fallback.
+
+Functions carry the C names:
+
+    submconv_build_map(coords, res, batch)        -> Rulebook
+    submconv_forward(feats, weight, bias, rb, ...) -> out
+    submconv_subdivide(coords, feats=None)          -> (coords8, feats8)
+    submconv_space_to_depth(coords, feats, res, batch) -> (coarse, feats8c, mask)
+    submconv_depth_to_space(coarse, feats8c, mask=None) -> (coords, feats)
+
+`RulebookCache` keeps one rulebook per coordinate set, keyed like the
+upstream library's indice_key, so every convolution on a set reuses its map
+(lato.2_mrp_mlx working notes, commit summary).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SubmconvError", "Rulebook", "RulebookCache", "lib_path", "load_library",
+    "submconv_build_map", "submconv_forward", "submconv_subdivide",
+    "submconv_space_to_depth", "submconv_depth_to_space",
+    "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libsubmconv.so")
+
+F32, BF16 = 0, 1
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_LOWC, KERNEL_MFMA = 0, 1, 2, 3
+
+_lib = None
+
+
+class SubmconvError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d): %s" % (where, _status_name(status), status, detail))
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsubmconv.so (torch's HIP runtime is already loaded by `import torch`)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libsubmconv.so is not built (%s); run "
+                           "`python -m submanifold_sparse_convolution_submconv3d_amd._build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    i64p, i32p = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "submconv_build_map": [vp, i64, i32, i32, vp, ctypes.POINTER(vp)],
+        "submconv_rulebook_neighbors": [vp, ctypes.POINTER(vp), i64p],
+        "submconv_rulebook_copy_neighbors": [vp, vp, vp],
+        "submconv_rulebook_info": [vp, i64p, i32p, i32p, i64p],
+        "submconv_rulebook_free": [vp, vp],
+        "submconv_forward": [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp],
+        "submconv_forward_variant": [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp],
+        "submconv_subdivide": [vp, vp, i64, i32, i32, vp, vp, vp],
+        "submconv_space_to_depth": [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, i64p, vp],
+        "submconv_depth_to_space": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    for name in ("submconv_status_string",):
+        getattr(lib, name).argtypes = [ctypes.c_int]
+        getattr(lib, name).restype = ctypes.c_char_p
+    for name in ("submconv_last_error", "submconv_version"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return load_library().submconv_status_string(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "status"
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SubmconvError(status, where, load_library().submconv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("feature tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Rulebook:
+    """A neighbour map built on the device for one coordinate set."""
+
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device, stream: torch.cuda.Stream):
+        self._h = handle
+        self.device = device
+        self._stream = stream
+        lib = load_library()
+        n, res, batch, taps = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+        _check(lib.submconv_rulebook_info(handle, ctypes.byref(n), ctypes.byref(res), ctypes.byref(batch),
+                                          ctypes.byref(taps)), "submconv_rulebook_info")
+        self.n, self.res, self.batch, self.taps_present = n.value, res.value, batch.value, taps.value
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise RuntimeError("rulebook already freed")
+        return self._h
+
+    def neighbors(self) -> torch.Tensor:
+        """A copy of the int32 [n,27] neighbour table (row i, tap k -> row or -1)."""
+        out = torch.empty((self.n, 27), dtype=torch.int32, device=self.device)
+        with torch.cuda.device(self.device):
+            _check(load_library().submconv_rulebook_copy_neighbors(self.handle, ctypes.c_void_p(out.data_ptr()),
+                                                                   _stream(self.device)),
+                   "submconv_rulebook_copy_neighbors")
+        return out
+
+    def free(self):
+        if self._h is not None and _lib is not None:
+            with torch.cuda.device(self.device):
+                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(self._stream.cuda_stream))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def submconv_build_map(coords: torch.Tensor, res: int, batch: Optional[int] = None) -> Rulebook:
+    """Build the rulebook of int32 coords [N,4] (b, z, y, x) on a res^3 grid.
+
+    `batch` is the number of batch entries; None reads max(b)+1 from the device."""
+    _dev(coords, "coords", torch.int32)
+    if coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be [N,4]")
+    if batch is None:
+        batch = int(coords[:, 0].max().item()) + 1 if coords.shape[0] else 1
+    lib = load_library()
+    h = ctypes.c_void_p()
+    with torch.cuda.device(coords.device):
+        stream = torch.cuda.current_stream(coords.device)
+        _check(lib.submconv_build_map(ctypes.c_void_p(coords.data_ptr()), coords.shape[0], int(res), int(batch),
+                                      ctypes.c_void_p(stream.cuda_stream), ctypes.byref(h)),
+               "submconv_build_map")
+        return Rulebook(h, coords.device, stream)
+
+
+def submconv_forward(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], rb: Rulebook,
+                     out: Optional[torch.Tensor] = None, flip: bool = False,
+                     variant: int = KERNEL_AUTO) -> torch.Tensor:
+    """out[i] = bias + sum_k W[k] . feats[nbr[i,k]]; feats [N,Cin], weight KRSC [Cout,3,3,3,Cin]."""
+    _dev(feats, "feats")
+    _dev(weight, "weight", feats.dtype)
+    if feats.dim() != 2 or feats.shape[0] != rb.n:
+        raise ValueError("feats must be [N,Cin] with N = %d" % rb.n)
+    cin = feats.shape[1]
+    if weight.dim() != 5 or tuple(weight.shape[1:]) != (3, 3, 3, cin):
+        raise ValueError("weight must be KRSC [Cout,3,3,3,%d]" % cin)
+    cout = weight.shape[0]
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+        if bias.shape != (cout,):
+            raise ValueError("bias must be fp32 [Cout]")
+    if out is None:
+        out = torch.empty((rb.n, cout), dtype=feats.dtype, device=feats.device)
+    else:
+        _dev(out, "out", feats.dtype)
+        if tuple(out.shape) != (rb.n, cout):
+            raise ValueError("out must be [N,Cout]")
+    with torch.cuda.device(feats.device):
+        _check(load_library().submconv_forward_variant(
+            ctypes.c_void_p(feats.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
+            ctypes.c_void_p(bias.data_ptr() if bias is not None else None), rb.handle,
+            ctypes.c_void_p(out.data_ptr()), cin, cout, _dtype_code(feats), int(bool(flip)), int(variant),
+            _stream(feats.device)), "submconv_forward")
+    return out
+
+
+def submconv_subdivide(coords: torch.Tensor, feats: Optional[torch.Tensor] = None):
+    """Children of every voxel: (int32 [8N,4], feats [8N,C] or None), parent-major, C order."""
+    _dev(coords, "coords", torch.int32)
+    n = coords.shape[0]
+    out_c = torch.empty((8 * n, 4), dtype=torch.int32, device=coords.device)
+    out_f, fp, ofp, c, dt = None, None, None, 0, F32
+    if feats is not None:
+        _dev(feats, "feats")
+        c, dt = feats.shape[1], _dtype_code(feats)
+        out_f = torch.empty((8 * n, c), dtype=feats.dtype, device=feats.device)
+        fp, ofp = feats.data_ptr(), out_f.data_ptr()
+    with torch.cuda.device(coords.device):
+        _check(load_library().submconv_subdivide(ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(fp), n, c, dt,
+                                                 ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(ofp),
+                                                 _stream(coords.device)), "submconv_subdivide")
+    return out_c, out_f
+
+
+def submconv_space_to_depth(coords: torch.Tensor, feats: torch.Tensor, res: int, batch: int):
+    """Factor-2 sparse space-to-depth: (coarse int32 [M,4], feats [M,8C], uint8 mask [M,8])."""
+    _dev(coords, "coords", torch.int32)
+    _dev(feats, "feats")
+    n, c = feats.shape
+    out_c = torch.empty((max(n, 1), 4), dtype=torch.int32, device=coords.device)
+    out_f = torch.empty((max(n, 1), 8 * c), dtype=feats.dtype, device=feats.device)
+    mask = torch.empty((max(n, 1), 8), dtype=torch.uint8, device=feats.device)
+    m = ctypes.c_int64()
+    with torch.cuda.device(coords.device):
+        _check(load_library().submconv_space_to_depth(
+            ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(feats.data_ptr()), n, c, _dtype_code(feats),
+            int(res), int(batch), ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(out_f.data_ptr()),
+            ctypes.c_void_p(mask.data_ptr()), ctypes.byref(m), _stream(coords.device)), "submconv_space_to_depth")
+    m = m.value
+    return out_c[:m], out_f[:m], mask[:m]
+
+
+def submconv_depth_to_space(coarse: torch.Tensor, coarse_feats: torch.Tensor, mask: Optional[torch.Tensor] = None):
+    """Inverse of space-to-depth: every slot (mask None) or the masked ones -> (coords, feats)."""
+    _dev(coarse, "coarse", torch.int32)
+    _dev(coarse_feats, "coarse_feats")
+    m, c8 = coarse_feats.shape
+    if c8 % 8:
+        raise ValueError("coarse_feats must be [M, 8C]")
+    c = c8 // 8
+    mp = None
+    if mask is not None:
+        _dev(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (m, 8):
+            raise ValueError("mask must be uint8 [M,8]")
+        mp = mask.data_ptr()
+    out_c = torch.empty((max(8 * m, 1), 4), dtype=torch.int32, device=coarse.device)
+    out_f = torch.empty((max(8 * m, 1), c), dtype=coarse_feats.dtype, device=coarse.device)
+    cnt = ctypes.c_int64()
+    with torch.cuda.device(coarse.device):
+        _check(load_library().submconv_depth_to_space(
+            ctypes.c_void_p(coarse.data_ptr()), ctypes.c_void_p(coarse_feats.data_ptr()), ctypes.c_void_p(mp), m, c,
+            _dtype_code(coarse_feats), ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(out_f.data_ptr()),
+            ctypes.byref(cnt), _stream(coarse.device)), "submconv_depth_to_space")
+    k = cnt.value
+    return out_c[:k], out_f[:k]
+
+
+class RulebookCache:
+    """One rulebook per coordinate set, looked up by a caller-chosen key
+    (the upstream library's indice_key), built on first use."""
+
+    def __init__(self):
+        self._maps = {}
+
+    def get(self, key, coords: torch.Tensor, res: int, batch: Optional[int] = None) -> Rulebook:
+        rb = self._maps.get(key)
+        if rb is None or rb.n != coords.shape[0]:
+            rb = submconv_build_map(coords, res, batch)
+            self._maps[key] = rb
+        return rb
+
+    def drop(self, key):
+        rb = self._maps.pop(key, None)
+        if rb is not None:
+            rb.free()
+
+    def clear(self):
+        for k in list(self._maps):
+            self.drop(k)
+
+    def __len__(self):
+        return len(self._maps)

@@ -1,0 +1,298 @@
+// C ABI of the submconv library: argument validation, rulebook lifetime,
+// kernel dispatch.  Every argument check here runs before any HIP call, so
+// invalid calls fail without touching the device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace sc {
+int build_map(const int32_t *coords, submconv_rulebook *rb, hipStream_t stream);
+int launch_forward(const void *feats, const void *w, const float *bias, const int32_t *nbr,
+                   void *out, int64_t n, int cin, int cout, int dtype, int flip, int variant,
+                   hipStream_t s);
+int choose_forward_kernel(int cin, int cout, int dtype);
+int subdivide(const int32_t *coords, const void *feats, int64_t n, int c, int dtype,
+              int32_t *out_coords, void *out_feats, hipStream_t s);
+int space_to_depth(const int32_t *coords, const void *feats, int64_t n, int c, int dtype, int res,
+                   int batch, int32_t *out_coords, void *out_feats, uint8_t *out_mask,
+                   int64_t *out_m, hipStream_t s);
+int depth_to_space(const int32_t *cc, const void *cf, const uint8_t *mask, int64_t m, int c,
+                   int dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
+
+static thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+static thread_local DevStatus *g_pinned = nullptr;
+
+int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
+{
+    if (!g_pinned) SC_HIP(hipHostMalloc((void **)&g_pinned, sizeof(DevStatus), hipHostMallocDefault));
+    SC_HIP(hipMemcpyAsync(g_pinned, d, sizeof(DevStatus), hipMemcpyDeviceToHost, stream));
+    SC_HIP(hipStreamSynchronize(stream));
+    *h = *g_pinned;
+    return SUBMCONV_OK;
+}
+
+int dev_alloc(void **p, size_t bytes, hipStream_t stream)
+{
+    *p = nullptr;
+    if (bytes == 0) bytes = 256;
+    hipError_t e = hipMallocAsync(p, bytes, stream);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(e == hipErrorOutOfMemory ? SUBMCONV_E_OOM : SUBMCONV_E_HIP,
+                    "device allocation of %zu bytes: %s", bytes, hipGetErrorString(e));
+    }
+    return SUBMCONV_OK;
+}
+
+void dev_free(void *p, hipStream_t stream)
+{
+    if (p) (void)hipFreeAsync(p, stream);
+}
+
+// Keep freed pool memory cached (once per device), so repeated builds do not
+// return it to the driver and fetch it again.
+static int keep_pool(int device)
+{
+    static bool done[64];
+    if (device < 0 || device >= 64 || done[device]) return SUBMCONV_OK;
+    hipMemPool_t pool;
+    SC_HIP(hipDeviceGetDefaultMemPool(&pool, device));
+    uint64_t threshold = UINT64_MAX;
+    SC_HIP(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold));
+    done[device] = true;
+    return SUBMCONV_OK;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const char *x = (const char *)a, *y = (const char *)b;
+    return x < y + nb && y < x + na;
+}
+
+static size_t elem_size(int dtype) { return dtype == SUBMCONV_F32 ? 4 : 2; }
+
+}  // namespace sc
+
+using namespace sc;
+
+extern "C" {
+
+const char *submconv_version(void) { return "submconv 0.1 gfx950"; }
+
+const char *submconv_status_string(int status)
+{
+    switch (status) {
+    case SUBMCONV_OK: return "ok";
+    case SUBMCONV_E_INVALID_ARG: return "invalid argument";
+    case SUBMCONV_E_COORD_RANGE: return "coordinate out of range";
+    case SUBMCONV_E_DUPLICATE: return "duplicate coordinate";
+    case SUBMCONV_E_UNSUPPORTED: return "unsupported configuration";
+    case SUBMCONV_E_ALIAS: return "output aliases an input";
+    case SUBMCONV_E_OOM: return "out of device memory";
+    case SUBMCONV_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *submconv_last_error(void) { return g_err; }
+
+int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t batch, void *stream,
+                       submconv_rulebook **out_rb)
+{
+    if (!out_rb) return fail(SUBMCONV_E_INVALID_ARG, "out_rb is NULL");
+    *out_rb = nullptr;
+    if (n < 0 || n >= (int64_t(1) << 31)) return fail(SUBMCONV_E_INVALID_ARG, "n = %lld outside [0, 2^31)", (long long)n);
+    if (n > 0 && !coords) return fail(SUBMCONV_E_INVALID_ARG, "coords is NULL");
+    if (n > 0 && !aligned16(coords)) return fail(SUBMCONV_E_INVALID_ARG, "coords must be 16-byte aligned");
+    if (res < 1) return fail(SUBMCONV_E_INVALID_ARG, "res = %d must be >= 1", res);
+    if (batch < 1) return fail(SUBMCONV_E_INVALID_ARG, "batch = %d must be >= 1", batch);
+    const int rb = bits_for(res) > 0 ? bits_for(res) : 1;
+    const int nbits = 3 * rb + bits_for(batch);
+    if (nbits > 64) return fail(SUBMCONV_E_UNSUPPORTED, "res %d and batch %d need %d key bits (max 64)", res, batch, nbits);
+    hipStream_t s = (hipStream_t)stream;
+
+    submconv_rulebook *r = new (std::nothrow) submconv_rulebook();
+    if (!r) return fail(SUBMCONV_E_OOM, "host allocation failed");
+    r->n = n;
+    r->res = res;
+    r->batch = batch;
+    r->rb = rb;
+    r->nbits = nbits;
+    r->key_bytes = nbits <= 32 ? 4 : 8;
+    r->taps = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) { delete r; return fail(SUBMCONV_E_HIP, "hipGetDevice failed"); }
+    r->device = dev;
+    int st = keep_pool(dev);
+    if (st != SUBMCONV_OK) { delete r; return st; }
+    const size_t kbytes = (((size_t)n * r->key_bytes) + 255) & ~size_t(255);
+    const size_t pbytes = (((size_t)n * 4) + 255) & ~size_t(255);
+    const size_t nbytes = (size_t)n * 27 * 4;
+    st = dev_alloc(&r->block, kbytes + pbytes + nbytes, s);
+    if (st != SUBMCONV_OK) { delete r; return st; }
+    r->keys = r->block;
+    r->perm = (int32_t *)((char *)r->block + kbytes);
+    r->nbr = (int32_t *)((char *)r->block + kbytes + pbytes);
+    if (n > 0) {
+        st = build_map(coords, r, s);
+        if (st != SUBMCONV_OK) {
+            dev_free(r->block, s);
+            delete r;
+            return st;
+        }
+    }
+    *out_rb = r;
+    return SUBMCONV_OK;
+}
+
+int submconv_rulebook_neighbors(const submconv_rulebook *rb, const int32_t **nbr, int64_t *n)
+{
+    if (!rb || !nbr || !n) return fail(SUBMCONV_E_INVALID_ARG, "NULL argument");
+    *nbr = rb->nbr;
+    *n = rb->n;
+    return SUBMCONV_OK;
+}
+
+int submconv_rulebook_copy_neighbors(const submconv_rulebook *rb, int32_t *dst, void *stream)
+{
+    if (!rb) return fail(SUBMCONV_E_INVALID_ARG, "rulebook is NULL");
+    if (rb->n == 0) return SUBMCONV_OK;
+    if (!dst) return fail(SUBMCONV_E_INVALID_ARG, "dst is NULL");
+    const size_t bytes = (size_t)rb->n * 27 * 4;
+    if (overlaps(dst, bytes, rb->nbr, bytes)) return fail(SUBMCONV_E_ALIAS, "dst overlaps the table");
+    SC_HIP(hipMemcpyAsync(dst, rb->nbr, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+    return SUBMCONV_OK;
+}
+
+int submconv_rulebook_info(const submconv_rulebook *rb, int64_t *n, int32_t *res, int32_t *batch,
+                           int64_t *taps_present)
+{
+    if (!rb) return fail(SUBMCONV_E_INVALID_ARG, "rulebook is NULL");
+    if (n) *n = rb->n;
+    if (res) *res = rb->res;
+    if (batch) *batch = rb->batch;
+    if (taps_present) *taps_present = rb->taps;
+    return SUBMCONV_OK;
+}
+
+int submconv_rulebook_free(submconv_rulebook *rb, void *stream)
+{
+    if (!rb) return SUBMCONV_OK;
+    dev_free(rb->block, (hipStream_t)stream);
+    delete rb;
+    return SUBMCONV_OK;
+}
+
+int submconv_forward_variant(const void *feats, const void *weight, const float *bias,
+                             const submconv_rulebook *rb, void *out, int32_t cin, int32_t cout,
+                             int32_t dtype, int32_t flip, int32_t variant, void *stream)
+{
+    if (!rb) return fail(SUBMCONV_E_INVALID_ARG, "rulebook is NULL");
+    if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+    if (cin < 1 || cin > 1024 || cout < 1 || cout > 1024)
+        return fail(SUBMCONV_E_UNSUPPORTED, "channel counts %d -> %d outside 1..1024", cin, cout);
+    if (flip != 0 && flip != 1) return fail(SUBMCONV_E_INVALID_ARG, "flip must be 0 or 1");
+    if (variant < SUBMCONV_KERNEL_AUTO || variant > SUBMCONV_KERNEL_MFMA)
+        return fail(SUBMCONV_E_INVALID_ARG, "unknown kernel variant %d", variant);
+    const int64_t n = rb->n;
+    if (n == 0) return SUBMCONV_OK;
+    if (!feats || !weight || !out) return fail(SUBMCONV_E_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned16(feats) || !aligned16(weight) || !aligned16(out) || (bias && !aligned16(bias)))
+        return fail(SUBMCONV_E_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t fb = (size_t)n * cin * es, wb = (size_t)cout * 27 * cin * es, ob = (size_t)n * cout * es;
+    if (overlaps(out, ob, feats, fb) || overlaps(out, ob, weight, wb) ||
+        (bias && overlaps(out, ob, bias, (size_t)cout * 4)))
+        return fail(SUBMCONV_E_ALIAS, "out overlaps feats, weight or bias");
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev != rb->device)
+        return fail(SUBMCONV_E_INVALID_ARG, "rulebook lives on device %d, current device is %d", rb->device, dev);
+    return launch_forward(feats, weight, bias, rb->nbr, out, n, cin, cout, dtype, flip, variant,
+                          (hipStream_t)stream);
+}
+
+int submconv_forward(const void *feats, const void *weight, const float *bias,
+                     const submconv_rulebook *rb, void *out, int32_t cin, int32_t cout,
+                     int32_t dtype, int32_t flip, void *stream)
+{
+    return submconv_forward_variant(feats, weight, bias, rb, out, cin, cout, dtype, flip,
+                                    SUBMCONV_KERNEL_AUTO, stream);
+}
+
+int submconv_subdivide(const int32_t *coords, const void *feats, int64_t n, int32_t c,
+                       int32_t dtype, int32_t *out_coords, void *out_feats, void *stream)
+{
+    if (n < 0 || n >= (int64_t(1) << 28)) return fail(SUBMCONV_E_INVALID_ARG, "n = %lld outside [0, 2^28)", (long long)n);
+    if (n == 0) return SUBMCONV_OK;
+    if (!coords || !out_coords) return fail(SUBMCONV_E_INVALID_ARG, "NULL coordinate pointer");
+    if (!aligned16(coords) || !aligned16(out_coords)) return fail(SUBMCONV_E_INVALID_ARG, "coordinate pointers must be 16-byte aligned");
+    if (overlaps(out_coords, (size_t)n * 128, coords, (size_t)n * 16)) return fail(SUBMCONV_E_ALIAS, "out_coords overlaps coords");
+    if (feats) {
+        if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+        if (c < 1 || c > 65536) return fail(SUBMCONV_E_INVALID_ARG, "c = %d", c);
+        if (!out_feats) return fail(SUBMCONV_E_INVALID_ARG, "out_feats is NULL");
+        const size_t es = elem_size(dtype);
+        if (((uintptr_t)feats | (uintptr_t)out_feats) & (((size_t)c * es) % 4 == 0 ? 3u : 1u))
+            return fail(SUBMCONV_E_INVALID_ARG, "feature pointers misaligned");
+        if (overlaps(out_feats, (size_t)n * 8 * c * es, feats, (size_t)n * c * es))
+            return fail(SUBMCONV_E_ALIAS, "out_feats overlaps feats");
+    }
+    return subdivide(coords, feats, n, c, dtype, out_coords, out_feats, (hipStream_t)stream);
+}
+
+int submconv_space_to_depth(const int32_t *coords, const void *feats, int64_t n, int32_t c,
+                            int32_t dtype, int32_t res, int32_t batch, int32_t *out_coords,
+                            void *out_feats, uint8_t *out_mask, int64_t *out_m, void *stream)
+{
+    if (!out_m) return fail(SUBMCONV_E_INVALID_ARG, "out_m is NULL");
+    *out_m = 0;
+    if (n < 0 || n >= (int64_t(1) << 31)) return fail(SUBMCONV_E_INVALID_ARG, "n = %lld outside [0, 2^31)", (long long)n);
+    if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+    if (c < 1 || c > 65536) return fail(SUBMCONV_E_INVALID_ARG, "c = %d", c);
+    if (res < 1 || batch < 1) return fail(SUBMCONV_E_INVALID_ARG, "res and batch must be >= 1");
+    if (n == 0) return SUBMCONV_OK;
+    if (!coords || !feats || !out_coords || !out_feats) return fail(SUBMCONV_E_INVALID_ARG, "NULL pointer");
+    if (!aligned16(coords) || !aligned16(out_coords)) return fail(SUBMCONV_E_INVALID_ARG, "coordinate pointers must be 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    if (overlaps(out_feats, (size_t)n * 8 * c * es, feats, (size_t)n * c * es) ||
+        overlaps(out_coords, (size_t)n * 16, coords, (size_t)n * 16))
+        return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
+    return space_to_depth(coords, feats, n, c, dtype, res, batch, out_coords, out_feats, out_mask,
+                          out_m, (hipStream_t)stream);
+}
+
+int submconv_depth_to_space(const int32_t *coarse_coords, const void *coarse_feats,
+                            const uint8_t *mask, int64_t m, int32_t c, int32_t dtype,
+                            int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream)
+{
+    if (!out_n) return fail(SUBMCONV_E_INVALID_ARG, "out_n is NULL");
+    *out_n = 0;
+    if (m < 0 || m >= (int64_t(1) << 28)) return fail(SUBMCONV_E_INVALID_ARG, "m = %lld outside [0, 2^28)", (long long)m);
+    if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+    if (c < 1 || c > 65536) return fail(SUBMCONV_E_INVALID_ARG, "c = %d", c);
+    if (m == 0) return SUBMCONV_OK;
+    if (!coarse_coords || !coarse_feats || !out_coords || !out_feats) return fail(SUBMCONV_E_INVALID_ARG, "NULL pointer");
+    if (!aligned16(coarse_coords) || !aligned16(out_coords)) return fail(SUBMCONV_E_INVALID_ARG, "coordinate pointers must be 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    if (overlaps(out_feats, (size_t)m * 8 * c * es, coarse_feats, (size_t)m * 8 * c * es) ||
+        overlaps(out_coords, (size_t)m * 128, coarse_coords, (size_t)m * 16))
+        return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
+    return depth_to_space(coarse_coords, coarse_feats, mask, m, c, dtype, out_coords, out_feats,
+                          out_n, (hipStream_t)stream);
+}
+
+}  // extern "C"

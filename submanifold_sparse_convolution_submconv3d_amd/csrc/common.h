@@ -1,0 +1,177 @@
+// Internal declarations of the submconv HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "submconv.h"
+
+namespace sc {
+
+// --------------------------------------------------------------------------
+// errors
+// --------------------------------------------------------------------------
+
+// Record a printf-style detail message for submconv_last_error; returns `status`.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+#define SC_HIP(expr)                                                              \
+    do {                                                                          \
+        hipError_t e_ = (expr);                                                   \
+        if (e_ != hipSuccess)                                                     \
+            return ::sc::fail(e_ == hipErrorOutOfMemory ? SUBMCONV_E_OOM          \
+                                                        : SUBMCONV_E_HIP,         \
+                              "%s: %s", #expr, hipGetErrorString(e_));            \
+    } while (0)
+
+#define SC_LAUNCHED(name)                                                         \
+    do {                                                                          \
+        hipError_t e_ = hipGetLastError();                                        \
+        if (e_ != hipSuccess)                                                     \
+            return ::sc::fail(SUBMCONV_E_HIP, "launch of %s: %s", name,           \
+                              hipGetErrorString(e_));                             \
+    } while (0)
+
+#define SC_CHECK(expr)                                                            \
+    do {                                                                          \
+        int s_ = (expr);                                                          \
+        if (s_ != SUBMCONV_OK) return s_;                                         \
+    } while (0)
+
+// --------------------------------------------------------------------------
+// device status block (one per map build / helper call)
+// --------------------------------------------------------------------------
+
+enum : uint32_t { FLAG_RANGE = 1u, FLAG_DUPLICATE = 2u };
+
+struct DevStatus {
+    uint32_t flags;              // FLAG_* bits, or-ed by kernels
+    uint32_t pad;
+    unsigned long long taps;     // present entries of the neighbour table
+    unsigned long long count;    // an output row count (helpers)
+    unsigned long long pad2;
+};
+
+// Enqueue a copy of `d` to a pinned host block, synchronise `stream`, return it in `h`.
+int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream);
+
+// --------------------------------------------------------------------------
+// stream-ordered device memory
+// --------------------------------------------------------------------------
+
+int dev_alloc(void **p, size_t bytes, hipStream_t stream);
+void dev_free(void *p, hipStream_t stream);
+
+// --------------------------------------------------------------------------
+// key layout: ((b << 3rb | z << 2rb | y << rb | x), rb = bits(res - 1)
+// --------------------------------------------------------------------------
+
+inline int bits_for(int64_t count)  // bits to hold values 0 .. count-1
+{
+    int b = 0;
+    while (b < 63 && (int64_t(1) << b) < count) ++b;
+    return b;
+}
+
+// Sort (key, value) pairs by the low `nbits` bits of the key, stable, LSD radix.
+// keys_a/vals_a hold the input; the sorted result ends in keys_a/vals_a.
+// keys_b/vals_b are scratch of the same size.  `scratch` must hold
+// sort_scratch_bytes(n) bytes.
+size_t sort_scratch_bytes(int64_t n);
+template <typename K>
+int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int64_t n, int nbits,
+                     void *scratch, hipStream_t stream);
+
+// Exclusive scan of n uint32 values (in place allowed); writes the total to *total_dev
+// if non-null.  `scratch` must hold scan_scratch_bytes(n) bytes.
+size_t scan_scratch_bytes(int64_t n);
+int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *total_dev,
+                       void *scratch, hipStream_t stream);
+
+// --------------------------------------------------------------------------
+// bf16 helpers (bf16 values travel as uint16_t bit patterns)
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)  // round to nearest even
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float *p) { return *p; }
+    static __device__ __forceinline__ float to_f32(float v) { return v; }
+    static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+    static __device__ __forceinline__ uint16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// --------------------------------------------------------------------------
+// wave64 helpers
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ unsigned lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint64_t lanemask_lt() { return (uint64_t(1) << lane_id()) - 1; }
+
+// Mask of the active lanes (valid == true) holding the same `dbits`-bit digit
+// as this lane.  Must be reached by all lanes of the wave.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid, int dbits)
+{
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < dbits; ++b) {
+        uint64_t bit = __ballot(valid && ((d >> b) & 1u));
+        m &= ((d >> b) & 1u) ? bit : ~bit;
+    }
+    return m;
+}
+
+// Inclusive scan of v over a 256-thread block; `lds` holds >= 4 words.
+// Returns the inclusive prefix; *total receives the block sum.
+__device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t *lds, uint32_t *total)
+{
+    const unsigned lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= (unsigned)off) x += y;
+    }
+    if (lane == 63) lds[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t t = lds[w];
+        before += (w < (int)wave) ? t : 0u;
+        sum += t;
+    }
+    __syncthreads();
+    *total = sum;
+    return x + before;
+}
+
+}  // namespace sc
+
+// Rulebook: library-owned device memory for one coordinate set.
+struct submconv_rulebook {
+    int64_t n;
+    int32_t res;
+    int32_t batch;
+    int32_t rb;         // bits per spatial axis in the key
+    int32_t nbits;      // significant key bits
+    int32_t key_bytes;  // 4 or 8
+    int32_t device;
+    int64_t taps;       // P: present entries of nbr
+    void *block;        // single allocation holding the arrays below
+    void *keys;         // sorted keys [n]
+    int32_t *perm;      // sorted position -> original row [n]
+    int32_t *nbr;       // [n,27] in original row order
+};
