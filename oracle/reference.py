@@ -102,10 +102,11 @@ def weight_tap(weight: np.ndarray, k: int, flip: bool) -> np.ndarray:
 def forward(feats: np.ndarray, weight: np.ndarray, bias, nbr: np.ndarray, flip: bool = False) -> np.ndarray:
     """out[i] = bias + sum over present taps k of W_k @ feats[nbr[i,k]], in float64.
 
-    feats [N,Cin], weight KRSC [Cout,3,3,3,Cin], bias [Cout] or None, nbr [N,27]."""
+    feats [N,Cin], weight KRSC [Cout,3,3,3,Cin], bias [Cout] or None, nbr [M,27]
+    (the table rows of the outputs wanted: all N, or a subset of them)."""
     f = np.asarray(feats, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
-    n, cout = f.shape[0], w.shape[0]
+    n, cout = nbr.shape[0], w.shape[0]          # one output row per table row
     out = np.zeros((n, cout), np.float64)
     for k in range(TAPS):
         rows = nbr[:, k]

@@ -410,3 +410,12 @@ def test_bf16_conversion_matches_torch():
     tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(bits, tb)
     np.testing.assert_array_equal(synth.bf16_to_f32(bits), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_forward_of_row_subset_equals_rows_of_full_forward():
+    coords = random_set(700, 9, 1, 81)
+    feats, weight, bias = synth.make_values(700, 4, 5, 82)
+    nbr = dense.neighbor_table(coords, 9)
+    rows = np.array([0, 5, 17, 699, 350])
+    np.testing.assert_array_equal(ref.forward(feats, weight, bias, nbr[rows]),
+                                  ref.forward(feats, weight, bias, nbr)[rows])
