@@ -110,31 +110,120 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
 }
 
 // ---------------------------------------------------------------------------
-// mfma, bf16: v_mfma_f32_32x32x16_bf16
-//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
-//   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
-//   D (32 x 32): lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4, r = 0..15
+// mfma: implicit GEMM on the matrix cores
+//
+// bf16 uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2_f32 four
+// times per 16-byte fragment.  Operand layout (both): a 1 KB fragment holds,
+// in lane l, the 16 bytes of matrix row (l % 32) at 16-byte chunk 2g + l / 32
+// of that row, where g is the fragment's group along Cin.  For bf16 a chunk is
+// 8 channels and the 32x32x16 instruction contracts both halves at once; for
+// fp32 a chunk is 4 channels and step e of the four 32x32x2 instructions takes
+// element e of both lanes' chunks, so each group covers its 8 channels once.
+// (The contraction order may be permuted freely as long as A and B agree.)
+// D (32 x 32): lane l holds column l % 32, rows 8 (q/4) + 4 (l/32) + q % 4.
+//
+// Data movement per block (4 waves, each 32*VT voxels x all Cout):
+//   * weight tap k' is copied once per block into LDS in fragment order by
+//     direct global->LDS loads (no register staging), double-buffered so the
+//     copy of the next tap overlaps this tap's MFMAs; when all 27 taps fit in
+//     64 KB they are copied once and stay resident (no per-tap barrier);
+//   * the B operand (gathered feature rows) is loaded straight into registers,
+//     one tap ahead of the MFMAs that use it; a missing neighbour gives zeros.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t *p)
-{
-    const uint4 v = *(const uint4 *)p;
-    return __builtin_bit_cast(bf16x8_t, v);
-}
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
-template <int CIN, int COUT, int VT>
-__global__ __launch_bounds__(256) void k_conv_mfma_bf16(const uint16_t *__restrict__ feats,
-                                                        const uint16_t *__restrict__ w,
-                                                        const float *__restrict__ bias,
-                                                        const int32_t *__restrict__ nbr,
-                                                        uint16_t *__restrict__ out, int64_t n,
-                                                        int flip)
+template <typename T> struct Mma;
+template <> struct Mma<uint16_t> {
+    static __device__ __forceinline__ void step(floatx16 &acc, const uint4 &a, const uint4 &b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
+};
+template <> struct Mma<float> {
+    static __device__ __forceinline__ void step(floatx16 &acc, const uint4 &a, const uint4 &b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    }
+};
+
+template <typename T> struct Store4;
+template <> struct Store4<uint16_t> {
+    static __device__ __forceinline__ void put(uint16_t *p, float a, float b, float c, float d)
+    {
+        const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+        *(uint2 *)p = make_uint2(lo, hi);
+    }
+};
+template <> struct Store4<float> {
+    static __device__ __forceinline__ void put(float *p, float a, float b, float c, float d)
+    {
+        *(float4 *)p = make_float4(a, b, c, d);
+    }
+};
+
+template <typename T, int CIN, int COUT, int VT>
+struct MfmaShape {
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int EPC = 16 / ES;                // elements per 16-byte chunk
+    static constexpr int G = CIN * ES / 32;            // fragment groups along Cin
+    static constexpr int RT = COUT / 32;               // row tiles (output channels)
+    static constexpr int NFRAG = RT * G;               // weight fragments per tap (1 KB each)
+    static constexpr bool RESIDENT = 27 * NFRAG * 1024 <= 65536;
+    static constexpr int WBUF = RESIDENT ? 27 : 2;     // tap buffers in LDS
+    static constexpr int VOX_PER_BLOCK = 4 * 32 * VT;
+    static_assert(G >= 1 && RT >= 1, "channel counts too small for the matrix-core path");
+};
+
+template <typename T, int CIN, int COUT, int VT>
+__global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
+                                                   const T *__restrict__ w,
+                                                   const float *__restrict__ bias,
+                                                   const int32_t *__restrict__ nbr,
+                                                   T *__restrict__ out, int64_t n, int flip)
 {
-    constexpr int RT = COUT / 32;  // row tiles (output channels)
-    constexpr int KS = CIN / 16;   // k steps per tap
+    using S = MfmaShape<T, CIN, COUT, VT>;
+    constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
+    __shared__ uint4 sW[S::WBUF][NFRAG * 64];
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t vbase = ((int64_t)blockIdx.x * 4 + wave) * (VT * 32);
+
+    // copy weight tap k (kernel tap k' = flip ? 26-k : k) into LDS buffer `buf`
+    auto stage_w = [&](int k, int buf) {
+        const int kw = flip ? 26 - k : k;
+        for (int f = wave; f < NFRAG; f += 4) {
+            const int r = f / G, g = f - r * G;
+            const T *src = w + ((int64_t)(32 * r + l32) * 27 + kw) * CIN + (2 * g + half) * EPC;
+            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)&sW[buf][f * 64], 16, 0, 0);
+        }
+    };
+    // neighbour rows of this wave's voxels for tap k, and their feature fragments
+    auto load_tap = [&](int k, int32_t (&j)[VT], uint4 (&F)[VT][G]) -> bool {
+        bool any = false;
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+            const int64_t v = vbase + 32 * t + l32;
+            int32_t r = v < n ? nbr[v * 27 + k] : -1;
+            if ((uint32_t)r >= (uint64_t)n) r = -1;
+            j[t] = r;
+            any |= r >= 0;
+        }
+#pragma unroll
+        for (int t = 0; t < VT; ++t)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                F[t][g] = j[t] >= 0 ? *(const uint4 *)(feats + (int64_t)j[t] * CIN + (2 * g + half) * EPC)
+                                    : make_uint4(0, 0, 0, 0);
+        return any;
+    };
 
     floatx16 acc[RT][VT];
 #pragma unroll
@@ -144,119 +233,49 @@ __global__ __launch_bounds__(256) void k_conv_mfma_bf16(const uint16_t *__restri
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[r][t][q] = 0.f;
 
-    for (int k = 0; k < 27; ++k) {
-        int32_t j[VT];
-        bool any = false;
+    auto compute = [&](const uint4 *wb, const uint4 (&F)[VT][G]) {
 #pragma unroll
-        for (int t = 0; t < VT; ++t) {
-            const int64_t v = vbase + 32 * t + l32;
-            j[t] = v < n ? nbr[v * 27 + k] : -1;
-            if ((uint32_t)j[t] >= (uint64_t)n) j[t] = -1;
-            any |= j[t] >= 0;
-        }
-        if (!__any(any)) continue;  // wave-uniform
-        const int kw = flip ? 26 - k : k;
-        bf16x8_t bf[VT][KS];
-#pragma unroll
-        for (int t = 0; t < VT; ++t)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if (j[t] >= 0) bf[t][s] = load_bf16x8(feats + (int64_t)j[t] * CIN + 16 * s + 8 * half);
-                else bf[t][s] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-            }
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            const uint16_t *wr = w + ((int64_t)(32 * r + l32) * 27 + kw) * CIN + 8 * half;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8_t a = load_bf16x8(wr + 16 * s);
-#pragma unroll
-                for (int t = 0; t < VT; ++t)
-                    acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[t][s], acc[r][t], 0, 0, 0);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-        const int64_t v = vbase + 32 * t + l32;
-        if (v >= n) continue;
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int o = 32 * r + 8 * g + 4 * half;
-                float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-                if (bias) { b0 = bias[o]; b1 = bias[o + 1]; b2 = bias[o + 2]; b3 = bias[o + 3]; }
-                const uint32_t lo = (uint32_t)f32_to_bf16(acc[r][t][4 * g] + b0) |
-                                    ((uint32_t)f32_to_bf16(acc[r][t][4 * g + 1] + b1) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16(acc[r][t][4 * g + 2] + b2) |
-                                    ((uint32_t)f32_to_bf16(acc[r][t][4 * g + 3] + b3) << 16);
-                *(uint2 *)(out + v * COUT + o) = make_uint2(lo, hi);
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// mfma, fp32: v_mfma_f32_32x32x2_f32
-//   A (32 x 2): lane l holds row l%32, k = l/32; B likewise with column l%32.
-//   The contraction index may be permuted as long as A and B agree: lane half h
-//   loads channels [8g + 4h, 8g + 4h + 4) and feeds element e in step e, so the
-//   four steps of group g cover channels 8g .. 8g+7 once each.
-// ---------------------------------------------------------------------------
-
-template <int CIN, int COUT, int VT>
-__global__ __launch_bounds__(256) void k_conv_mfma_f32(const float *__restrict__ feats,
-                                                       const float *__restrict__ w,
-                                                       const float *__restrict__ bias,
-                                                       const int32_t *__restrict__ nbr,
-                                                       float *__restrict__ out, int64_t n, int flip)
-{
-    constexpr int RT = COUT / 32;
-    constexpr int KG = CIN / 8;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int half = lane >> 5, l32 = lane & 31;
-    const int64_t vbase = ((int64_t)blockIdx.x * 4 + wave) * (VT * 32);
-
-    floatx16 acc[RT][VT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int t = 0; t < VT; ++t)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[r][t][q] = 0.f;
-
-    for (int k = 0; k < 27; ++k) {
-        int32_t j[VT];
-        bool any = false;
-#pragma unroll
-        for (int t = 0; t < VT; ++t) {
-            const int64_t v = vbase + 32 * t + l32;
-            j[t] = v < n ? nbr[v * 27 + k] : -1;
-            if ((uint32_t)j[t] >= (uint64_t)n) j[t] = -1;
-            any |= j[t] >= 0;
-        }
-        if (!__any(any)) continue;
-        const int kw = flip ? 26 - k : k;
-#pragma unroll
-        for (int g = 0; g < KG; ++g) {
-            float4 bf[VT];
-#pragma unroll
-            for (int t = 0; t < VT; ++t)
-                bf[t] = j[t] >= 0 ? *(const float4 *)(feats + (int64_t)j[t] * CIN + 8 * g + 4 * half)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const float4 a = *(const float4 *)(w + ((int64_t)(32 * r + l32) * 27 + kw) * CIN + 8 * g + 4 * half);
+                const uint4 a = wb[(r * G + g) * 64 + lane];
 #pragma unroll
-                for (int t = 0; t < VT; ++t) {
-                    acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bf[t].x, acc[r][t], 0, 0, 0);
-                    acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bf[t].y, acc[r][t], 0, 0, 0);
-                    acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bf[t].z, acc[r][t], 0, 0, 0);
-                    acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bf[t].w, acc[r][t], 0, 0, 0);
-                }
+                for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], a, F[t][g]);
             }
-        }
+    };
+
+    int32_t j0[VT], j1[VT];
+    uint4 F0[VT][G], F1[VT][G];
+    if constexpr (S::RESIDENT) {
+        for (int k = 0; k < 27; ++k) stage_w(k, k);
+    } else {
+        stage_w(0, 0);
     }
+    bool any0 = load_tap(0, j0, F0), any1 = false;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // one tap: prefetch tap k+1 (weights into LDS, features into the other
+    // register set), run tap k's MFMAs, then wait and (when the weights
+    // rotate through two buffers) meet at a barrier
+    auto tap = [&](int k, uint4 (&Fc)[VT][G], bool anyc, int32_t (&jn)[VT], uint4 (&Fn)[VT][G]) -> bool {
+        bool anyn = false;
+        if (k + 1 < 27) {
+            if constexpr (!S::RESIDENT) stage_w(k + 1, (k + 1) & 1);
+            anyn = load_tap(k + 1, jn, Fn);
+        }
+        if (__any(anyc)) compute(sW[S::RESIDENT ? k : (k & 1)], Fc);
+        if constexpr (!S::RESIDENT) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return anyn;
+    };
+    for (int k = 0; k < 27; k += 2) {
+        any1 = tap(k, F0, any0, j1, F1);
+        if (k + 1 < 27) any0 = tap(k + 1, F1, any1, j0, F0);
+    }
+
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
         const int64_t v = vbase + 32 * t + l32;
@@ -264,13 +283,12 @@ __global__ __launch_bounds__(256) void k_conv_mfma_f32(const float *__restrict__
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int o = 32 * r + 8 * g + 4 * half;
+            for (int q = 0; q < 4; ++q) {
+                const int o = 32 * r + 8 * q + 4 * half;
                 float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (bias) b = *(const float4 *)(bias + o);
-                *(float4 *)(out + v * COUT + o) =
-                    make_float4(acc[r][t][4 * g] + b.x, acc[r][t][4 * g + 1] + b.y,
-                                acc[r][t][4 * g + 2] + b.z, acc[r][t][4 * g + 3] + b.w);
+                Store4<T>::put(out + v * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
+                               acc[r][t][4 * q + 2] + b.z, acc[r][t][4 * q + 3] + b.w);
             }
     }
 }
@@ -342,16 +360,16 @@ static int launch_mfma_t(const void *f, const void *w, const float *b, const int
                          int64_t n, int dtype, int flip, hipStream_t s)
 {
     if (dtype == SUBMCONV_BF16) {
-        constexpr int VT = (COUT >= 128) ? 2 : 2;
-        const int64_t per_block = 4 * 32 * VT;
+        constexpr int VT = 2;
+        constexpr int per_block = MfmaShape<uint16_t, CIN, COUT, VT>::VOX_PER_BLOCK;
         const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
-        hipLaunchKernelGGL((k_conv_mfma_bf16<CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_conv_mfma<uint16_t, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
                            (const uint16_t *)f, (const uint16_t *)w, b, nbr, (uint16_t *)o, n, flip);
     } else {
-        constexpr int VT = 1;
-        const int64_t per_block = 4 * 32 * VT;
+        constexpr int VT = (CIN >= 128 || COUT >= 128) ? 1 : 2;
+        constexpr int per_block = MfmaShape<float, CIN, COUT, VT>::VOX_PER_BLOCK;
         const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
-        hipLaunchKernelGGL((k_conv_mfma_f32<CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_conv_mfma<float, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
                            (const float *)f, (const float *)w, b, nbr, (float *)o, n, flip);
     }
     SC_LAUNCHED("conv_mfma");
