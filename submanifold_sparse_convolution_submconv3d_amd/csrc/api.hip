@@ -141,7 +141,8 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     if (st != SUBMCONV_OK) { delete r; return st; }
     const size_t kbytes = (((size_t)n * r->key_bytes) + 255) & ~size_t(255);
     const size_t pbytes = (((size_t)n * 4) + 255) & ~size_t(255);
-    const size_t nbytes = (size_t)n * 27 * 4;
+    // +1 KB: kernels copy table rows in 16-byte chunks that may run past the last row
+    const size_t nbytes = ((((size_t)n * 27 * 4) + 255) & ~size_t(255)) + 1024;
     st = dev_alloc(&r->block, kbytes + pbytes + nbytes, s);
     if (st != SUBMCONV_OK) { delete r; return st; }
     r->keys = r->block;

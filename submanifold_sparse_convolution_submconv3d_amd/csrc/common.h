@@ -75,19 +75,22 @@ inline int bits_for(int64_t count)  // bits to hold values 0 .. count-1
 }
 
 // Sort (key, value) pairs by the low `nbits` bits of the key, stable, LSD radix.
-// keys_a/vals_a hold the input; the sorted result ends in keys_a/vals_a.
-// keys_b/vals_b are scratch of the same size.  `scratch` must hold
-// sort_scratch_bytes(n) bytes.
+// The input is in the a buffers, or in the b buffers when input_in_b; the sorted
+// result always ends in keys_a/vals_a (no copy when the input side is chosen by
+// the parity of radix_sort_passes).  `scratch` must hold sort_scratch_bytes(n) bytes.
 size_t sort_scratch_bytes(int64_t n);
+int radix_sort_passes(int64_t n, int nbits);
 template <typename K>
 int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int64_t n, int nbits,
-                     void *scratch, hipStream_t stream);
+                     void *scratch, hipStream_t stream, bool input_in_b = false);
 
-// Exclusive scan of n uint32 values (in place allowed); writes the total to *total_dev
-// if non-null.  `scratch` must hold scan_scratch_bytes(n) bytes.
+// Exclusive scan of n uint32 values (in place allowed), or of the set-bit counts of
+// n 32-bit / 64-bit words; writes the total to *total_dev if non-null.  `scratch`
+// must hold scan_scratch_bytes(n) bytes.
+enum { SCAN_VALUES = 0, SCAN_POPC32 = 1, SCAN_POPC64 = 2 };
 size_t scan_scratch_bytes(int64_t n);
 int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *total_dev,
-                       void *scratch, hipStream_t stream);
+                       void *scratch, hipStream_t stream, int input_mode = SCAN_VALUES);
 
 // --------------------------------------------------------------------------
 // bf16 helpers (bf16 values travel as uint16_t bit patterns)

@@ -134,6 +134,29 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
+__device__ uint4 g_zero_row[64] = {};  // 1 KB of zeros: the row of a missing neighbour
+
+// s_waitcnt with only the LDS/scalar counter at zero (vector-memory loads may stay in flight)
+#define SC_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// Copy the neighbour-table rows of voxels [v0, v0 + nvox) into LDS (direct loads,
+// 1 KB per wave instruction).  The table allocation is padded, so a 16-byte chunk
+// that straddles its end stays inside it; chunks wholly past the end read zeros
+// (those voxels do not exist and their entries are never used).
+template <int NVOX>
+__device__ __forceinline__ void stage_nbr(const int32_t *nbr, int64_t n, int64_t v0, char *dst,
+                                          int wave, int lane)
+{
+    constexpr int NI = (NVOX * 27 * 4 + 1023) / 1024;
+    const char *base = (const char *)(nbr + v0 * 27);
+    const int64_t left = (n - v0) * 27 * 4;  // valid bytes from base
+    for (int i = wave; i < NI; i += 4) {
+        const int64_t off = (int64_t)i * 1024 + lane * 16;
+        const void *src = off < left ? (const void *)(base + off) : (const void *)g_zero_row;
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
+    }
+}
+
 template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {
     static __device__ __forceinline__ void step(floatx16 &acc, const uint4 &a, const uint4 &b)
@@ -191,6 +214,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     using S = MfmaShape<T, CIN, COUT, VT>;
     constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
     __shared__ uint4 sW[S::WBUF][NFRAG * 64];
+    __shared__ __attribute__((aligned(16))) int32_t sN[S::VOX_PER_BLOCK * 27 + 256];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
 #pragma unroll
         for (int t = 0; t < VT; ++t) {
             const int64_t v = vbase + 32 * t + l32;
-            int32_t r = v < n ? nbr[v * 27 + k] : -1;
+            int32_t r = v < n ? sN[(wave * VT * 32 + 32 * t + l32) * 27 + k] : -1;
             if ((uint32_t)r >= (uint64_t)n) r = -1;
             j[t] = r;
             any |= r >= 0;
@@ -251,6 +275,9 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     } else {
         stage_w(0, 0);
     }
+    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, (int64_t)blockIdx.x * S::VOX_PER_BLOCK, (char *)sN, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     bool any0 = load_tap(0, j0, F0), any1 = false;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -274,6 +301,167 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     for (int k = 0; k < 27; k += 2) {
         any1 = tap(k, F0, any0, j1, F1);
         if (k + 1 < 27) any0 = tap(k + 1, F1, any1, j0, F0);
+    }
+
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+        const int64_t v = vbase + 32 * t + l32;
+        if (v >= n) continue;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int o = 32 * r + 8 * q + 4 * half;
+                float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (bias) b = *(const float4 *)(bias + o);
+                Store4<T>::put(out + v * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
+                               acc[r][t][4 * q + 2] + b.z, acc[r][t][4 * q + 3] + b.w);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// mfma, row-gathered operands (used where its LDS fits)
+//
+// Same MFMA fragments as above, but operands travel through LDS as whole
+// rows: a direct global->LDS load moves 1 KB per wave instruction, 64 lanes
+// x 16 bytes, with consecutive lanes covering consecutive 16-byte chunks of
+// one row, so each gathered feature row (and each weight row) is fetched as
+// whole cache lines.  Inside LDS a row's chunk c sits in slot c ^ sw(row),
+// an XOR swizzle that puts the 16 rows read by 16 consecutive lanes in 16
+// different bank groups, so fragment reads are free of bank conflicts.
+// Missing neighbours load from a zero row.  Per wave, the next tap's rows are
+// gathered into its private LDS region while the current tap's MFMAs run
+// (the B fragments of the current tap having been read into registers first).
+// ---------------------------------------------------------------------------
+
+template <int RB>  // row bytes
+__device__ __forceinline__ int swz(int row)
+{
+    constexpr int CH = RB / 16;                   // 16-byte chunks per row
+    if constexpr (CH >= 16) return row & 15;
+    else return (row / (16 / CH)) & (CH - 1);
+}
+
+template <typename T, int CIN, int COUT, int VT>
+struct RowShape {
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int RB = CIN * ES;                // bytes per feature / weight row
+    static constexpr int CH = RB / 16;                 // chunks per row
+    static constexpr int RPI = 1024 / RB;              // rows per 1 KB load instruction
+    static constexpr int EPC = 16 / ES;
+    static constexpr int G = CH / 2;
+    static constexpr int RT = COUT / 32;
+    static constexpr int ROWS = VT * 32;               // gathered rows per wave
+    static constexpr int W_TAP = COUT * RB;            // bytes of one weight tap
+    static constexpr bool RESIDENT = 27 * W_TAP <= 65536;
+    static constexpr int WBUF = RESIDENT ? 27 : 2;
+    static constexpr int VOX_PER_BLOCK = 4 * ROWS;
+    static constexpr int NBR_BYTES = VOX_PER_BLOCK * 27 * 4;
+    static constexpr int LDS = WBUF * W_TAP + 4 * ROWS * RB + NBR_BYTES;
+    static_assert(RB >= 64 && RB <= 1024 && (RB & (RB - 1)) == 0, "row size");
+};
+
+template <typename T, int CIN, int COUT, int VT>
+__global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ feats,
+                                                        const T *__restrict__ w,
+                                                        const float *__restrict__ bias,
+                                                        const int32_t *__restrict__ nbr,
+                                                        T *__restrict__ out, int64_t n, int flip)
+{
+    using S = RowShape<T, CIN, COUT, VT>;
+    constexpr int RB = S::RB, CH = S::CH, RPI = S::RPI, EPC = S::EPC, G = S::G, RT = S::RT;
+    constexpr int ROWS = S::ROWS;
+    __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
+    char *sW = lds;                                             // [WBUF][COUT rows][RB]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    char *sF = lds + S::WBUF * S::W_TAP + wave * ROWS * RB;     // this wave's [ROWS][RB]
+    const int32_t *sN = (const int32_t *)(lds + S::WBUF * S::W_TAP + 4 * ROWS * RB);  // [block voxels][27]
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t vbase = ((int64_t)blockIdx.x * 4 + wave) * ROWS;
+
+    // weight tap k -> LDS buffer buf, whole rows, swizzled
+    auto stage_w = [&](int k, int buf) {
+        const int kw = flip ? 26 - k : k;
+        constexpr int NI = COUT / RPI;                          // 1 KB instructions per tap
+        for (int i = wave; i < NI; i += 4) {
+            const int o = i * RPI + lane / CH;
+            const int c = (lane % CH) ^ swz<RB>(o);
+            const T *src = w + ((int64_t)o * 27 + kw) * CIN + c * EPC;
+            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(sW + buf * S::W_TAP + i * 1024), 16, 0, 0);
+        }
+    };
+    // this wave's neighbour rows for tap k -> its LDS region; returns whether any exists
+    auto gather = [&](int k) -> bool {
+        int32_t j = -1;
+        if (lane < ROWS && vbase + lane < n) {
+            j = sN[(wave * ROWS + lane) * 27 + k];
+            if ((uint32_t)j >= (uint64_t)n) j = -1;
+        }
+        const bool any = __any(j >= 0);
+        if (any) {
+#pragma unroll
+            for (int i = 0; i < ROWS / RPI; ++i) {
+                const int row = i * RPI + lane / CH;
+                const int jr = __shfl(j, row, 64);
+                const int c = (lane % CH) ^ swz<RB>(row);
+                const void *src = jr >= 0 ? (const void *)(feats + (int64_t)jr * CIN + c * EPC)
+                                          : (const void *)((const char *)g_zero_row + c * 16);
+                __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(sF + i * 1024), 16, 0, 0);
+            }
+        }
+        return any;
+    };
+
+    floatx16 acc[RT][VT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < VT; ++t)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[r][t][q] = 0.f;
+
+    if constexpr (S::RESIDENT) {
+        for (int k = 0; k < 27; ++k) stage_w(k, k);
+    } else {
+        stage_w(0, 0);
+    }
+    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, (int64_t)blockIdx.x * S::VOX_PER_BLOCK,
+                                lds + S::WBUF * S::W_TAP + 4 * ROWS * RB, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    bool any = gather(0);
+    for (int k = 0; k < 27; ++k) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into LDS have landed
+        __syncthreads();                 // ... and everyone's; buffer (k+1)&1 is free
+        if constexpr (!S::RESIDENT) {
+            if (k + 1 < 27) stage_w(k + 1, (k + 1) & 1);
+        }
+        uint4 F[VT][G];
+        if (any) {
+#pragma unroll
+            for (int t = 0; t < VT; ++t)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int row = 32 * t + l32;
+                    F[t][g] = *(const uint4 *)(sF + row * RB + (((2 * g + half) ^ swz<RB>(row)) << 4));
+                }
+        }
+        SC_WAIT_LGKM0();                 // fragments are in registers: the region may be refilled
+        const bool any_now = any;
+        any = (k + 1 < 27) ? gather(k + 1) : false;
+        if (any_now) {
+            const char *wb = sW + (S::RESIDENT ? k : (k & 1)) * S::W_TAP;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    const int o = 32 * r + l32;
+                    const uint4 a = *(const uint4 *)(wb + o * RB + (((2 * g + half) ^ swz<RB>(o)) << 4));
+#pragma unroll
+                    for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], a, F[t][g]);
+                }
+        }
     }
 
 #pragma unroll
@@ -355,25 +543,32 @@ static int launch_lowc(const void *f, const void *w, const float *b, const int32
     return fail(SUBMCONV_E_UNSUPPORTED, "lowc kernel: Cin must be a power of two <= 32");
 }
 
+template <typename T, int CIN, int COUT>
+static int launch_mfma_tt(const void *f, const void *w, const float *b, const int32_t *nbr, void *o,
+                          int64_t n, int flip, hipStream_t s)
+{
+    constexpr int VT = (sizeof(T) == 4 && (CIN >= 128 || COUT >= 128)) ? 1 : 2;
+    if constexpr (RowShape<T, CIN, COUT, VT>::LDS <= 160 * 1024) {
+        constexpr int per_block = RowShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
+        const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
+        hipLaunchKernelGGL((k_conv_mfma_rows<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
+                           (const T *)f, (const T *)w, b, nbr, (T *)o, n, flip);
+    } else {
+        constexpr int per_block = MfmaShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
+        const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
+        hipLaunchKernelGGL((k_conv_mfma<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
+                           (const T *)f, (const T *)w, b, nbr, (T *)o, n, flip);
+    }
+    SC_LAUNCHED("conv_mfma");
+    return SUBMCONV_OK;
+}
+
 template <int CIN, int COUT>
 static int launch_mfma_t(const void *f, const void *w, const float *b, const int32_t *nbr, void *o,
                          int64_t n, int dtype, int flip, hipStream_t s)
 {
-    if (dtype == SUBMCONV_BF16) {
-        constexpr int VT = 2;
-        constexpr int per_block = MfmaShape<uint16_t, CIN, COUT, VT>::VOX_PER_BLOCK;
-        const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
-        hipLaunchKernelGGL((k_conv_mfma<uint16_t, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
-                           (const uint16_t *)f, (const uint16_t *)w, b, nbr, (uint16_t *)o, n, flip);
-    } else {
-        constexpr int VT = (CIN >= 128 || COUT >= 128) ? 1 : 2;
-        constexpr int per_block = MfmaShape<float, CIN, COUT, VT>::VOX_PER_BLOCK;
-        const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
-        hipLaunchKernelGGL((k_conv_mfma<float, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
-                           (const float *)f, (const float *)w, b, nbr, (float *)o, n, flip);
-    }
-    SC_LAUNCHED("conv_mfma");
-    return SUBMCONV_OK;
+    if (dtype == SUBMCONV_BF16) return launch_mfma_tt<uint16_t, CIN, COUT>(f, w, b, nbr, o, n, flip, s);
+    return launch_mfma_tt<float, CIN, COUT>(f, w, b, nbr, o, n, flip, s);
 }
 
 template <int CIN>

@@ -210,9 +210,10 @@ static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, 
     do {
         if (hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
         const unsigned grid = (unsigned)((n + 255) / 256);
+        const bool in_b = radix_sort_passes(n, nbits) & 1;
         hipLaunchKernelGGL(k_s2d_pack<K>, dim3(grid), dim3(256), 0, s, (const int4 *)coords, n, res,
-                           batch, rbc, ka, va, st);
-        if ((status = radix_sort_pairs<K>(ka, va, kb_, vb_, n, nbits, sc + o_sort, s)) != SUBMCONV_OK) break;
+                           batch, rbc, in_b ? kb_ : ka, in_b ? vb_ : va, st);
+        if ((status = radix_sort_pairs<K>(ka, va, kb_, vb_, n, nbits, sc + o_sort, s, in_b)) != SUBMCONV_OK) break;
         hipLaunchKernelGGL(k_s2d_heads<K>, dim3(grid), dim3(256), 0, s, ka, n, head, st);
         if ((status = exclusive_scan_u32(head, seg, n, tot, sc + o_scan, s)) != SUBMCONV_OK) break;
         hipLaunchKernelGGL(k_excl_to_seg, dim3(grid), dim3(256), 0, s, head, seg, n);

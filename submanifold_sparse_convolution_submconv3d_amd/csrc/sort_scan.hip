@@ -143,20 +143,32 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort_scatter(
     }
 }
 
+int radix_sort_passes(int64_t n, int nbits)
+{
+    if (n <= 1 || nbits <= 0) return 0;
+    return (nbits + MAX_DIGIT_BITS - 1) / MAX_DIGIT_BITS;
+}
+
 template <typename K>
 int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int64_t n, int nbits,
-                     void *scratch, hipStream_t stream)
+                     void *scratch, hipStream_t stream, bool input_in_b)
 {
-    if (n <= 1 || nbits <= 0) return SUBMCONV_OK;
-    const int npass = (nbits + MAX_DIGIT_BITS - 1) / MAX_DIGIT_BITS;
+    const int npass = radix_sort_passes(n, nbits);
+    if (npass == 0) {
+        if (input_in_b && n > 0) {
+            SC_HIP(hipMemcpyAsync(keys_a, keys_b, (size_t)n * sizeof(K), hipMemcpyDeviceToDevice, stream));
+            SC_HIP(hipMemcpyAsync(vals_a, vals_b, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
+        }
+        return SUBMCONV_OK;
+    }
     const int dbits = (nbits + npass - 1) / npass;
     const int bins = 1 << dbits;
     const int ntiles = (int)sort_tiles(n);
     uint32_t *hist = (uint32_t *)scratch;
     uint32_t *offs = hist + (size_t)MAX_BINS * ntiles;
     uint32_t *bin_total = offs + (size_t)MAX_BINS * ntiles;
-    K *src_k = keys_a, *dst_k = keys_b;
-    int32_t *src_v = vals_a, *dst_v = vals_b;
+    K *src_k = input_in_b ? keys_b : keys_a, *dst_k = input_in_b ? keys_a : keys_b;
+    int32_t *src_v = input_in_b ? vals_b : vals_a, *dst_v = input_in_b ? vals_a : vals_b;
     for (int p = 0; p < npass; ++p) {
         const int shift = p * dbits;
         hipLaunchKernelGGL(k_sort_hist<K>, dim3(ntiles), dim3(SORT_THREADS), 0, stream, src_k, n,
@@ -171,7 +183,7 @@ int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int
         K *tk = src_k; src_k = dst_k; dst_k = tk;
         int32_t *tv = src_v; src_v = dst_v; dst_v = tv;
     }
-    if (src_k != keys_a) {  // odd pass count: result is in the b buffers
+    if (src_k != keys_a) {  // the pass count left the result in the b buffers
         SC_HIP(hipMemcpyAsync(keys_a, src_k, (size_t)n * sizeof(K), hipMemcpyDeviceToDevice, stream));
         SC_HIP(hipMemcpyAsync(vals_a, src_v, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToDevice,
                               stream));
@@ -180,9 +192,9 @@ int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int
 }
 
 template int radix_sort_pairs<uint32_t>(uint32_t *, int32_t *, uint32_t *, int32_t *, int64_t, int,
-                                        void *, hipStream_t);
+                                        void *, hipStream_t, bool);
 template int radix_sort_pairs<uint64_t>(uint64_t *, int32_t *, uint64_t *, int32_t *, int64_t, int,
-                                        void *, hipStream_t);
+                                        void *, hipStream_t, bool);
 
 // --------------------------------------------------------------------------
 // exclusive scan of uint32 (tiles of 2048, then the tile sums, then add back)
@@ -197,7 +209,11 @@ size_t scan_scratch_bytes(int64_t n)
     return (size_t)(tiles + 1) * sizeof(uint32_t) + 256;
 }
 
-// Per tile: exclusive scan in place into `out`, tile sum into sums[tile].
+// Per tile: exclusive scan in place into `out`, tile sum into sums[tile].  With
+// POPC the scanned value of an input word is its number of set bits.
+// MODE 0: the values themselves; 1: set bits of 32-bit words; 2: set bits of
+// 64-bit words (`in` then points at n 64-bit words).
+template <int MODE>
 __global__ __launch_bounds__(256) void k_scan_tiles(const uint32_t *__restrict__ in,
                                                     uint32_t *__restrict__ out, int64_t n,
                                                     uint32_t *__restrict__ sums)
@@ -208,7 +224,13 @@ __global__ __launch_bounds__(256) void k_scan_tiles(const uint32_t *__restrict__
     uint32_t local = 0;
 #pragma unroll
     for (int e = 0; e < SCAN_ITEMS; ++e) {
-        v[e] = (base + e < n) ? in[base + e] : 0u;
+        if (MODE == 2) {
+            const uint64_t x = (base + e < n) ? ((const uint64_t *)in)[base + e] : 0ull;
+            v[e] = (uint32_t)__popcll(x);
+        } else {
+            const uint32_t x = (base + e < n) ? in[base + e] : 0u;
+            v[e] = MODE == 1 ? (uint32_t)__popc(x) : x;
+        }
         local += v[e];
     }
     uint32_t total;
@@ -249,7 +271,7 @@ __global__ __launch_bounds__(256) void k_scan_add(uint32_t *__restrict__ out, in
 }
 
 int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *total_dev,
-                       void *scratch, hipStream_t stream)
+                       void *scratch, hipStream_t stream, int input_mode)
 {
     if (n <= 0) {
         if (total_dev) SC_HIP(hipMemsetAsync(total_dev, 0, sizeof(uint32_t), stream));
@@ -257,7 +279,12 @@ int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *t
     }
     const int64_t tiles = (n + SCAN_TILE - 1) / SCAN_TILE;
     uint32_t *sums = (uint32_t *)scratch;
-    hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)tiles), dim3(256), 0, stream, in, out, n, sums);
+    if (input_mode == SCAN_POPC64)
+        hipLaunchKernelGGL(k_scan_tiles<2>, dim3((unsigned)tiles), dim3(256), 0, stream, in, out, n, sums);
+    else if (input_mode == SCAN_POPC32)
+        hipLaunchKernelGGL(k_scan_tiles<1>, dim3((unsigned)tiles), dim3(256), 0, stream, in, out, n, sums);
+    else
+        hipLaunchKernelGGL(k_scan_tiles<0>, dim3((unsigned)tiles), dim3(256), 0, stream, in, out, n, sums);
     SC_LAUNCHED("scan_tiles");
     hipLaunchKernelGGL(k_scan_sums, dim3(1), dim3(256), 0, stream, sums, tiles, total_dev);
     SC_LAUNCHED("scan_sums");

@@ -47,6 +47,44 @@ def test_map_random_sets(n, res, batch, seed):
     assert rb.taps_present == int((got >= 0).sum())
 
 
+# The builder picks one of four strategies by set size and key-space size:
+#   small bitmap (n <= 2048, <= 16 key bits), small sort (n <= 2048, more bits),
+#   occupancy bitmap + rank (dense key space), radix sort + windowed search (sparse).
+@pytest.mark.parametrize("n,res,batch,seed,shift,extent", [
+    (700, 16, 1, 20, 0, 12),          # small bitmap
+    (1500, 64, 2, 21, 30, 12),        # small sort (19 key bits)
+    (30000, 48, 3, 22, 0, 48),        # occupancy bitmap
+    (6000, 1024, 1, 23, 970, 24),     # radix sort + windows (30 key bits, sparse)
+    (150000, 1024, 2, 24, 976, 48),   # radix sort + windows, many blocks
+])
+def test_map_build_strategies(n, res, batch, seed, shift, extent):
+    # a dense cluster (neighbours exist) of the given extent, `shift` voxels into the grid
+    c = synth.random_coords(n, extent, batch, seed)
+    c[:, 1:] += shift
+    c = c[synth.shuffle_rows(len(c), seed)]
+    note("map strategy n=%d res=%d batch=%d" % (n, res, batch))
+    got = build(c, res, batch).neighbors().cpu().numpy()
+    expect = ref.neighbor_table(c, res, batch) if res > 256 else dense.neighbor_table(c, res, batch)
+    assert (expect >= 0).sum() > 2 * n
+    np.testing.assert_array_equal(got, expect)
+
+
+@pytest.mark.parametrize("res,n,shift", [(16, 500, 0), (64, 1500, 0), (48, 3000, 0), (1024, 3000, 970)])
+def test_map_duplicate_and_range_each_strategy(res, n, shift):
+    base = synth.random_coords(n, min(res, 48), 1, 30)
+    base[:, 1:] += shift
+    dup = np.concatenate([base, base[17:18]])
+    note("map dup res=%d" % res)
+    with pytest.raises(sc.SubmconvError) as e:
+        build(dup, res, 1)
+    assert e.value.status == -3
+    bad = base.copy()
+    bad[5, 3] = res
+    with pytest.raises(sc.SubmconvError) as e:
+        build(bad, res, 1)
+    assert e.value.status == -2
+
+
 def test_map_hand_example():
     c = np.array([[0, 1, 1, 1], [0, 1, 1, 2], [0, 2, 1, 1], [0, 3, 3, 3]], np.int32)
     note("map hand example")
