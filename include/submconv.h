@@ -90,12 +90,14 @@ typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
 int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t batch,
                        void *stream, submconv_rulebook **out_rb);
 
-/* Device pointer to the rulebook's nbr table int32 [n,27] (owned by the
- * rulebook, valid until it is freed) and its row count. */
-int submconv_rulebook_neighbors(const submconv_rulebook *rb, const int32_t **nbr, int64_t *n);
+/* Device pointer to the nbr table int32 [n,27] in input row order (owned by the
+ * rulebook, valid until it is freed) and its row count.  The rulebook keeps its
+ * table by sorted position; the input-order copy is built on the first call, on
+ * `stream` (one allocation and one kernel), and reused afterwards. */
+int submconv_rulebook_neighbors(submconv_rulebook *rb, void *stream, const int32_t **nbr, int64_t *n);
 
-/* Copy the rulebook's nbr table into caller memory dst (device int32 [n,27]),
- * enqueued on `stream`. */
+/* Write the nbr table int32 [n,27] in input row order into caller memory dst
+ * (device), enqueued on `stream`. */
 int submconv_rulebook_copy_neighbors(const submconv_rulebook *rb, int32_t *dst, void *stream);
 
 /* Host-side facts of a rulebook: rows, grid, batch count, and P = number of

@@ -69,7 +69,7 @@ def load_library():
     i64p, i32p = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
     sig = {
         "submconv_build_map": [vp, i64, i32, i32, vp, ctypes.POINTER(vp)],
-        "submconv_rulebook_neighbors": [vp, ctypes.POINTER(vp), i64p],
+        "submconv_rulebook_neighbors": [vp, vp, ctypes.POINTER(vp), i64p],
         "submconv_rulebook_copy_neighbors": [vp, vp, vp],
         "submconv_rulebook_info": [vp, i64p, i32p, i32p, i64p],
         "submconv_rulebook_free": [vp, vp],

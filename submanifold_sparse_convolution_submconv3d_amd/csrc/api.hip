@@ -9,9 +9,10 @@
 
 namespace sc {
 int build_map(const int32_t *coords, submconv_rulebook *rb, hipStream_t stream);
-int launch_forward(const void *feats, const void *w, const float *bias, const int32_t *nbr,
-                   void *out, int64_t n, int cin, int cout, int dtype, int flip, int variant,
-                   hipStream_t s);
+int launch_forward(const void *feats, const void *w, const float *bias,
+                   const submconv_rulebook *rb, void *out, int cin, int cout, int dtype, int flip,
+                   int variant, hipStream_t s);
+int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s);
 int choose_forward_kernel(int cin, int cout, int dtype);
 int subdivide(const int32_t *coords, const void *feats, int64_t n, int c, int dtype,
               int32_t *out_coords, void *out_feats, hipStream_t s);
@@ -139,15 +140,19 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     r->device = dev;
     int st = keep_pool(dev);
     if (st != SUBMCONV_OK) { delete r; return st; }
+    r->ntiles = (n + 255) / 256;
+    r->nbr_in = nullptr;
     const size_t kbytes = (((size_t)n * r->key_bytes) + 255) & ~size_t(255);
     const size_t pbytes = (((size_t)n * 4) + 255) & ~size_t(255);
     // +1 KB: kernels copy table rows in 16-byte chunks that may run past the last row
     const size_t nbytes = ((((size_t)n * 27 * 4) + 255) & ~size_t(255)) + 1024;
-    st = dev_alloc(&r->block, kbytes + pbytes + nbytes, s);
+    const size_t mbytes = (size_t)r->ntiles * 32 * 4 + 256;
+    st = dev_alloc(&r->block, kbytes + pbytes + nbytes + mbytes, s);
     if (st != SUBMCONV_OK) { delete r; return st; }
     r->keys = r->block;
     r->perm = (int32_t *)((char *)r->block + kbytes);
-    r->nbr = (int32_t *)((char *)r->block + kbytes + pbytes);
+    r->nbr_sp = (int32_t *)((char *)r->block + kbytes + pbytes);
+    r->meta = (int32_t *)((char *)r->block + kbytes + pbytes + nbytes);
     if (n > 0) {
         st = build_map(coords, r, s);
         if (st != SUBMCONV_OK) {
@@ -160,10 +165,17 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     return SUBMCONV_OK;
 }
 
-int submconv_rulebook_neighbors(const submconv_rulebook *rb, const int32_t **nbr, int64_t *n)
+int submconv_rulebook_neighbors(submconv_rulebook *rb, void *stream, const int32_t **nbr, int64_t *n)
 {
     if (!rb || !nbr || !n) return fail(SUBMCONV_E_INVALID_ARG, "NULL argument");
-    *nbr = rb->nbr;
+    if (!rb->nbr_in && rb->n > 0) {
+        void *p = nullptr;
+        SC_CHECK(dev_alloc(&p, (size_t)rb->n * 27 * 4, (hipStream_t)stream));
+        const int st = input_order_table(rb, (int32_t *)p, (hipStream_t)stream);
+        if (st != SUBMCONV_OK) { dev_free(p, (hipStream_t)stream); return st; }
+        rb->nbr_in = (int32_t *)p;
+    }
+    *nbr = rb->nbr_in;
     *n = rb->n;
     return SUBMCONV_OK;
 }
@@ -174,9 +186,8 @@ int submconv_rulebook_copy_neighbors(const submconv_rulebook *rb, int32_t *dst, 
     if (rb->n == 0) return SUBMCONV_OK;
     if (!dst) return fail(SUBMCONV_E_INVALID_ARG, "dst is NULL");
     const size_t bytes = (size_t)rb->n * 27 * 4;
-    if (overlaps(dst, bytes, rb->nbr, bytes)) return fail(SUBMCONV_E_ALIAS, "dst overlaps the table");
-    SC_HIP(hipMemcpyAsync(dst, rb->nbr, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
-    return SUBMCONV_OK;
+    if (overlaps(dst, bytes, rb->block, (size_t)rb->n * 40)) return fail(SUBMCONV_E_ALIAS, "dst overlaps the rulebook");
+    return input_order_table(rb, dst, (hipStream_t)stream);
 }
 
 int submconv_rulebook_info(const submconv_rulebook *rb, int64_t *n, int32_t *res, int32_t *batch,
@@ -193,6 +204,7 @@ int submconv_rulebook_info(const submconv_rulebook *rb, int64_t *n, int32_t *res
 int submconv_rulebook_free(submconv_rulebook *rb, void *stream)
 {
     if (!rb) return SUBMCONV_OK;
+    dev_free(rb->nbr_in, (hipStream_t)stream);
     dev_free(rb->block, (hipStream_t)stream);
     delete rb;
     return SUBMCONV_OK;
@@ -222,7 +234,7 @@ int submconv_forward_variant(const void *feats, const void *weight, const float 
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev != rb->device)
         return fail(SUBMCONV_E_INVALID_ARG, "rulebook lives on device %d, current device is %d", rb->device, dev);
-    return launch_forward(feats, weight, bias, rb->nbr, out, n, cin, cout, dtype, flip, variant,
+    return launch_forward(feats, weight, bias, rb, out, cin, cout, dtype, flip, variant,
                           (hipStream_t)stream);
 }
 

@@ -163,7 +163,8 @@ __device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t *lds
 
 }  // namespace sc
 
-// Rulebook: library-owned device memory for one coordinate set.
+// Rulebook: library-owned device memory for one coordinate set.  Everything is
+// indexed by sorted position s (C order of the packed key).
 struct submconv_rulebook {
     int64_t n;
     int32_t res;
@@ -172,9 +173,12 @@ struct submconv_rulebook {
     int32_t nbits;      // significant key bits
     int32_t key_bytes;  // 4 or 8
     int32_t device;
-    int64_t taps;       // P: present entries of nbr
+    int64_t taps;       // P: present entries of the table
+    int64_t ntiles;     // tiles of 256 sorted voxels
     void *block;        // single allocation holding the arrays below
     void *keys;         // sorted keys [n]
-    int32_t *perm;      // sorted position -> original row [n]
-    int32_t *nbr;       // [n,27] in original row order
+    int32_t *perm;      // sorted position -> input row [n]
+    int32_t *nbr_sp;    // [n,27]: sorted position of each neighbour, or -1 (padded allocation)
+    int32_t *meta;      // [ntiles,32]: tile neighbourhood ranges (see mapbuild.hip)
+    int32_t *nbr_in;    // [n,27] input-order table of input rows, built on first request (or null)
 };

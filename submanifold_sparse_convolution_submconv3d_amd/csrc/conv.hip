@@ -5,6 +5,10 @@
 // over the taps k with nbr[i, k] >= 0, k' = k (correlation) or 26 - k (the
 // mirrored kernel), W in KRSC layout [Cout, 27, Cin] (lato.2_mrp_mlx working
 // notes, "Key facts" for the layout, commit summary for the mirror flag).
+// Voxels are visited in sorted order s (the rulebook's order): the output row is
+// perm[s] and the row of neighbour tap k is perm[nbr_sp[s][k]].  For inputs that
+// arrive in grid order perm is the identity; otherwise sorted order still keeps
+// a block's neighbourhoods spatially compact.
 // All kernels are output-stationary: a voxel's output row is accumulated in
 // registers over its 27 taps and written once, so no atomics are needed (the
 // output set equals the input set).  Accumulation is fp32; a bf16 output is
@@ -39,16 +43,21 @@ __global__ __launch_bounds__(256) void k_conv_generic(const T *__restrict__ feat
                                                       const T *__restrict__ w,
                                                       const float *__restrict__ bias,
                                                       const int32_t *__restrict__ nbr,
+                                                      const int32_t *__restrict__ perm,
                                                       T *__restrict__ out, int64_t n, int cin,
                                                       int cout, int flip)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t i = idx / cout;
-    const int o = (int)(idx - i * cout);
-    if (i >= n) return;
+    const int64_t s = idx / cout;
+    const int o = (int)(idx - s * cout);
+    if (s >= n) return;
+    const int64_t i = perm[s];
+    if ((uint64_t)i >= (uint64_t)n) return;
     float acc = 0.f;
     for (int k = 0; k < 27; ++k) {
-        const int32_t j = nbr[i * 27 + k];
+        const int32_t p = nbr[s * 27 + k];
+        if ((uint32_t)p >= (uint64_t)n) continue;
+        const int32_t j = perm[p];
         if ((uint32_t)j >= (uint64_t)n) continue;
         const int kw = flip ? 26 - k : k;
         const T *wr = w + ((int64_t)o * 27 + kw) * cin;
@@ -68,6 +77,7 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
                                                    const T *__restrict__ w,
                                                    const float *__restrict__ bias,
                                                    const int32_t *__restrict__ nbr,
+                                                   const int32_t *__restrict__ perm,
                                                    T *__restrict__ out, int64_t n, int flip)
 {
     static_assert(COUT <= 64 && (64 % COUT) == 0, "group must divide the wave");
@@ -86,11 +96,13 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
     const int64_t stride = (int64_t)gridDim.x * VPB;
     // every lane of a wave runs the same number of iterations (shuffles need all lanes)
     for (int64_t i0 = (int64_t)blockIdx.x * VPB; i0 < n; i0 += stride) {
-        const int64_t i = i0 + threadIdx.x / COUT;
-        const bool live = i < n;
+        const int64_t s = i0 + threadIdx.x / COUT;
+        const int64_t i = s < n ? (int64_t)perm[s] : -1;
+        const bool live = (uint64_t)i < (uint64_t)n;
         float acc = 0.f;
         for (int k = 0; k < 27; ++k) {
-            int32_t j = live ? nbr[i * 27 + k] : -1;
+            int32_t j = live ? nbr[s * 27 + k] : -1;
+            j = (uint32_t)j < (uint64_t)n ? perm[j] : -1;
             if ((uint32_t)j >= (uint64_t)n) j = -1;
             float f[PER];
 #pragma unroll
@@ -209,6 +221,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
                                                    const T *__restrict__ w,
                                                    const float *__restrict__ bias,
                                                    const int32_t *__restrict__ nbr,
+                                                   const int32_t *__restrict__ perm,
                                                    T *__restrict__ out, int64_t n, int flip)
 {
     using S = MfmaShape<T, CIN, COUT, VT>;
@@ -236,6 +249,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
         for (int t = 0; t < VT; ++t) {
             const int64_t v = vbase + 32 * t + l32;
             int32_t r = v < n ? sN[(wave * VT * 32 + 32 * t + l32) * 27 + k] : -1;
+            r = (uint32_t)r < (uint64_t)n ? perm[r] : -1;
             if ((uint32_t)r >= (uint64_t)n) r = -1;
             j[t] = r;
             any |= r >= 0;
@@ -307,6 +321,8 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     for (int t = 0; t < VT; ++t) {
         const int64_t v = vbase + 32 * t + l32;
         if (v >= n) continue;
+        const int64_t orow = perm[v];
+        if ((uint64_t)orow >= (uint64_t)n) continue;
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -314,7 +330,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
                 const int o = 32 * r + 8 * q + 4 * half;
                 float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (bias) b = *(const float4 *)(bias + o);
-                Store4<T>::put(out + v * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
+                Store4<T>::put(out + orow * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
                                acc[r][t][4 * q + 2] + b.z, acc[r][t][4 * q + 3] + b.w);
             }
     }
@@ -367,6 +383,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
                                                         const T *__restrict__ w,
                                                         const float *__restrict__ bias,
                                                         const int32_t *__restrict__ nbr,
+                                                        const int32_t *__restrict__ perm,
                                                         T *__restrict__ out, int64_t n, int flip)
 {
     using S = RowShape<T, CIN, COUT, VT>;
@@ -396,6 +413,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
         int32_t j = -1;
         if (lane < ROWS && vbase + lane < n) {
             j = sN[(wave * ROWS + lane) * 27 + k];
+            j = (uint32_t)j < (uint64_t)n ? perm[j] : -1;
             if ((uint32_t)j >= (uint64_t)n) j = -1;
         }
         const bool any = __any(j >= 0);
@@ -468,6 +486,8 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     for (int t = 0; t < VT; ++t) {
         const int64_t v = vbase + 32 * t + l32;
         if (v >= n) continue;
+        const int64_t orow = perm[v];
+        if ((uint64_t)orow >= (uint64_t)n) continue;
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -475,7 +495,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
                 const int o = 32 * r + 8 * q + 4 * half;
                 float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (bias) b = *(const float4 *)(bias + o);
-                Store4<T>::put(out + v * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
+                Store4<T>::put(out + orow * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
                                acc[r][t][4 * q + 2] + b.z, acc[r][t][4 * q + 3] + b.w);
             }
     }
@@ -490,61 +510,62 @@ static bool mfma_size(int c) { return c == 32 || c == 64 || c == 128; }
 
 template <typename T>
 static int launch_generic(const void *feats, const void *w, const float *bias, const int32_t *nbr,
-                          void *out, int64_t n, int cin, int cout, int flip, hipStream_t s)
+                          const int32_t *perm, void *out, int64_t n, int cin, int cout, int flip,
+                          hipStream_t s)
 {
     const int64_t total = n * cout;
     const unsigned grid = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(k_conv_generic<T>, dim3(grid), dim3(256), 0, s, (const T *)feats,
-                       (const T *)w, bias, nbr, (T *)out, n, cin, cout, flip);
+                       (const T *)w, bias, nbr, perm, (T *)out, n, cin, cout, flip);
     SC_LAUNCHED("conv_generic");
     return SUBMCONV_OK;
 }
 
 template <typename T, int CIN, int COUT>
 static int launch_lowc_t(const void *feats, const void *w, const float *bias, const int32_t *nbr,
-                         void *out, int64_t n, int flip, hipStream_t s)
+                         const int32_t *perm, void *out, int64_t n, int flip, hipStream_t s)
 {
     constexpr int VPB = 256 / COUT;
     int64_t blocks = (n + VPB - 1) / VPB;
     if (blocks > 2048) blocks = 2048;  // grid-stride beyond: amortises the weight staging
     hipLaunchKernelGGL((k_conv_lowc<T, CIN, COUT>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const T *)feats, (const T *)w, bias, nbr, (T *)out, n, flip);
+                       (const T *)feats, (const T *)w, bias, nbr, perm, (T *)out, n, flip);
     SC_LAUNCHED("conv_lowc");
     return SUBMCONV_OK;
 }
 
 template <typename T, int CIN>
-static int launch_lowc_cout(const void *f, const void *w, const float *b, const int32_t *nbr,
+static int launch_lowc_cout(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm,
                             void *o, int64_t n, int cout, int flip, hipStream_t s)
 {
     switch (cout) {
-    case 1: return launch_lowc_t<T, CIN, 1>(f, w, b, nbr, o, n, flip, s);
-    case 2: return launch_lowc_t<T, CIN, 2>(f, w, b, nbr, o, n, flip, s);
-    case 4: return launch_lowc_t<T, CIN, 4>(f, w, b, nbr, o, n, flip, s);
-    case 8: return launch_lowc_t<T, CIN, 8>(f, w, b, nbr, o, n, flip, s);
-    case 16: return launch_lowc_t<T, CIN, 16>(f, w, b, nbr, o, n, flip, s);
-    case 32: return launch_lowc_t<T, CIN, 32>(f, w, b, nbr, o, n, flip, s);
+    case 1: return launch_lowc_t<T, CIN, 1>(f, w, b, nbr, perm, o, n, flip, s);
+    case 2: return launch_lowc_t<T, CIN, 2>(f, w, b, nbr, perm, o, n, flip, s);
+    case 4: return launch_lowc_t<T, CIN, 4>(f, w, b, nbr, perm, o, n, flip, s);
+    case 8: return launch_lowc_t<T, CIN, 8>(f, w, b, nbr, perm, o, n, flip, s);
+    case 16: return launch_lowc_t<T, CIN, 16>(f, w, b, nbr, perm, o, n, flip, s);
+    case 32: return launch_lowc_t<T, CIN, 32>(f, w, b, nbr, perm, o, n, flip, s);
     }
     return fail(SUBMCONV_E_UNSUPPORTED, "lowc kernel: Cout must be a power of two <= 32");
 }
 
 template <typename T>
-static int launch_lowc(const void *f, const void *w, const float *b, const int32_t *nbr, void *o,
+static int launch_lowc(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
                        int64_t n, int cin, int cout, int flip, hipStream_t s)
 {
     switch (cin) {
-    case 1: return launch_lowc_cout<T, 1>(f, w, b, nbr, o, n, cout, flip, s);
-    case 2: return launch_lowc_cout<T, 2>(f, w, b, nbr, o, n, cout, flip, s);
-    case 4: return launch_lowc_cout<T, 4>(f, w, b, nbr, o, n, cout, flip, s);
-    case 8: return launch_lowc_cout<T, 8>(f, w, b, nbr, o, n, cout, flip, s);
-    case 16: return launch_lowc_cout<T, 16>(f, w, b, nbr, o, n, cout, flip, s);
-    case 32: return launch_lowc_cout<T, 32>(f, w, b, nbr, o, n, cout, flip, s);
+    case 1: return launch_lowc_cout<T, 1>(f, w, b, nbr, perm, o, n, cout, flip, s);
+    case 2: return launch_lowc_cout<T, 2>(f, w, b, nbr, perm, o, n, cout, flip, s);
+    case 4: return launch_lowc_cout<T, 4>(f, w, b, nbr, perm, o, n, cout, flip, s);
+    case 8: return launch_lowc_cout<T, 8>(f, w, b, nbr, perm, o, n, cout, flip, s);
+    case 16: return launch_lowc_cout<T, 16>(f, w, b, nbr, perm, o, n, cout, flip, s);
+    case 32: return launch_lowc_cout<T, 32>(f, w, b, nbr, perm, o, n, cout, flip, s);
     }
     return fail(SUBMCONV_E_UNSUPPORTED, "lowc kernel: Cin must be a power of two <= 32");
 }
 
 template <typename T, int CIN, int COUT>
-static int launch_mfma_tt(const void *f, const void *w, const float *b, const int32_t *nbr, void *o,
+static int launch_mfma_tt(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
                           int64_t n, int flip, hipStream_t s)
 {
     constexpr int VT = (sizeof(T) == 4 && (CIN >= 128 || COUT >= 128)) ? 1 : 2;
@@ -552,44 +573,44 @@ static int launch_mfma_tt(const void *f, const void *w, const float *b, const in
         constexpr int per_block = RowShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
         const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
         hipLaunchKernelGGL((k_conv_mfma_rows<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
-                           (const T *)f, (const T *)w, b, nbr, (T *)o, n, flip);
+                           (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     } else {
         constexpr int per_block = MfmaShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
         const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
         hipLaunchKernelGGL((k_conv_mfma<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
-                           (const T *)f, (const T *)w, b, nbr, (T *)o, n, flip);
+                           (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     }
     SC_LAUNCHED("conv_mfma");
     return SUBMCONV_OK;
 }
 
 template <int CIN, int COUT>
-static int launch_mfma_t(const void *f, const void *w, const float *b, const int32_t *nbr, void *o,
+static int launch_mfma_t(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
                          int64_t n, int dtype, int flip, hipStream_t s)
 {
-    if (dtype == SUBMCONV_BF16) return launch_mfma_tt<uint16_t, CIN, COUT>(f, w, b, nbr, o, n, flip, s);
-    return launch_mfma_tt<float, CIN, COUT>(f, w, b, nbr, o, n, flip, s);
+    if (dtype == SUBMCONV_BF16) return launch_mfma_tt<uint16_t, CIN, COUT>(f, w, b, nbr, perm, o, n, flip, s);
+    return launch_mfma_tt<float, CIN, COUT>(f, w, b, nbr, perm, o, n, flip, s);
 }
 
 template <int CIN>
-static int launch_mfma_cout(const void *f, const void *w, const float *b, const int32_t *nbr,
+static int launch_mfma_cout(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm,
                             void *o, int64_t n, int cout, int dtype, int flip, hipStream_t s)
 {
     switch (cout) {
-    case 32: return launch_mfma_t<CIN, 32>(f, w, b, nbr, o, n, dtype, flip, s);
-    case 64: return launch_mfma_t<CIN, 64>(f, w, b, nbr, o, n, dtype, flip, s);
-    case 128: return launch_mfma_t<CIN, 128>(f, w, b, nbr, o, n, dtype, flip, s);
+    case 32: return launch_mfma_t<CIN, 32>(f, w, b, nbr, perm, o, n, dtype, flip, s);
+    case 64: return launch_mfma_t<CIN, 64>(f, w, b, nbr, perm, o, n, dtype, flip, s);
+    case 128: return launch_mfma_t<CIN, 128>(f, w, b, nbr, perm, o, n, dtype, flip, s);
     }
     return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: Cout must be 32, 64 or 128");
 }
 
-static int launch_mfma(const void *f, const void *w, const float *b, const int32_t *nbr, void *o,
+static int launch_mfma(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
                        int64_t n, int cin, int cout, int dtype, int flip, hipStream_t s)
 {
     switch (cin) {
-    case 32: return launch_mfma_cout<32>(f, w, b, nbr, o, n, cout, dtype, flip, s);
-    case 64: return launch_mfma_cout<64>(f, w, b, nbr, o, n, cout, dtype, flip, s);
-    case 128: return launch_mfma_cout<128>(f, w, b, nbr, o, n, cout, dtype, flip, s);
+    case 32: return launch_mfma_cout<32>(f, w, b, nbr, perm, o, n, cout, dtype, flip, s);
+    case 64: return launch_mfma_cout<64>(f, w, b, nbr, perm, o, n, cout, dtype, flip, s);
+    case 128: return launch_mfma_cout<128>(f, w, b, nbr, perm, o, n, cout, dtype, flip, s);
     }
     return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: Cin must be 32, 64 or 128");
 }
@@ -602,23 +623,24 @@ int choose_forward_kernel(int cin, int cout, int dtype)
     return SUBMCONV_KERNEL_GENERIC;
 }
 
-int launch_forward(const void *feats, const void *w, const float *bias, const int32_t *nbr,
-                   void *out, int64_t n, int cin, int cout, int dtype, int flip, int variant,
-                   hipStream_t s)
+int launch_forward(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb,
+                   void *out, int cin, int cout, int dtype, int flip, int variant, hipStream_t s)
 {
+    const int64_t n = rb->n;
+    const int32_t *nbr = rb->nbr_sp, *perm = rb->perm;
     if (n == 0) return SUBMCONV_OK;
     if (variant == SUBMCONV_KERNEL_AUTO) variant = choose_forward_kernel(cin, cout, dtype);
     switch (variant) {
     case SUBMCONV_KERNEL_GENERIC:
         return dtype == SUBMCONV_F32
-                   ? launch_generic<float>(feats, w, bias, nbr, out, n, cin, cout, flip, s)
-                   : launch_generic<uint16_t>(feats, w, bias, nbr, out, n, cin, cout, flip, s);
+                   ? launch_generic<float>(feats, w, bias, nbr, perm, out, n, cin, cout, flip, s)
+                   : launch_generic<uint16_t>(feats, w, bias, nbr, perm, out, n, cin, cout, flip, s);
     case SUBMCONV_KERNEL_LOWC:
         return dtype == SUBMCONV_F32
-                   ? launch_lowc<float>(feats, w, bias, nbr, out, n, cin, cout, flip, s)
-                   : launch_lowc<uint16_t>(feats, w, bias, nbr, out, n, cin, cout, flip, s);
+                   ? launch_lowc<float>(feats, w, bias, nbr, perm, out, n, cin, cout, flip, s)
+                   : launch_lowc<uint16_t>(feats, w, bias, nbr, perm, out, n, cin, cout, flip, s);
     case SUBMCONV_KERNEL_MFMA:
-        return launch_mfma(feats, w, bias, nbr, out, n, cin, cout, dtype, flip, s);
+        return launch_mfma(feats, w, bias, nbr, perm, out, n, cin, cout, dtype, flip, s);
     }
     return fail(SUBMCONV_E_INVALID_ARG, "unknown forward kernel variant %d", variant);
 }

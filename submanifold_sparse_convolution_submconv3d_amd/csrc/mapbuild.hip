@@ -4,40 +4,46 @@
 // voxel, cached per coordinate set (lato.2_mrp_mlx working notes, commit
 // summary).  Every coordinate is validated and packed into an integer key
 // ((b << 3rb) | (z << 2rb) | (y << rb) | x); keys are sorted, and each voxel's
-// 27 neighbour keys are looked up in the sorted order.  Two device strategies:
+// 27 neighbour keys are looked up in the sorted order.
 //
-// Dense key space (2^nbits bits of occupancy bitmap affordable next to N):
-//   mark     - set the key's bit in an occupancy bitmap (atomicOr); a bit that
-//              was already set is a duplicate coordinate;
-//   scan     - exclusive scan of the bitmap words' popcounts;
+// What the rulebook keeps, all indexed by sorted position s (C order of
+// (b, z, y, x)):
+//   keys[s], perm[s] (the input row of sorted voxel s),
+//   nbr_sp[s][k]  the SORTED POSITION of the voxel at key[s] + offset(k), or -1,
+//   tile metadata  per tile of 256 sorted voxels: the merged ranges of sorted
+//                  positions that hold all the tile's neighbours, and for each
+//                  (dz, dy) row the offset from a sorted position to its place
+//                  in the concatenated ranges (so a kernel can stage the tile's
+//                  whole neighbourhood in LDS and index it directly).
+// The input-order table nbr[i][k] (input rows) is derived from these on request.
+//
+// Dense key space (2^nbits bitmap bits affordable next to N):
+//   mark     - set the key's bit in an occupancy bitmap (no-return atomicOr;
+//              lanes of a wave that hit the same word are combined first);
+//   scan     - exclusive scan of the bitmap words' popcounts; its total is the
+//              number of distinct keys, so a total below N means a duplicate;
 //   rank     - a key's sorted position is prefix[word] + popcount of the lower
 //              bits of its word: one radix pass whose digit is the whole key
 //              (histogram = bitmap, counts are 0/1 because keys are distinct);
-//              scatter key and row to their sorted position;
-//   resolve  - per voxel, in input row order, each neighbour is a bit test and,
-//              when set, the same rank query plus one read of the row at that
-//              sorted position.  The block's 256 table rows are contiguous and
-//              are written through LDS as one coalesced run.
-//
+//   resolve  - per sorted voxel, each neighbour is a bit test plus the same rank
+//              query; no gathers, and table rows are written as coalesced runs.
 // Sparse key space (huge grid, few voxels):
-//   pack + multi-pass LSD radix sort over the significant key bits, then a
-//   windowed resolve: per block of 256 consecutive sorted voxels, the x
-//   neighbours of the centre row are the adjacent sorted entries; for each of
-//   the other 8 (dz, dy) rows every target key of the block lies in
-//   [first + off - 1, last + off + 1] (off = that row's key offset), so the block
-//   copies that window of the sorted array into LDS and resolves its voxels by
-//   binary search there (a window too big for LDS is searched in place).
-//
-// Small sets (n <= 2048) run in one block and one launch.  Coordinates are
-// range-checked before packing and every neighbour coordinate is bounds-checked
-// before its key is formed, so a key never wraps into the next row, plane or
-// batch entry.
+//   pack + multi-pass LSD radix sort, then per tile of 256 sorted voxels: the x
+//   neighbours of the centre row are the adjacent sorted entries; for each of the
+//   other 8 (dz, dy) rows every target key lies in [first + off - 1, last + off + 1]
+//   (off = the row's key offset), so the block copies that window of sorted keys
+//   into LDS and binary-searches there (a window too big for LDS is searched in
+//   place).
+// Small sets (n <= 2048) build in one block.  Coordinates are range-checked
+// before packing and every neighbour coordinate is bounds-checked before its key
+// is formed, so a key never wraps into the next row, plane or batch entry.
 #include "common.h"
 
 namespace sc {
 
-constexpr int WIN_MAX = 2048;      // window keys held in LDS
+constexpr int WIN_MAX = 2048;      // window keys held in LDS (sparse path)
 constexpr int SMALL_N = 2048;      // single-block build up to this many voxels
+constexpr int SMALL_BITS = 16;     // single-block bitmap up to 2^16 bits
 
 template <typename K>
 __device__ __forceinline__ K pack_key(int b, int z, int y, int x, int rb)
@@ -46,18 +52,11 @@ __device__ __forceinline__ K pack_key(int b, int z, int y, int x, int rb)
 }
 
 template <typename K>
-__global__ __launch_bounds__(256) void k_pack(const int4 *__restrict__ coords, int64_t n, int res,
-                                              int batch, int rb, K *__restrict__ keys,
-                                              int32_t *__restrict__ rows, DevStatus *st)
+__device__ __forceinline__ bool key_valid(K key, int rb, int res, int batch)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int4 c = coords[i];  // (b, z, y, x)
-    const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
-                     (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
-    keys[i] = bad ? K(0) : pack_key<K>(c.x, c.y, c.z, c.w, rb);
-    rows[i] = (int32_t)i;
-    if (bad) atomicOr(&st->flags, FLAG_RANGE);
+    const K m = (K(1) << rb) - 1;
+    return (uint64_t)(key >> (3 * rb)) < (uint64_t)batch && (int)(key & m) < res &&
+           (int)((key >> rb) & m) < res && (int)((key >> (2 * rb)) & m) < res;
 }
 
 // first index in a[0, n) with a[i] >= t
@@ -85,18 +84,358 @@ __device__ __forceinline__ K add_sat(K a, int64_t delta)
     return a > (K)~K(0) - d ? (K)~K(0) : a + d;
 }
 
+// ---------------------------------------------------------------------------
+// tile metadata
+// ---------------------------------------------------------------------------
+
+// Fold one voxel's 27 sorted positions into the tile's per-row [lo, hi] in LDS.
+// Every lane of the block must call it, lanes in sorted order.
+//
+// For a fixed (dz, dy) row the window [first present, last present] of a voxel
+// is monotone in sorted order: a later voxel's cells are all >= the earlier
+// voxel's cell at dx = 0, which is present or else not before the earlier
+// voxel's first present cell.  So a wave's window for the row is the first
+// such lane's lo and the last such lane's hi: one ballot per row, no reduction.
+__device__ __forceinline__ void tile_windows_add(const int32_t (&p)[27], bool valid, int32_t *s_lo,
+                                                 int32_t *s_hi)
+{
+    const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+        const int32_t a = p[3 * d], b = p[3 * d + 1], c = p[3 * d + 2];
+        const int32_t lo = a >= 0 ? a : (b >= 0 ? b : c);
+        const int32_t hi = c >= 0 ? c : (b >= 0 ? b : a);
+        const uint64_t mask = __ballot(valid && hi >= 0);
+        if (!mask) continue;
+        const int first = __ffsll((long long)mask) - 1;
+        const int last = 63 - __clzll((long long)mask);
+        if (lane == first) atomicMin(&s_lo[d], lo);
+        if (lane == last) atomicMax(&s_hi[d], hi);
+    }
+}
+
+// Merge the 9 row windows into disjoint ranges and write the tile's metadata.
+// One thread, all in registers: an unrolled compare-exchange sort with
+// compile-time indices and a straight-line merge (no private arrays indexed at
+// run time, no LDS round trips).  meta: [0] ranges, [1] total rows,
+// [2..10] range start, [11..19] range length, [20..28] per-row offset.
+__device__ void tile_meta_write(const int32_t *s_lo, const int32_t *s_hi, int32_t *meta)
+{
+    constexpr int32_t NONE = 0x7fffffff;
+    int32_t lo[9], hi[9], row[9];
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+        hi[d] = s_hi[d];
+        lo[d] = hi[d] >= 0 ? s_lo[d] : NONE;  // absent rows sort last
+        row[d] = d;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8 - i; ++j) {
+            const bool sw = lo[j] > lo[j + 1];
+            const int32_t a = lo[j], b = hi[j], c = row[j];
+            lo[j] = sw ? lo[j + 1] : a;
+            hi[j] = sw ? hi[j + 1] : b;
+            row[j] = sw ? row[j + 1] : c;
+            lo[j + 1] = sw ? a : lo[j + 1];
+            hi[j + 1] = sw ? b : hi[j + 1];
+            row[j + 1] = sw ? c : row[j + 1];
+        }
+#pragma unroll
+    for (int d = 0; d < 9; ++d) meta[20 + d] = 0;
+    int nr = 0, total = 0;
+    int32_t cur_lo = 0, cur_hi = -2, cur_base = 0;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        if (lo[i] == NONE) continue;
+        if (nr == 0 || lo[i] > cur_hi + 1) {  // a new range starts here
+            if (nr > 0) {
+                meta[11 + nr - 1] = cur_hi - cur_lo + 1;
+                total += cur_hi - cur_lo + 1;
+            }
+            meta[2 + nr] = lo[i];
+            cur_lo = lo[i];
+            cur_hi = hi[i];
+            cur_base = total;
+            ++nr;
+        } else if (hi[i] > cur_hi) {
+            cur_hi = hi[i];
+        }
+        meta[20 + row[i]] = cur_base - cur_lo;
+    }
+    if (nr > 0) {
+        meta[11 + nr - 1] = cur_hi - cur_lo + 1;
+        total += cur_hi - cur_lo + 1;
+    }
+    for (int r = nr; r < 9; ++r) meta[2 + r] = meta[11 + r] = 0;
+    meta[0] = nr;
+    meta[1] = total;
+    meta[29] = meta[30] = meta[31] = 0;
+}
+
+// Per-tile record written by the resolve kernels for the merge kernel: the 9 row
+// windows (lo, hi) and the tile's present-entry count.
+constexpr int WREC = 20;
+
+// Table rows of one tile from LDS to global (contiguous run), the tile's record
+// stored.  Called by every thread after its row of s_rows and its share of
+// s_lo / s_hi / *s_taps are written.  No device-scope atomic here: thousands of
+// blocks adding to one address serialise at the memory side.
+__device__ __forceinline__ void tile_finish(const int32_t *s_rows, int count, int32_t *dst,
+                                            const uint32_t *s_taps, const int32_t *s_lo,
+                                            const int32_t *s_hi, int32_t *rec)
+{
+    __syncthreads();
+    if (threadIdx.x < 9) {
+        rec[threadIdx.x] = s_lo[threadIdx.x];
+        rec[9 + threadIdx.x] = s_hi[threadIdx.x];
+    } else if (threadIdx.x == 9) {
+        rec[18] = (int32_t)*s_taps;
+    }
+    for (int e = threadIdx.x; e < count * 27; e += 256) dst[e] = s_rows[e];
+}
+
+// One thread per tile: merge its row windows into the tile metadata; the tiles'
+// present counts are summed per block and added to st->taps once per block.
+__global__ __launch_bounds__(256) void k_tile_merge(const int32_t *__restrict__ rec, int64_t ntiles,
+                                                    int32_t *__restrict__ meta, DevStatus *st)
+{
+    __shared__ unsigned long long s_sum[4];
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    unsigned long long taps = 0;
+    if (t < ntiles) {
+        tile_meta_write(rec + t * WREC, rec + t * WREC + 9, meta + t * 32);
+        taps = (uint32_t)rec[t * WREC + 18];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) taps += __shfl_xor(taps, off, 64);
+    if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = taps;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned long long sum = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+        if (sum) atomicAdd(&st->taps, sum);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dense key space: occupancy bitmap + rank
+// ---------------------------------------------------------------------------
+
+constexpr int MARK_ROWS = 1;  // rows per thread in k_mark
+
 template <typename K>
-__global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk,
-                                                     const int32_t *__restrict__ perm, int64_t n,
-                                                     int res, int rb, int32_t *__restrict__ nbr,
-                                                     DevStatus *st)
+__global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, int64_t n, int res,
+                                              int batch, int rb, K *__restrict__ keys,
+                                              unsigned long long *__restrict__ bm, DevStatus *st)
+{
+    const unsigned lane = threadIdx.x & 63;
+    const int64_t base = (int64_t)blockIdx.x * (256 * MARK_ROWS) + threadIdx.x;
+    uint64_t word[MARK_ROWS];
+    unsigned long long bit[MARK_ROWS];
+    bool live[MARK_ROWS];
+    bool bad_any = false;
+#pragma unroll
+    for (int q = 0; q < MARK_ROWS; ++q) {
+        const int64_t i = base + q * 256;  // consecutive threads read consecutive rows
+        live[q] = false;
+        K key = (K)~K(0);  // marks an invalid row for the rank pass
+        if (i < n) {
+            const int4 c = coords[i];
+            const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
+                             (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
+            bad_any |= bad;
+            if (!bad) {
+                key = pack_key<K>(c.x, c.y, c.z, c.w, rb);
+                live[q] = true;
+            }
+            keys[i] = key;
+        }
+        word[q] = (uint64_t)(key >> 6);
+        bit[q] = 1ull << (uint32_t)(key & 63);
+    }
+    if (bad_any) atomicOr(&st->flags, FLAG_RANGE);
+    // The wave's 256 rows are grouped by bitmap word (one ballot round per distinct
+    // word, led by the lowest lane that still holds an unwritten row) and each
+    // word gets one no-return atomic: ordered inputs touch only a few words.
+    for (;;) {
+        int have = -1;
+#pragma unroll
+        for (int q = MARK_ROWS - 1; q >= 0; --q)
+            if (live[q]) have = q;
+        const uint64_t pending = __ballot(have >= 0);
+        if (!pending) break;
+        const int leader = __ffsll((long long)pending) - 1;
+        uint64_t mine_w = 0;
+#pragma unroll
+        for (int q = 0; q < MARK_ROWS; ++q)
+            if (q == have) mine_w = word[q];
+        const uint64_t lw = __shfl(mine_w, leader, 64);
+        unsigned long long acc = 0ull;
+#pragma unroll
+        for (int q = 0; q < MARK_ROWS; ++q)
+            if (live[q] && word[q] == lw) {
+                acc |= bit[q];
+                live[q] = false;
+            }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc |= __shfl_xor(acc, off, 64);
+        if ((int)lane == leader) atomicOr(&bm[lw], acc);
+    }
+}
+
+template <typename K>
+__global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys, int64_t n,
+                                              const unsigned long long *__restrict__ bm,
+                                              const uint32_t *__restrict__ prefix,
+                                              K *__restrict__ sk, int32_t *__restrict__ perm)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const K key = keys[i];
+    if (key == (K)~K(0)) return;  // out-of-range row (the build reports it)
+    const unsigned long long word = bm[key >> 6];
+    const int64_t r = (int64_t)prefix[key >> 6] + __popcll(word & ((1ull << (uint32_t)(key & 63)) - 1ull));
+    if (r < n) {
+        sk[r] = key;
+        perm[r] = (int32_t)i;
+    }
+}
+
+// Occupancy bits of cells c, c+1, c+2 (bit 0 = c) from the 64-bit bitmap words.
+__device__ __forceinline__ uint32_t three_bits(const unsigned long long *bm, uint64_t c)
+{
+    const uint64_t w = c >> 6;
+    const uint32_t b = (uint32_t)(c & 63);
+    unsigned long long v = bm[w] >> b;
+    if (b > 61) v |= bm[w + 1] << (64 - b);  // cells c+1 / c+2 spill into the next word
+    return (uint32_t)(v & 7ull);
+}
+
+// Number of keys below cell c (its sorted position if present).
+__device__ __forceinline__ int64_t rank_below(const unsigned long long *bm, const uint32_t *prefix, uint64_t c)
+{
+    const uint64_t w = c >> 6;
+    const uint32_t b = (uint32_t)(c & 63);
+    return (int64_t)prefix[w] + __popcll(bm[w] & ((1ull << b) - 1ull));
+}
+
+template <typename K>
+__global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, int64_t n, int res, int rb,
+                                                    int batch, const unsigned long long *__restrict__ bm,
+                                                    const uint32_t *__restrict__ prefix,
+                                                    int32_t *__restrict__ nbr_sp,
+                                                    int32_t *__restrict__ windows)
+{
+    __shared__ int32_t s_rows[256 * 27];
+    __shared__ int32_t s_lo[9], s_hi[9];
+    __shared__ uint32_t s_taps;
+    const int tid = threadIdx.x;
+    const int64_t s0 = (int64_t)blockIdx.x * 256;
+    const int count = (int)((n - s0) < 256 ? (n - s0) : 256);
+    if (tid < 9) {
+        s_lo[tid] = 0x7fffffff;
+        s_hi[tid] = -1;
+    }
+    if (tid == 0) s_taps = 0;
+    __syncthreads();
+    int32_t p[27];
+#pragma unroll
+    for (int k = 0; k < 27; ++k) p[k] = -1;
+    uint32_t present = 0;
+    K key = K(0);
+    if (tid < count) key = sk[s0 + tid];
+    // positions past the last distinct key are never written when the set holds
+    // a duplicate or an invalid row (the build then reports an error): skip them
+    const bool valid = tid < count && key_valid(key, rb, res, batch);
+    if (valid) {
+        const int64_t s = s0 + tid;
+        const K m = (K(1) << rb) - 1;
+        const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
+        const K bpart = (key >> (3 * rb)) << (3 * rb);
+        const int xs = x > 0 ? x - 1 : 0;                      // first cell of each row window
+        const uint32_t valid3 = (x > 0 ? 1u : 0u) | 2u | (x + 1 < res ? 4u : 0u);  // cells x-1, x, x+1 on the grid
+        const uint32_t shift = x > 0 ? 0u : 1u;                // window bit j <-> cell x-1+j
+        // Each row (dz, dy): the occupancy of cells x-1 .. x+1 (3 bits, from one or
+        // two words) and the rank of the row's first cell; the positions of the
+        // present cells follow by adding bits.  All 27 loads are issued without
+        // branching (rows off the grid read word 0 and are masked), so the whole
+        // neighbourhood costs one memory round trip.
+        uint64_t wd[9];
+        uint32_t bsh[9];
+        bool rok[9];
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const int nz = z + d / 3 - 1, ny = y + d % 3 - 1;
+            rok[d] = nz >= 0 && nz < res && ny >= 0 && ny < res;
+            const uint64_t c0 = rok[d] ? (uint64_t)(bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)xs) : 0;
+            wd[d] = c0 >> 6;
+            bsh[d] = (uint32_t)(c0 & 63);
+        }
+        unsigned long long lo_w[9], hi_w[9];
+        uint32_t pre[9];
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            lo_w[d] = bm[wd[d]];
+            hi_w[d] = bm[wd[d] + 1];  // the bitmap has one word of padding
+            pre[d] = prefix[wd[d]];
+        }
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const uint32_t b = bsh[d];
+            unsigned long long v = lo_w[d] >> b;
+            if (b > 61) v |= hi_w[d] << (64 - b);
+            const uint32_t bits = rok[d] ? (((uint32_t)(v & 7ull) << shift) & valid3) : 0u;
+            // keys below the row window's first cell (the centre row: the voxel is at s)
+            int64_t q = (d == 4) ? s - (int64_t)(bits & 1u)
+                                 : (int64_t)pre[d] + __popcll(lo_w[d] & ((1ull << b) - 1ull));
+            if (bits & 1u) { p[3 * d] = (int32_t)q; ++q; }
+            if (bits & 2u) { p[3 * d + 1] = (int32_t)q; ++q; }
+            if (bits & 4u) p[3 * d + 2] = (int32_t)q;
+        }
+    }
+    if (tid < count) {
+        int32_t *row = s_rows + tid * 27;
+#pragma unroll
+        for (int k = 0; k < 27; ++k) {
+            row[k] = p[k] < n ? p[k] : -1;
+            present += p[k] >= 0 && p[k] < n;
+        }
+    }
+    if (present) atomicAdd(&s_taps, present);
+    tile_windows_add(p, valid, s_lo, s_hi);
+    tile_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, s_lo, s_hi, windows + blockIdx.x * WREC);
+}
+
+// ---------------------------------------------------------------------------
+// sparse key space: radix sort + windowed search
+// ---------------------------------------------------------------------------
+
+template <typename K>
+__global__ __launch_bounds__(256) void k_pack(const int4 *__restrict__ coords, int64_t n, int res,
+                                              int batch, int rb, K *__restrict__ keys,
+                                              int32_t *__restrict__ rows, DevStatus *st)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int4 c = coords[i];  // (b, z, y, x)
+    const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
+                     (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
+    keys[i] = bad ? K(0) : pack_key<K>(c.x, c.y, c.z, c.w, rb);
+    rows[i] = (int32_t)i;
+    if (bad) atomicOr(&st->flags, FLAG_RANGE);
+}
+
+template <typename K>
+__global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, int64_t n, int res,
+                                                     int rb, int32_t *__restrict__ nbr_sp,
+                                                     int32_t *__restrict__ windows, DevStatus *st)
 {
     __shared__ K s_win[WIN_MAX];
-    __shared__ int32_t s_wrow[WIN_MAX];
     __shared__ int32_t s_rows[256 * 27];
-    __shared__ int32_t s_dst[256];
-    __shared__ int64_t s_lo[8], s_hi[8];
-    __shared__ uint32_t s_red[4];
+    __shared__ int64_t s_wlo[8], s_whi[8];
+    __shared__ int32_t s_lo[9], s_hi[9];
+    __shared__ uint32_t s_taps;
 
     const int tid = threadIdx.x;
     const int64_t s0 = (int64_t)blockIdx.x * 256;
@@ -107,12 +446,15 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk,
     const K key = valid ? sk[s] : K(0);
     const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
     const K bpart = (key >> (3 * rb)) << (3 * rb);
-    int32_t *row = s_rows + tid * 27;
-
+    if (tid < 9) {
+        s_lo[tid] = 0x7fffffff;
+        s_hi[tid] = -1;
+    }
+    if (tid == 0) s_taps = 0;
     // window bounds of the 8 off-centre (dz, dy) rows: 16 binary searches, one per thread
     if (tid < 16) {
         int d = tid >> 1;
-        d += (d >= 4);  // skip the centre row (dz, dy) = (0, 0), index 4 of 9
+        d += (d >= 4);  // skip the centre row (dz, dy) = (0, 0)
         const int dz = d / 3 - 1, dy = d % 3 - 1;
         const int64_t off = (int64_t)dz * ((int64_t)1 << (2 * rb)) + (int64_t)dy * ((int64_t)1 << rb);
         const K first = sk[s0], last = sk[s0 + count - 1];
@@ -122,85 +464,167 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk,
             const K t = add_sat(last, off + 1);  // first index with a key > t
             r = (t == (K)~K(0)) ? n : lower_bound_key(sk, n, (K)(t + 1));
         }
-        if ((tid & 1) == 0) s_lo[tid >> 1] = r;
-        else s_hi[tid >> 1] = r;
+        if ((tid & 1) == 0) s_wlo[tid >> 1] = r;
+        else s_whi[tid >> 1] = r;
     }
-
-    // centre row: adjacent sorted entries
-    uint32_t present = 0;
+    int32_t p[27];
+#pragma unroll
+    for (int k = 0; k < 27; ++k) p[k] = -1;
     bool dup = false;
-    if (valid) {
+    if (valid) {  // centre row: adjacent sorted entries
         dup = (s + 1 < n) && sk[s + 1] == key;
-        row[12] = (x > 0 && s > 0 && sk[s - 1] == key - 1) ? perm[s - 1] : -1;
-        row[13] = perm[s];
-        row[14] = (x + 1 < res && s + 1 < n && sk[s + 1] == key + 1) ? perm[s + 1] : -1;
-        s_dst[tid] = perm[s];
+        if (x > 0 && s > 0 && sk[s - 1] == key - 1) p[12] = (int32_t)(s - 1);
+        p[13] = (int32_t)s;
+        if (x + 1 < res && s + 1 < n && sk[s + 1] == key + 1) p[14] = (int32_t)(s + 1);
     }
     __syncthreads();
-
     for (int w = 0; w < 8; ++w) {
         const int d = w + (w >= 4);
         const int dz = d / 3 - 1, dy = d % 3 - 1;
-        const int kb = 9 * (dz + 1) + 3 * (dy + 1);
-        const int64_t lo = s_lo[w], hi = s_hi[w];
+        const int64_t lo = s_wlo[w], hi = s_whi[w];
         const int64_t wn = hi - lo;
         const bool in_lds = wn <= WIN_MAX;
-        if (in_lds) {
-            for (int i = tid; i < wn; i += 256) {
-                s_win[i] = sk[lo + i];
-                s_wrow[i] = perm[lo + i];
-            }
-        }
+        if (in_lds)
+            for (int i = tid; i < wn; i += 256) s_win[i] = sk[lo + i];
         __syncthreads();
         if (valid) {
             const int nz = z + dz, ny = y + dy;
-            if (nz < 0 || nz >= res || ny < 0 || ny >= res) {
-                row[kb] = row[kb + 1] = row[kb + 2] = -1;
-            } else {
+            if (nz >= 0 && nz < res && ny >= 0 && ny < res) {
                 const K rowkey = bpart | ((K)nz << (2 * rb)) | ((K)ny << rb);
                 const K t0 = rowkey | (K)(x > 0 ? x - 1 : 0);
-                int64_t p = in_lds ? lower_bound_key(s_win, wn, t0) : lower_bound_key(sk + lo, wn, t0);
+                int64_t q = in_lds ? lower_bound_key(s_win, wn, t0) : lower_bound_key(sk + lo, wn, t0);
                 for (int dx = -1; dx <= 1; ++dx) {
                     const int nx = x + dx;
-                    int32_t r = -1;
-                    if (nx >= 0 && nx < res) {
-                        const K t = rowkey | (K)nx;
-                        if (in_lds) {
-                            while (p < wn && s_win[p] < t) ++p;
-                            if (p < wn && s_win[p] == t) r = s_wrow[p];
-                        } else {
-                            while (p < wn && sk[lo + p] < t) ++p;
-                            if (p < wn && sk[lo + p] == t) r = perm[lo + p];
-                        }
+                    if (nx < 0 || nx >= res) continue;
+                    const K t = rowkey | (K)nx;
+                    if (in_lds) {
+                        while (q < wn && s_win[q] < t) ++q;
+                        if (q < wn && s_win[q] == t) p[3 * d + dx + 1] = (int32_t)(lo + q);
+                    } else {
+                        while (q < wn && sk[lo + q] < t) ++q;
+                        if (q < wn && sk[lo + q] == t) p[3 * d + dx + 1] = (int32_t)(lo + q);
                     }
-                    row[kb + dx + 1] = r;
                 }
             }
         }
         __syncthreads();
     }
+    uint32_t present = 0;
     if (valid) {
+        int32_t *row = s_rows + tid * 27;
 #pragma unroll
-        for (int k = 0; k < 27; ++k) present += row[k] >= 0;
+        for (int k = 0; k < 27; ++k) {
+            row[k] = p[k];
+            present += p[k] >= 0;
+        }
     }
     if (dup) atomicOr(&st->flags, FLAG_DUPLICATE);
-    uint32_t total;
-    block_incl_scan256(present, s_red, &total);  // also a barrier for s_rows / s_dst
-    if (tid == 0 && total) atomicAdd(&st->taps, (unsigned long long)total);
-    for (int e = tid; e < count * 27; e += 256) {
-        const int r = e / 27, k = e - r * 27;
-        const uint32_t dst = (uint32_t)s_dst[r];
-        if (dst < (uint64_t)n) nbr[(int64_t)dst * 27 + k] = s_rows[e];
-    }
+    if (present) atomicAdd(&s_taps, present);
+    tile_windows_add(p, valid, s_lo, s_hi);
+    tile_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, s_lo, s_hi, windows + blockIdx.x * WREC);
 }
 
-// One block: pack, bitonic sort in LDS, resolve by binary search in LDS, write table.
+// ---------------------------------------------------------------------------
+// small sets: one block
+// ---------------------------------------------------------------------------
+
+// Key space of at most 2^16 bits: bitmap and prefix in LDS.
+template <typename K>
+__global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict__ coords, int n,
+                                                         int res, int batch, int rb, int nbits,
+                                                         K *__restrict__ keys_out,
+                                                         int32_t *__restrict__ perm_out,
+                                                         int32_t *__restrict__ nbr_sp, DevStatus *st)
+{
+    constexpr int WORDS = (1 << SMALL_BITS) / 32;
+    __shared__ uint32_t s_bm[WORDS];
+    __shared__ uint32_t s_pre[WORDS];
+    __shared__ uint32_t s_wave[16];
+    __shared__ uint32_t s_flags, s_taps;
+    const int tid = threadIdx.x;
+    const int words = nbits > 5 ? (1 << (nbits - 5)) : 1;
+    for (int w = tid; w < words; w += 1024) s_bm[w] = 0;
+    if (tid == 0) { s_flags = 0; s_taps = 0; }
+    __syncthreads();
+    K key[2];
+    bool ok[2];
+    for (int q = 0; q < 2; ++q) {  // n <= 2048 = 2 per thread
+        const int i = tid + q * 1024;
+        ok[q] = false;
+        key[q] = K(0);
+        if (i < n) {
+            const int4 c = coords[i];
+            const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
+                             (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
+            if (bad) atomicOr(&s_flags, FLAG_RANGE);
+            else {
+                key[q] = pack_key<K>(c.x, c.y, c.z, c.w, rb);
+                ok[q] = true;
+                const uint32_t bit = 1u << (uint32_t)(key[q] & 31);
+                if (atomicOr(&s_bm[key[q] >> 5], bit) & bit) atomicOr(&s_flags, FLAG_DUPLICATE);
+            }
+        }
+    }
+    __syncthreads();
+    {   // exclusive prefix of word popcounts (words <= 2048: two per thread)
+        const int w0 = 2 * tid;
+        const uint32_t a = w0 < words ? (uint32_t)__popc(s_bm[w0]) : 0u;
+        const uint32_t b = w0 + 1 < words ? (uint32_t)__popc(s_bm[w0 + 1]) : 0u;
+        const uint32_t v = a + b;
+        const unsigned lane = tid & 63, wave = tid >> 6;
+        uint32_t x = v;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off, 64);
+            if (lane >= (unsigned)off) x += y;
+        }
+        if (lane == 63) s_wave[wave] = x;
+        __syncthreads();
+        uint32_t before = 0;
+        for (int w = 0; w < (int)wave; ++w) before += s_wave[w];
+        const uint32_t ex = x - v + before;
+        if (w0 < words) s_pre[w0] = ex;
+        if (w0 + 1 < words) s_pre[w0 + 1] = ex + a;
+    }
+    __syncthreads();
+    if (s_flags) {  // invalid set: report only
+        if (tid == 0) atomicOr(&st->flags, s_flags);
+        return;
+    }
+    const K m = (K(1) << rb) - 1;
+    uint32_t present = 0;
+    for (int q = 0; q < 2; ++q) {
+        if (!ok[q]) continue;
+        const int i = tid + q * 1024;
+        const int s = (int)(s_pre[key[q] >> 5] + __popc(s_bm[key[q] >> 5] & ((1u << (uint32_t)(key[q] & 31)) - 1u)));
+        keys_out[s] = key[q];
+        perm_out[s] = i;
+        const int x = (int)(key[q] & m), y = (int)((key[q] >> rb) & m), z = (int)((key[q] >> (2 * rb)) & m);
+        const K bpart = (key[q] >> (3 * rb)) << (3 * rb);
+        int32_t *out = nbr_sp + (int64_t)s * 27;
+        for (int k = 0; k < 27; ++k) {
+            const int nz = z + k / 9 - 1, ny = y + (k / 3) % 3 - 1, nx = x + k % 3 - 1;
+            int32_t r = -1;
+            if (nz >= 0 && nz < res && ny >= 0 && ny < res && nx >= 0 && nx < res) {
+                const K t = bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)nx;
+                const uint32_t word = s_bm[t >> 5], b = (uint32_t)(t & 31);
+                if ((word >> b) & 1u) r = (int32_t)(s_pre[t >> 5] + __popc(word & ((1u << b) - 1u)));
+            }
+            present += r >= 0;
+            out[k] = r;
+        }
+    }
+    if (present) atomicAdd(&s_taps, present);
+    __syncthreads();
+    if (tid == 0 && s_taps) atomicAdd(&st->taps, (unsigned long long)s_taps);
+}
+
+// Larger key space: bitonic sort of (key, row) in LDS, binary search in LDS.
 template <typename K>
 __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ coords, int n,
                                                       int res, int batch, int rb,
                                                       K *__restrict__ keys_out,
                                                       int32_t *__restrict__ perm_out,
-                                                      int32_t *__restrict__ nbr, DevStatus *st)
+                                                      int32_t *__restrict__ nbr_sp, DevStatus *st)
 {
     __shared__ K s_key[SMALL_N];
     __shared__ int32_t s_row[SMALL_N];
@@ -257,14 +681,14 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
         if (s + 1 < n && s_key[s + 1] == key) atomicOr(&st->flags, FLAG_DUPLICATE);
         const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
         const K bpart = (key >> (3 * rb)) << (3 * rb);
-        int32_t *out = nbr + (int64_t)s_row[s] * 27;
+        int32_t *out = nbr_sp + (int64_t)s * 27;
         for (int k = 0; k < 27; ++k) {
             const int nz = z + k / 9 - 1, ny = y + (k / 3) % 3 - 1, nx = x + k % 3 - 1;
             int32_t r = -1;
             if (nz >= 0 && nz < res && ny >= 0 && ny < res && nx >= 0 && nx < res) {
                 const K t = bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)nx;
-                const int64_t p = lower_bound_key(s_key, n, t);
-                if (p < n && s_key[p] == t) r = s_row[p];
+                const int64_t q = lower_bound_key(s_key, n, t);
+                if (q < n && s_key[q] == t) r = (int32_t)q;
             }
             present += r >= 0;
             out[k] = r;
@@ -275,236 +699,62 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
     if (tid == 0 && s_red[0]) atomicAdd(&st->taps, (unsigned long long)s_red[0]);
 }
 
-// ---------------------------------------------------------------------------
-// dense key space: occupancy bitmap + rank
-// ---------------------------------------------------------------------------
-
-template <typename K>
-__global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, int64_t n, int res,
-                                              int batch, int rb, K *__restrict__ keys,
-                                              unsigned long long *__restrict__ bm, DevStatus *st)
+// Row windows of every tile from a finished table (used after the single-block builds).
+__global__ __launch_bounds__(256) void k_tile_windows(const int32_t *__restrict__ nbr_sp, int64_t n,
+                                                      int32_t *__restrict__ windows)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const unsigned lane = threadIdx.x & 63;
-    bool valid = i < n, bad = false;
-    K key = K(0);
-    if (valid) {
-        const int4 c = coords[i];
-        bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
-              (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
-        if (!bad) key = pack_key<K>(c.x, c.y, c.z, c.w, rb);
-        keys[i] = key;
-    }
-    if (bad) atomicOr(&st->flags, FLAG_RANGE);
-    const bool live = valid && !bad;
-    // Runs of consecutive lanes that set bits of the same word (ordered inputs) are
-    // merged by a segmented inclusive OR-scan (head flag = first lane of a run), so
-    // only the last lane of each run touches memory.  Two lanes of one run with the
-    // same bit are a duplicate; each merge joins disjoint lane ranges, so checking
-    // the overlap at every merge sees every such pair.
-    const uint64_t word = live ? (uint64_t)(key >> 6) : ~uint64_t(0);
-    const unsigned long long bit = live ? (1ull << (uint32_t)(key & 63)) : 0ull;
-    const uint64_t w_prev = __shfl_up(word, 1, 64);
-    bool head = lane == 0 || w_prev != word;
-    unsigned long long acc = bit;
-    bool dup_in_run = false;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long a_up = __shfl_up(acc, off, 64);
-        const bool h_up = __shfl_up((int)head, off, 64) != 0;
-        if (lane >= (unsigned)off && !head) {
-            dup_in_run |= (a_up & acc) != 0ull;
-            acc |= a_up;
-            head = h_up;
-        }
-    }
-    const uint64_t w_next = __shfl_down(word, 1, 64);
-    const bool last_of_run = lane == 63 || w_next != word;
-    if (live && last_of_run) {
-        const unsigned long long old = atomicOr(&bm[word], acc);
-        if (old & acc) dup_in_run = true;
-    }
-    if (live && dup_in_run) atomicOr(&st->flags, FLAG_DUPLICATE);
-}
-
-template <typename K>
-__device__ __forceinline__ int64_t rank_of(K key, const unsigned long long *bm, const uint32_t *prefix)
-{
-    const unsigned long long word = bm[key >> 6];
-    return (int64_t)prefix[key >> 6] + __popcll(word & ((1ull << (uint32_t)(key & 63)) - 1ull));
-}
-
-template <typename K>
-__global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys, int64_t n,
-                                              const unsigned long long *__restrict__ bm,
-                                              const uint32_t *__restrict__ prefix,
-                                              K *__restrict__ sk, int32_t *__restrict__ perm)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const K key = keys[i];
-    const int64_t r = rank_of(key, bm, prefix);
-    if (r < n) {  // always, unless the set is invalid (then the build reports an error)
-        sk[r] = key;
-        perm[r] = (int32_t)i;
-    }
-}
-
-template <typename K>
-__global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ keys, int64_t n, int res,
-                                                    int rb, const unsigned long long *__restrict__ bm,
-                                                    const uint32_t *__restrict__ prefix,
-                                                    const int32_t *__restrict__ perm,
-                                                    int32_t *__restrict__ nbr, DevStatus *st)
-{
-    __shared__ int32_t s_rows[256 * 27];
-    __shared__ uint32_t s_red[4];
+    __shared__ int32_t s_lo[9], s_hi[9];
     const int tid = threadIdx.x;
-    const int64_t i0 = (int64_t)blockIdx.x * 256;
-    const int count = (int)((n - i0) < 256 ? (n - i0) : 256);
-    uint32_t present = 0;
-    if (tid < count) {
-        const K key = keys[i0 + tid];
-        const K m = (K(1) << rb) - 1;
-        const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
-        const K bpart = (key >> (3 * rb)) << (3 * rb);
-        int32_t *row = s_rows + tid * 27;
-        // ranks first (bitmap + prefix), then the rows at those ranks: 27 independent chains
-        int64_t p[27];
-#pragma unroll
-        for (int d = 0; d < 9; ++d) {
-            const int dz = d / 3 - 1, dy = d % 3 - 1;
-            const int nz = z + dz, ny = y + dy;
-            const bool row_ok = nz >= 0 && nz < res && ny >= 0 && ny < res;
-            const K rowkey = bpart | ((K)nz << (2 * rb)) | ((K)ny << rb);
-#pragma unroll
-            for (int dx = -1; dx <= 1; ++dx) {
-                const int nx = x + dx;
-                p[3 * d + dx + 1] = -1;
-                if (row_ok && nx >= 0 && nx < res) {
-                    const K t = rowkey | (K)nx;
-                    const unsigned long long word = bm[t >> 6];
-                    const uint32_t b = (uint32_t)(t & 63);
-                    if ((word >> b) & 1ull)
-                        p[3 * d + dx + 1] = (int64_t)prefix[t >> 6] + __popcll(word & ((1ull << b) - 1ull));
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 27; ++k) {
-            const int32_t r = (p[k] >= 0 && p[k] < n) ? perm[p[k]] : -1;
-            row[k] = r;
-            present += r >= 0;
-        }
+    const int64_t s = (int64_t)blockIdx.x * 256 + tid;
+    if (tid < 9) {
+        s_lo[tid] = 0x7fffffff;
+        s_hi[tid] = -1;
     }
-    uint32_t total;
-    block_incl_scan256(present, s_red, &total);  // also the barrier for s_rows
-    if (tid == 0 && total) atomicAdd(&st->taps, (unsigned long long)total);
-    int32_t *dst = nbr + i0 * 27;  // rows i0 .. i0+count-1 are contiguous
-    for (int e = tid; e < count * 27; e += 256) dst[e] = s_rows[e];
+    __syncthreads();
+    int32_t p[27];
+    const bool valid = s < n;
+#pragma unroll
+    for (int k = 0; k < 27; ++k) p[k] = valid ? nbr_sp[s * 27 + k] : -1;
+    tile_windows_add(p, valid, s_lo, s_hi);
+    __syncthreads();
+    if (tid < 9) {
+        windows[blockIdx.x * WREC + tid] = s_lo[tid];
+        windows[blockIdx.x * WREC + 9 + tid] = s_hi[tid];
+    } else if (tid == 9) {
+        windows[blockIdx.x * WREC + 18] = 0;  // the single-block builds count their taps themselves
+    }
 }
 
-// One block, key space of at most 2^16 bits: the bitmap, its prefix and the
-// sorted rows all live in LDS.
-constexpr int SMALL_BITS = 16;
+// ---------------------------------------------------------------------------
+// input-order table, on request
+// ---------------------------------------------------------------------------
 
-template <typename K>
-__global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict__ coords, int n,
-                                                         int res, int batch, int rb, int nbits,
-                                                         K *__restrict__ keys_out,
-                                                         int32_t *__restrict__ perm_out,
-                                                         int32_t *__restrict__ nbr, DevStatus *st)
+__global__ __launch_bounds__(256) void k_input_order_table(const int32_t *__restrict__ nbr_sp,
+                                                           const int32_t *__restrict__ perm, int64_t n,
+                                                           int32_t *__restrict__ out)
 {
-    constexpr int WORDS = (1 << SMALL_BITS) / 32;
-    __shared__ uint32_t s_bm[WORDS];
-    __shared__ uint32_t s_pre[WORDS];
-    __shared__ int32_t s_perm[SMALL_N];
-    __shared__ uint32_t s_wave[16];
-    __shared__ uint32_t s_flags, s_taps;
-    const int tid = threadIdx.x;
-    const int words = nbits > 5 ? (1 << (nbits - 5)) : 1;
-    for (int w = tid; w < words; w += 1024) s_bm[w] = 0;
-    if (tid == 0) { s_flags = 0; s_taps = 0; }
-    __syncthreads();
-    K key[2];
-    bool ok[2];
-    for (int q = 0; q < 2; ++q) {  // n <= 2048 = 2 per thread
-        const int i = tid + q * 1024;
-        ok[q] = false;
-        key[q] = K(0);
-        if (i < n) {
-            const int4 c = coords[i];
-            const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
-                             (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
-            if (bad) atomicOr(&s_flags, FLAG_RANGE);
-            else {
-                key[q] = pack_key<K>(c.x, c.y, c.z, c.w, rb);
-                ok[q] = true;
-                const uint32_t bit = 1u << (uint32_t)(key[q] & 31);
-                if (atomicOr(&s_bm[key[q] >> 5], bit) & bit) atomicOr(&s_flags, FLAG_DUPLICATE);
-            }
-        }
-    }
-    __syncthreads();
-    // exclusive prefix of word popcounts (words <= 2048: two per thread)
-    {
-        const int w0 = 2 * tid;
-        const uint32_t a = w0 < words ? (uint32_t)__popc(s_bm[w0]) : 0u;
-        const uint32_t b = w0 + 1 < words ? (uint32_t)__popc(s_bm[w0 + 1]) : 0u;
-        const uint32_t v = a + b;
-        const unsigned lane = tid & 63, wave = tid >> 6;
-        uint32_t x = v;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(x, off, 64);
-            if (lane >= (unsigned)off) x += y;
-        }
-        if (lane == 63) s_wave[wave] = x;
-        __syncthreads();
-        uint32_t before = 0;
-        for (int w = 0; w < (int)wave; ++w) before += s_wave[w];
-        const uint32_t ex = x - v + before;
-        if (w0 < words) s_pre[w0] = ex;
-        if (w0 + 1 < words) s_pre[w0 + 1] = ex + a;
-    }
-    __syncthreads();
-    if (s_flags) {  // invalid set: report only
-        if (tid == 0) atomicOr(&st->flags, s_flags);
-        return;
-    }
-    for (int q = 0; q < 2; ++q) {
-        const int i = tid + q * 1024;
-        if (ok[q]) {
-            const int r = (int)(s_pre[key[q] >> 5] + __popc(s_bm[key[q] >> 5] & ((1u << (uint32_t)(key[q] & 31)) - 1u)));
-            s_perm[r] = i;
-            keys_out[r] = key[q];
-            perm_out[r] = i;
-        }
-    }
-    __syncthreads();
-    const K m = (K(1) << rb) - 1;
-    uint32_t present = 0;
-    for (int q = 0; q < 2; ++q) {
-        const int i = tid + q * 1024;
-        if (!ok[q]) continue;
-        const int x = (int)(key[q] & m), y = (int)((key[q] >> rb) & m), z = (int)((key[q] >> (2 * rb)) & m);
-        const K bpart = (key[q] >> (3 * rb)) << (3 * rb);
-        int32_t *out = nbr + (int64_t)i * 27;
-        for (int k = 0; k < 27; ++k) {
-            const int nz = z + k / 9 - 1, ny = y + (k / 3) % 3 - 1, nx = x + k % 3 - 1;
-            int32_t r = -1;
-            if (nz >= 0 && nz < res && ny >= 0 && ny < res && nx >= 0 && nx < res) {
-                const K t = bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)nx;
-                const uint32_t word = s_bm[t >> 5], b = (uint32_t)(t & 31);
-                if ((word >> b) & 1u) r = s_perm[s_pre[t >> 5] + __popc(word & ((1u << b) - 1u))];
-            }
-            present += r >= 0;
-            out[k] = r;
-        }
-    }
-    if (present) atomicAdd(&s_taps, present);
-    __syncthreads();
-    if (tid == 0 && s_taps) atomicAdd(&st->taps, (unsigned long long)s_taps);
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over n x 27, sorted order
+    if (e >= n * 27) return;
+    const int64_t s = e / 27;
+    const int k = (int)(e - s * 27);
+    const int32_t p = nbr_sp[e];
+    const uint32_t row = (uint32_t)perm[s];
+    if (row < (uint64_t)n) out[(int64_t)row * 27 + k] = (p >= 0 && p < n) ? perm[p] : -1;
 }
+
+int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s)
+{
+    const int64_t total = rb->n * 27;
+    if (total == 0) return SUBMCONV_OK;
+    hipLaunchKernelGGL(k_input_order_table, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       rb->nbr_sp, rb->perm, rb->n, out);
+    SC_LAUNCHED("input_order_table");
+    return SUBMCONV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// driver
+// ---------------------------------------------------------------------------
 
 // Bitmap bytes are affordable when they stay within a small multiple of the
 // per-voxel data (a 512^3 grid of 3M voxels: 16 MB).
@@ -519,14 +769,15 @@ template <typename K>
 static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStream_t stream)
 {
     const int64_t n = rb->n;
-    const int path = (n <= SMALL_N && rb->nbits <= SMALL_BITS) ? 0 : (n <= SMALL_N ? 1 : (use_bitmap(n, rb->nbits) ? 2 : 3));
+    const int path = n <= SMALL_N ? (rb->nbits <= SMALL_BITS ? 0 : 1) : (use_bitmap(n, rb->nbits) ? 2 : 3);
     auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
     const int64_t words = rb->nbits > 6 ? (int64_t(1) << (rb->nbits - 6)) : 1;  // 64-bit bitmap words
-    // scratch: path 2 = tmp keys, bitmap, prefix, scan scratch; path 3 = alt keys/rows, sort scratch
     size_t off = 0, o_keys = 0, o_vals = 0, o_bm = 0, o_pre = 0, o_aux = 0;
+    const size_t o_win = off;  // per tile: row windows and tap count, merged after the resolve
+    off += up((size_t)rb->ntiles * WREC * 4);
     if (path == 2) {
         o_keys = off; off += up((size_t)n * sizeof(K));
-        o_bm = off; off += up((size_t)words * 8);
+        o_bm = off; off += up((size_t)(words + 1) * 8);  // +1: a 3-cell window may touch the next word
         o_pre = off; off += up((size_t)words * 4);
         o_aux = off; off += up(scan_scratch_bytes(words));
     } else if (path == 3) {
@@ -539,28 +790,33 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     char *scratch = nullptr;
     SC_CHECK(dev_alloc((void **)&scratch, off, stream));
     DevStatus *st = (DevStatus *)(scratch + o_stat);
+    int32_t *windows = (int32_t *)(scratch + o_win);
     int status = SUBMCONV_OK;
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
         if (hipMemsetAsync(st, 0, sizeof(DevStatus), stream) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
-        if (path == 0) {
-            hipLaunchKernelGGL(k_build_small_bm<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
-                               (int)n, rb->res, rb->batch, rb->rb, rb->nbits, (K *)rb->keys, rb->perm, rb->nbr, st);
-        } else if (path == 1) {
-            hipLaunchKernelGGL(k_build_small<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
-                               (int)n, rb->res, rb->batch, rb->rb, (K *)rb->keys, rb->perm, rb->nbr, st);
+        if (path == 0 || path == 1) {
+            if (path == 0)
+                hipLaunchKernelGGL(k_build_small_bm<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
+                                   (int)n, rb->res, rb->batch, rb->rb, rb->nbits, (K *)rb->keys, rb->perm, rb->nbr_sp, st);
+            else
+                hipLaunchKernelGGL(k_build_small<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
+                                   (int)n, rb->res, rb->batch, rb->rb, (K *)rb->keys, rb->perm, rb->nbr_sp, st);
+            hipLaunchKernelGGL(k_tile_windows, dim3(grid), dim3(256), 0, stream, rb->nbr_sp, n, windows);
         } else if (path == 2) {
             K *tmp = (K *)(scratch + o_keys);
             unsigned long long *bm = (unsigned long long *)(scratch + o_bm);
             uint32_t *pre = (uint32_t *)(scratch + o_pre);
-            if (hipMemsetAsync(bm, 0, (size_t)words * 8, stream) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "bitmap clear failed"); break; }
-            hipLaunchKernelGGL(k_mark<K>, dim3(grid), dim3(256), 0, stream, (const int4 *)coords, n, rb->res,
-                               rb->batch, rb->rb, tmp, bm, st);
-            if ((status = exclusive_scan_u32((const uint32_t *)bm, pre, words, nullptr, scratch + o_aux, stream, SCAN_POPC64)) != SUBMCONV_OK) break;
+            if (hipMemsetAsync(bm, 0, (size_t)(words + 1) * 8, stream) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "bitmap clear failed"); break; }
+            hipLaunchKernelGGL(k_mark<K>, dim3((unsigned)((n + 256 * MARK_ROWS - 1) / (256 * MARK_ROWS))), dim3(256),
+                               0, stream, (const int4 *)coords, n, rb->res, rb->batch, rb->rb, tmp, bm, st);
+            // the total number of set bits lands in st->count: below n means a duplicate
+            if ((status = exclusive_scan_u32((const uint32_t *)bm, pre, words, (uint32_t *)&st->count,
+                                             scratch + o_aux, stream, SCAN_POPC64)) != SUBMCONV_OK) break;
             hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n, bm, pre,
                                (K *)rb->keys, rb->perm);
-            hipLaunchKernelGGL(k_resolve_bm<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n, rb->res,
-                               rb->rb, bm, pre, rb->perm, rb->nbr, st);
+            hipLaunchKernelGGL(k_resolve_bm<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
+                               rb->res, rb->rb, rb->batch, bm, pre, rb->nbr_sp, windows);
         } else {
             K *keys_b = (K *)(scratch + o_keys);
             int32_t *vals_b = (int32_t *)(scratch + o_vals);
@@ -570,12 +826,15 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
                                in_b ? vals_b : rb->perm, st);
             if ((status = radix_sort_pairs<K>((K *)rb->keys, rb->perm, keys_b, vals_b, n, rb->nbits,
                                               scratch + o_aux, stream, in_b)) != SUBMCONV_OK) break;
-            hipLaunchKernelGGL(k_resolve_win<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys,
-                               rb->perm, n, rb->res, rb->rb, rb->nbr, st);
+            hipLaunchKernelGGL(k_resolve_win<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
+                               rb->res, rb->rb, rb->nbr_sp, windows, st);
         }
+        hipLaunchKernelGGL(k_tile_merge, dim3((unsigned)((rb->ntiles + 255) / 256)), dim3(256), 0, stream,
+                           windows, rb->ntiles, rb->meta, st);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "kernel launch in build_map failed"); break; }
         DevStatus h;
         if ((status = read_status(st, &h, stream)) != SUBMCONV_OK) break;
+        if (path == 2 && !(h.flags & FLAG_RANGE) && (int64_t)(uint32_t)h.count != n) h.flags |= FLAG_DUPLICATE;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
         rb->taps = (int64_t)h.taps;

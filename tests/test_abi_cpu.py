@@ -87,7 +87,7 @@ def test_helper_argument_errors(lib):
     assert lib.submconv_space_to_depth(fake, fake, 4, 0, 0, 16, 1, fake, fake, None, ctypes.byref(m), None) == E_INVALID_ARG
     assert lib.submconv_depth_to_space(fake, fake, None, 4, 8, 0, fake, fake, None, None) == E_INVALID_ARG
     assert lib.submconv_depth_to_space(fake, fake, None, -2, 8, 0, fake, fake, ctypes.byref(m), None) == E_INVALID_ARG
-    assert lib.submconv_rulebook_neighbors(None, None, None) == E_INVALID_ARG
+    assert lib.submconv_rulebook_neighbors(None, None, None, None) == E_INVALID_ARG
     assert lib.submconv_rulebook_info(None, None, None, None, None) == E_INVALID_ARG
     assert lib.submconv_rulebook_free(None, None) == 0
 

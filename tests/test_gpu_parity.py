@@ -342,3 +342,24 @@ def test_space_to_depth_errors():
     with pytest.raises(sc.SubmconvError) as e:
         sc.submconv_space_to_depth(coords_dev(np.array([[0, 9, 1, 1]], np.int32)), f[:1], 4, 1)
     assert e.value.status == -2
+
+
+def test_rulebook_neighbors_pointer_matches_copy():
+    """submconv_rulebook_neighbors builds the input-order table once and hands out
+    a device pointer; its bytes equal the copy API's and the oracle's."""
+    import ctypes
+    w, c = synth.workload(2)
+    rb = build(c[synth.shuffle_rows(len(c), 5)], w.res, 1)
+    lib = sc.load_library()
+    ptr, n = ctypes.c_void_p(), ctypes.c_int64()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    note("rulebook_neighbors pointer")
+    assert lib.submconv_rulebook_neighbors(rb.handle, stream, ctypes.byref(ptr), ctypes.byref(n)) == 0
+    ptr2 = ctypes.c_void_p()
+    assert lib.submconv_rulebook_neighbors(rb.handle, stream, ctypes.byref(ptr2), ctypes.byref(n)) == 0
+    assert ptr.value == ptr2.value and n.value == rb.n
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    host = np.empty((rb.n, 27), np.int32)
+    assert hip.hipMemcpy(host.ctypes.data_as(ctypes.c_void_p), ptr, ctypes.c_size_t(host.nbytes), 2) == 0
+    np.testing.assert_array_equal(host, rb.neighbors().cpu().numpy())
