@@ -67,6 +67,8 @@ extern "C" {
 #define SUBMCONV_KERNEL_GENERIC 1 /* one thread per output element, any channel counts */
 #define SUBMCONV_KERNEL_LOWC 2    /* narrow channels (<= 32), wave shuffles, no matrix cores */
 #define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128} */
+#define SUBMCONV_KERNEL_WINDOW 4  /* matrix cores fed from a tile's neighbourhood staged in LDS
+                                     (bf16, Cin = Cout = 32) */
 
 typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
 

@@ -13,6 +13,8 @@ int launch_forward(const void *feats, const void *w, const float *bias,
                    const submconv_rulebook *rb, void *out, int cin, int cout, int dtype, int flip,
                    int variant, hipStream_t s);
 int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s);
+int64_t win_plan_ints(int64_t n);
+int win_plan_build(submconv_rulebook *rb, hipStream_t s);
 int choose_forward_kernel(int cin, int cout, int dtype);
 int subdivide(const int32_t *coords, const void *feats, int64_t n, int c, int dtype,
               int32_t *out_coords, void *out_feats, hipStream_t s);
@@ -140,21 +142,25 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     r->device = dev;
     int st = keep_pool(dev);
     if (st != SUBMCONV_OK) { delete r; return st; }
-    r->ntiles = (n + 255) / 256;
+    r->ngroups = (n + 31) / 32;
     r->nbr_in = nullptr;
+
     const size_t kbytes = (((size_t)n * r->key_bytes) + 255) & ~size_t(255);
     const size_t pbytes = (((size_t)n * 4) + 255) & ~size_t(255);
     // +1 KB: kernels copy table rows in 16-byte chunks that may run past the last row
     const size_t nbytes = ((((size_t)n * 27 * 4) + 255) & ~size_t(255)) + 1024;
-    const size_t mbytes = (size_t)r->ntiles * 32 * 4 + 256;
-    st = dev_alloc(&r->block, kbytes + pbytes + nbytes + mbytes, s);
+    const size_t mbytes = (((size_t)r->ngroups * GWIN_INTS * 4) + 255) & ~size_t(255);
+    const size_t lbytes = (size_t)win_plan_ints(n) * 4 + 256;
+    st = dev_alloc(&r->block, kbytes + pbytes + nbytes + mbytes + lbytes, s);
     if (st != SUBMCONV_OK) { delete r; return st; }
     r->keys = r->block;
     r->perm = (int32_t *)((char *)r->block + kbytes);
     r->nbr_sp = (int32_t *)((char *)r->block + kbytes + pbytes);
-    r->meta = (int32_t *)((char *)r->block + kbytes + pbytes + nbytes);
+    r->gwin = (int32_t *)((char *)r->block + kbytes + pbytes + nbytes);
+    r->plan = (int32_t *)((char *)r->block + kbytes + pbytes + nbytes + mbytes);
     if (n > 0) {
         st = build_map(coords, r, s);
+        if (st == SUBMCONV_OK) st = win_plan_build(r, s);
         if (st != SUBMCONV_OK) {
             dev_free(r->block, s);
             delete r;
@@ -219,7 +225,7 @@ int submconv_forward_variant(const void *feats, const void *weight, const float 
     if (cin < 1 || cin > 1024 || cout < 1 || cout > 1024)
         return fail(SUBMCONV_E_UNSUPPORTED, "channel counts %d -> %d outside 1..1024", cin, cout);
     if (flip != 0 && flip != 1) return fail(SUBMCONV_E_INVALID_ARG, "flip must be 0 or 1");
-    if (variant < SUBMCONV_KERNEL_AUTO || variant > SUBMCONV_KERNEL_MFMA)
+    if (variant < SUBMCONV_KERNEL_AUTO || variant > SUBMCONV_KERNEL_WINDOW)
         return fail(SUBMCONV_E_INVALID_ARG, "unknown kernel variant %d", variant);
     const int64_t n = rb->n;
     if (n == 0) return SUBMCONV_OK;

@@ -161,6 +161,12 @@ __device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t *lds
     return x + before;
 }
 
+// Group windows: per group of 32 consecutive sorted voxels, for each of the 9
+// (dz, dy) rows the first (ints 0-8) and last (ints 9-17) sorted position its
+// neighbours in that row occupy; an empty row holds (GWIN_NONE, -1).
+constexpr int GWIN_INTS = 18;
+constexpr int32_t GWIN_NONE = 0x7fffffff;
+
 }  // namespace sc
 
 // Rulebook: library-owned device memory for one coordinate set.  Everything is
@@ -174,11 +180,12 @@ struct submconv_rulebook {
     int32_t key_bytes;  // 4 or 8
     int32_t device;
     int64_t taps;       // P: present entries of the table
-    int64_t ntiles;     // tiles of 256 sorted voxels
+    int64_t ngroups;    // groups of 32 sorted voxels
     void *block;        // single allocation holding the arrays below
     void *keys;         // sorted keys [n]
     int32_t *perm;      // sorted position -> input row [n]
     int32_t *nbr_sp;    // [n,27]: sorted position of each neighbour, or -1 (padded allocation)
-    int32_t *meta;      // [ntiles,32]: tile neighbourhood ranges (see mapbuild.hip)
+    int32_t *gwin;      // [ngroups,18]: group row windows (see mapbuild.hip)
     int32_t *nbr_in;    // [n,27] input-order table of input rows, built on first request (or null)
+    int32_t *plan;      // staging plan of the windowed forward kernel (see conv_win.hip)
 };

@@ -615,8 +615,13 @@ static int launch_mfma(const void *f, const void *w, const float *b, const int32
     return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: Cin must be 32, 64 or 128");
 }
 
+bool window_supported(int cin, int cout, int dtype);
+int launch_window(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb,
+                  void *out, int cin, int cout, int dtype, int flip, hipStream_t s);
+
 int choose_forward_kernel(int cin, int cout, int dtype)
 {
+    if (window_supported(cin, cout, dtype)) return SUBMCONV_KERNEL_WINDOW;
     if (mfma_size(cin) && mfma_size(cout)) return SUBMCONV_KERNEL_MFMA;
     if (pow2_le32(cin) && pow2_le32(cout)) return SUBMCONV_KERNEL_LOWC;
     (void)dtype;
@@ -641,6 +646,8 @@ int launch_forward(const void *feats, const void *w, const float *bias, const su
                    : launch_lowc<uint16_t>(feats, w, bias, nbr, perm, out, n, cin, cout, flip, s);
     case SUBMCONV_KERNEL_MFMA:
         return launch_mfma(feats, w, bias, nbr, perm, out, n, cin, cout, dtype, flip, s);
+    case SUBMCONV_KERNEL_WINDOW:
+        return launch_window(feats, w, bias, rb, out, cin, cout, dtype, flip, s);
     }
     return fail(SUBMCONV_E_INVALID_ARG, "unknown forward kernel variant %d", variant);
 }

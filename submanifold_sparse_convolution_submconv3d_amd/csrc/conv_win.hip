@@ -1,0 +1,536 @@
+// Windowed forward kernel: a tile's whole neighbourhood staged once in LDS.
+//
+// The convolution (lato.2_mrp_mlx working notes, "Key facts" and commit
+// summary) is the same as in conv.hip:
+//   out[i, o] = bias[o] + sum_k sum_c W[o, k', c] * feats[nbr[i, k], c].
+// Gathering a 64-byte feature row per (voxel, tap) through the vector-memory
+// path is bound by per-cache-line work, not bytes: a random-row gather that
+// misses L1 moves only a fraction of what LDS moves for the same pattern.  So
+// this kernel stages each tile's neighbour rows in LDS once, using what the map
+// builder records: sorted voxels' neighbours in one (dz, dy) row lie in a narrow
+// window of sorted positions, and the windows of a tile's 9 rows merge into a
+// few ranges.  A neighbour's LDS slot is then its sorted position plus a
+// per-row constant, so no search and no deduplication is needed.
+//
+// Tiles of 128 sorted voxels; one persistent block per CU, 8 waves (two per
+// SIMD).  Waves w and w + 4 compute the same 32-voxel column of the tile, over
+// taps 0-13 and 14-26, and add their partial sums through LDS at the end.
+//   * each wave's weight taps sit in registers for the whole kernel (MFMA A
+//     operand, out^T = W_k . F_k^T, rows = output channels);
+//   * double-buffered LDS: while a tile is computed, the next tile's rows and
+//     neighbour-table block are copied in by direct global->LDS loads, and the
+//     sorted->input row numbers of the tile after that are fetched;
+//   * rows are stored as four 16-byte chunks with the chunk order XOR-swizzled
+//     by the slot, so the 32 rows a B-operand read touches spread over the
+//     LDS banks;
+//   * a tile whose merged windows exceed the buffer is computed with direct
+//     global gathers instead (rare on surface data);
+//   * tiles are split among the 8 XCDs in contiguous runs (a workgroup's XCD is
+//     its id mod 8), so neighbouring tiles share an L2.
+// Accumulation is fp32; the bf16 output is one rounding of the fp32 sum.
+#include <type_traits>
+#include <utility>
+
+#include "common.h"
+
+namespace sc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));  // converted with round-to-nearest-even
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+__device__ uint4 g_win_zero[16] = {};  // 256 bytes of zeros: padding slots and missing rows
+
+// ---------------------------------------------------------------------------
+// staging plan: one record of PLAN_INTS per tile
+//   [0]      rows to stage R, or -1 when they exceed the capacity (direct gathers)
+//   [1]      number of ranges nr (<= 9)
+//   [2..10]  first sorted position of range r
+//   [11..19] first slot of range r (slot 0 for range 0, increasing)
+//   [20..28] per (dz, dy) row d: slot = sorted position + delta[d]
+// ---------------------------------------------------------------------------
+
+constexpr int PLAN_INTS = 32;
+constexpr int WIN_TILE = 128;    // voxels per tile (4 groups of 32)
+constexpr int WIN_SLOTS = 1024;  // row slots per buffer; the last one always holds zeros
+constexpr int WIN_CAP = WIN_SLOTS - 1;
+
+// One thread per tile: union of its groups' row windows, sorted and merged.
+// Straight-line code with compile-time indices (registers only).
+__global__ __launch_bounds__(256) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
+                                                  int64_t ntiles, int gpt, int cap,
+                                                  int32_t *__restrict__ plan)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= ntiles) return;
+    int32_t lo[9], hi[9], row[9];
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+        lo[d] = GWIN_NONE;
+        hi[d] = -1;
+        row[d] = d;
+    }
+    for (int g = 0; g < gpt; ++g) {
+        const int64_t gi = t * gpt + g;
+        if (gi >= ngroups) break;
+        const int32_t *w = gwin + gi * GWIN_INTS;
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const int32_t h = w[9 + d];
+            if (h >= 0) {
+                lo[d] = min(lo[d], w[d]);
+                hi[d] = max(hi[d], h);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8 - i; ++j) {
+            const bool sw = lo[j] > lo[j + 1];
+            const int32_t a = lo[j], b = hi[j], c = row[j];
+            lo[j] = sw ? lo[j + 1] : a;
+            hi[j] = sw ? hi[j + 1] : b;
+            row[j] = sw ? row[j + 1] : c;
+            lo[j + 1] = sw ? a : lo[j + 1];
+            hi[j + 1] = sw ? b : hi[j + 1];
+            row[j + 1] = sw ? c : row[j + 1];
+        }
+    int32_t *p = plan + t * PLAN_INTS;
+    int nr = 0, total = 0;
+    int32_t cur_lo = 0, cur_hi = -2;
+    int32_t delta[9];
+#pragma unroll
+    for (int d = 0; d < 9; ++d) delta[d] = 0;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        if (lo[i] == GWIN_NONE) continue;  // empty rows sort last
+        if (nr == 0 || lo[i] > cur_hi + 1) {
+            if (nr > 0) total += cur_hi - cur_lo + 1;
+            p[2 + nr] = lo[i];
+            p[11 + nr] = total;
+            cur_lo = lo[i];
+            cur_hi = hi[i];
+            ++nr;
+        } else if (hi[i] > cur_hi) {
+            cur_hi = hi[i];
+        }
+        const int32_t dl = total - cur_lo;  // slot of sorted position q in this range: q + dl
+#pragma unroll
+        for (int d = 0; d < 9; ++d)
+            if (row[i] == d) delta[d] = dl;
+    }
+    if (nr > 0) total += cur_hi - cur_lo + 1;
+    for (int r = nr; r < 9; ++r) {
+        p[2 + r] = 0;
+        p[11 + r] = total;
+    }
+#pragma unroll
+    for (int d = 0; d < 9; ++d) p[20 + d] = delta[d];
+    p[0] = total <= cap ? total : -1;
+    p[1] = nr;
+    p[29] = p[30] = p[31] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// the kernel (bf16, Cin = Cout = 32)
+// ---------------------------------------------------------------------------
+
+constexpr int W32_ROW = 64;                                   // bytes per staged row
+constexpr int W32_TBL = 14 * 1024 + 512;                      // table block (13824 B in whole 1-KB copies)
+                                                              // then the tile's 128 sort-order row numbers
+constexpr int W32_PERM = WIN_SLOTS * 64 + 14 * 1024;          // offset of those row numbers
+constexpr int W32_BUF = WIN_SLOTS * W32_ROW + W32_TBL;        // one buffer
+constexpr int W32_LDS = 2 * W32_BUF;                          // 159744 B, two buffers
+static_assert(W32_LDS <= 160 * 1024, "LDS budget");
+static_assert(WIN_TILE * 27 * 4 <= W32_TBL, "table block");
+
+__device__ __forceinline__ int w32_chunk_addr(int slot, int chunk)  // byte offset of a row chunk
+{
+    return slot * W32_ROW + ((chunk ^ ((slot >> 1) & 3)) << 4);
+}
+
+__device__ __forceinline__ int plan_get(int pv, int idx) { return __builtin_amdgcn_readlane(pv, idx); }
+
+constexpr int W32_WAVES = 8;   // two per SIMD; waves w and w+4 share a 32-voxel column
+constexpr int W32_CHUNKS = 2;  // 64-slot chunks of a tile's row numbers per wave: wave + 8c
+static_assert(W32_WAVES * W32_CHUNKS * 64 >= WIN_SLOTS, "row-number chunks cover the buffer");
+
+// A copy instruction puts lane l's 16 bytes at slot 16i + l/4, position l%4; the
+// position holds chunk (l%4) ^ ((slot >> 1) & 3) = (l%4) ^ ((l >> 3) & 3).
+__device__ __forceinline__ int w32_lane_chunk(int lane) { return (lane & 3) ^ ((lane >> 3) & 3); }
+
+// The ranges of a tile's plan in registers: slots from off[r] hold sorted
+// positions slot + base[r].
+struct W32Ranges {
+    int R, nr;
+    int off[9], base[9];
+};
+__device__ __forceinline__ W32Ranges w32_ranges(int pv)
+{
+    W32Ranges g;
+    g.R = plan_get(pv, 0);
+    g.nr = plan_get(pv, 1);
+#pragma unroll
+    for (int r = 0; r < 9; ++r) {
+        g.off[r] = plan_get(pv, 11 + r);
+        g.base[r] = plan_get(pv, 2 + r) - g.off[r];
+    }
+    return g;
+}
+
+// Input row of `slot` (-1 past R): one lane per slot.
+__device__ __forceinline__ int32_t w32_row_of(const int32_t *__restrict__ perm, int64_t n, const W32Ranges &g,
+                                              int slot)
+{
+    if (slot >= g.R) return -1;
+    int32_t b = g.base[0];
+#pragma unroll
+    for (int q = 1; q < 9; ++q) {
+        if (q >= g.nr) break;
+        b = slot >= g.off[q] ? g.base[q] : b;
+    }
+    const int32_t pos = b + slot;
+    return (uint32_t)pos < (uint64_t)n ? perm[pos] : -1;
+}
+
+// Row copy `item` = 4c + q of this wave: slots 64k + 16q .. +15 of chunk k = wave + 8c.
+// rid[item] holds, in lane l, the input row of slot 64k + 16q + l/4.
+__device__ __forceinline__ void w32_copy_rows(char *buf, const uint16_t *__restrict__ feats, int64_t n, int R,
+                                              int32_t rid, int item, int wave, int lane, int lchunk)
+{
+    const int k = wave + W32_WAVES * (item >> 2);
+    const int slot0 = 64 * k + 16 * (item & 3);
+    if (slot0 >= R) return;
+    const int slot = slot0 + (lane >> 2);
+    const void *src = slot < R && (uint32_t)rid < (uint64_t)n ? (const void *)(feats + (int64_t)rid * 32 + lchunk * 8)
+                                                              : (const void *)g_win_zero;
+    __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(buf + slot0 * W32_ROW), 16, 0, 0);
+}
+
+// Copies of a tile's neighbour-table block (whole 1-KB copies; the table
+// allocation is padded by 1 KB) and of its 128 output row numbers perm[s0 ..]
+// (4 bytes per lane; entries past n read the table allocation that follows perm
+// and are never used).
+__device__ __forceinline__ void w32_copy_table(char *buf, const int32_t *__restrict__ nbr_sp,
+                                               const int32_t *__restrict__ perm, int64_t n, int64_t tile,
+                                               int wave, int lane)
+{
+    const int64_t s0 = tile * WIN_TILE;
+    const int64_t cnt = (n - s0) < WIN_TILE ? (n - s0) : WIN_TILE;
+    const int nt = (int)((cnt * 27 * 4 + 1023) >> 10);
+    const char *tb = (const char *)(nbr_sp + s0 * 27);
+    for (int i = wave; i < nt; i += W32_WAVES)
+        __builtin_amdgcn_global_load_lds((gbl_void *)(tb + i * 1024 + lane * 16),
+                                         (lds_void *)(buf + WIN_SLOTS * W32_ROW + i * 1024), 16, 0, 0);
+    if (wave == W32_WAVES - 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_global_load_lds((gbl_void *)(perm + s0 + 64 * h + lane),
+                                             (lds_void *)(buf + W32_PERM + 256 * h), 4, 0, 0);
+    }
+}
+
+// Spread the row numbers (one per lane and slot) to the copy lanes (four per slot).
+__device__ __forceinline__ void w32_expand(const int32_t (&rows)[W32_CHUNKS], int32_t (&rid)[4 * W32_CHUNKS],
+                                           int lane)
+{
+#pragma unroll
+    for (int c = 0; c < W32_CHUNKS; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rid[4 * c + q] = __shfl(rows[c], 16 * q + (lane >> 2), 64);
+}
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// global loads (the next tile's copies stay in flight across it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void w32_mfma(floatx16 &acc, const uint4 &a, const uint4 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  acc, 0, 0, 0);
+}
+
+template <int J> using w32_item = std::integral_constant<int, J>;
+constexpr int W32_ITEMS = 13;  // side-work items per tile (see the kernel)
+
+// f(w32_item<I>{}), ..., f(w32_item<N - 1>{}) with compile-time indices
+template <int I, int N, typename F>
+__device__ __forceinline__ void w32_unroll(F &&f)
+{
+    if constexpr (I < N) {
+        f(w32_item<I>{});
+        w32_unroll<I + 1, N>(f);
+    }
+}
+
+// Taps K0 .. K0 + NK - 1 of this lane's voxel from the staged rows, with the
+// tile's side work (copies for the next tiles, stores of the previous one)
+// issued between the MFMAs.  e: the voxel's table entries for these taps
+// (sorted positions); delta from the plan; ok: the voxel exists.  Row reads run
+// PF taps ahead of their MFMAs.  Chunk 2 + kh sits at the chunk-kh address XOR
+// 32 (the swizzle flips bit 1 of the position, and 2 + kh = kh ^ 2).
+template <int K0, int NK, typename Side>
+__device__ __forceinline__ void w32_taps_lds(floatx16 &acc, const char *cur, const int (&e)[14], const int (&delta)[9],
+                                             bool ok, int kh, const uint4 (&wf)[14][2], Side &&side)
+{
+    constexpr int PF = 1;
+    int addr[NK];
+    uint4 b[PF + 1][2];
+    auto prep = [&](int j) {
+        int slot = e[j] + delta[(K0 + j) / 3];
+        slot = (ok && e[j] >= 0 && (unsigned)slot < (unsigned)WIN_CAP) ? slot : WIN_CAP;
+        addr[j] = w32_chunk_addr(slot, kh);
+        b[j % (PF + 1)][0] = *(const uint4 *)(cur + addr[j]);
+        b[j % (PF + 1)][1] = *(const uint4 *)(cur + (addr[j] ^ 32));
+    };
+#pragma unroll
+    for (int j = 0; j < PF; ++j) prep(j);
+    auto one = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + PF < NK) prep(j + PF);
+        if constexpr (j < W32_ITEMS) side(jc);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads and the side work ahead of the MFMAs
+        w32_mfma(acc, wf[j][0], b[j % (PF + 1)][0]);
+        w32_mfma(acc, wf[j][1], b[j % (PF + 1)][1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    w32_unroll<0, NK>(one);
+    w32_unroll<NK, W32_ITEMS>(side);
+}
+
+// The same taps gathered from global memory (a tile whose neighbourhood did not fit);
+// the side work goes first.
+template <int K0, int NK, typename Side>
+__device__ __forceinline__ void w32_taps_global(floatx16 &acc, const uint16_t *__restrict__ feats,
+                                                const int32_t *__restrict__ perm, int64_t n, const int (&e)[14],
+                                                bool ok, int kh, const uint4 (&wf)[14][2], Side &&side)
+{
+    w32_unroll<0, W32_ITEMS>(side);
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int32_t r = (ok && e[j] >= 0 && e[j] < n) ? perm[e[j]] : -1;
+        uint4 b0 = make_uint4(0, 0, 0, 0), b1 = b0;
+        if ((uint32_t)r < (uint64_t)n) {
+            b0 = *(const uint4 *)(feats + (int64_t)r * 32 + 8 * kh);
+            b1 = *(const uint4 *)(feats + (int64_t)r * 32 + 16 + 8 * kh);
+        }
+        w32_mfma(acc, wf[j][0], b0);
+        w32_mfma(acc, wf[j][1], b1);
+    }
+}
+
+__global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restrict__ feats,
+                                                       const uint16_t *__restrict__ weight,
+                                                       const float *__restrict__ bias,
+                                                       const int32_t *__restrict__ nbr_sp,
+                                                       const int32_t *__restrict__ perm,
+                                                       const int32_t *__restrict__ plan,
+                                                       uint16_t *__restrict__ out, int64_t n,
+                                                       int64_t ntiles, int flip)
+{
+    // two buffers as two objects: the compiler tracks the direct-to-LDS copies per
+    // object, so reads of one buffer need not wait for copies into the other
+    __shared__ __attribute__((aligned(1024))) char buf0[W32_BUF];
+    __shared__ __attribute__((aligned(1024))) char buf1[W32_BUF];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, kh = lane >> 5;
+    const int cb = wave & 3, th = wave >> 2;  // column block, tap half (taps 0-13 or 14-26)
+    const int lchunk = w32_lane_chunk(lane);
+
+    // tiles of this block: the XCD's contiguous run, dealt round-robin to its blocks
+    const int xcd = blockIdx.x & 7, bpx = gridDim.x >> 3, jb = blockIdx.x >> 3;
+    const int64_t t_begin = ntiles * xcd / 8, t_end = ntiles * (xcd + 1) / 8;
+    const int64_t first = t_begin + jb;
+    const int64_t count = first < t_end ? (t_end - first + bpx - 1) / bpx : 0;
+    if (count == 0) return;
+
+    // the zero slot of both buffers
+    if (tid < 4) *(uint4 *)(buf0 + WIN_CAP * W32_ROW + tid * 16) = make_uint4(0, 0, 0, 0);
+    else if (tid < 8) *(uint4 *)(buf1 + WIN_CAP * W32_ROW + (tid - 4) * 16) = make_uint4(0, 0, 0, 0);
+
+    // weights of this wave's taps: lane holds output channel `col`, input
+    // channels 16h + 8kh .. +7 (the last slot of the second half is unused)
+    uint4 wf[14][2];
+#pragma unroll
+    for (int j = 0; j < 14; ++j) {
+        const int k = 14 * th + j < 27 ? 14 * th + j : 26;
+        const int kk = flip ? 26 - k : k;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            wf[j][h] = *(const uint4 *)(weight + ((int64_t)col * 27 + kk) * 32 + 16 * h + 8 * kh);
+    }
+
+    auto tile_at = [&](int64_t i) { return first + i * bpx; };
+    auto plan_load = [&](int64_t i) { return i < count ? plan[tile_at(i) * PLAN_INTS + (lane & 31)] : 0; };
+
+    // prologue: plans of tiles 0, 1, 2; copies of tile 0; row numbers of tile 1
+    int pv0 = plan_load(0), pv1 = plan_load(1), pv2 = plan_load(2);
+    int32_t rows[W32_CHUNKS], rid[4 * W32_CHUNKS];
+    {
+        const W32Ranges g0 = w32_ranges(pv0);
+#pragma unroll
+        for (int c = 0; c < W32_CHUNKS; ++c) rows[c] = w32_row_of(perm, n, g0, 64 * (wave + W32_WAVES * c) + lane);
+        w32_expand(rows, rid, lane);
+#pragma unroll
+        for (int it = 0; it < 4 * W32_CHUNKS; ++it) w32_copy_rows(buf0, feats, n, g0.R, rid[it], it, wave, lane, lchunk);
+        w32_copy_table(buf0, nbr_sp, perm, n, tile_at(0), wave, lane);
+        if (count > 1) {
+            const W32Ranges g1 = w32_ranges(pv1);
+#pragma unroll
+            for (int c = 0; c < W32_CHUNKS; ++c) rows[c] = w32_row_of(perm, n, g1, 64 * (wave + W32_WAVES * c) + lane);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // the finished outputs of the previous tile, stored during the next one
+    uint16_t *pend_out = nullptr;
+    uint32_t pend[8];
+
+    // one tile; ODD selects the buffers at compile time (the loop is unrolled by two)
+    auto step = [&](auto odd, int64_t i) {
+        char *cur = decltype(odd)::value ? buf1 : buf0;
+        char *nxt = decltype(odd)::value ? buf0 : buf1;
+        const int64_t tile = tile_at(i);
+        const int R0 = plan_get(pv0, 0), R1 = plan_get(pv1, 0);
+        int delta[9];
+#pragma unroll
+        for (int d = 0; d < 9; ++d) delta[d] = plan_get(pv0, 20 + d);
+        W32Ranges g2;
+        const bool more1 = i + 1 < count, more2 = i + 2 < count;
+        w32_expand(rows, rid, lane);  // row numbers of tile i+1, for its copies
+        int pv3 = 0;
+
+        // side work, one item per tap: 0 the table block of tile i+1 (first: it comes
+        // from HBM, read once), 1-8 its row copies, 9 the stores of tile i-1, 10 the
+        // plan of tile i+3, 11-12 row numbers of tile i+2
+        auto side = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j == 0) {
+                if (more1) w32_copy_table(nxt, nbr_sp, perm, n, tile_at(i + 1), wave, lane);
+            } else if constexpr (j <= 8) {
+                if (more1) w32_copy_rows(nxt, feats, n, R1, rid[j - 1], j - 1, wave, lane, lchunk);
+            } else if constexpr (j == 9) {
+                if (pend_out) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) *(uint2 *)(pend_out + 8 * g) = make_uint2(pend[2 * g], pend[2 * g + 1]);
+                }
+            } else if constexpr (j == 10) {
+                pv3 = plan_load(i + 3);
+            } else if constexpr (j == 11 || j == 12) {
+                constexpr int c = j - 11;
+                if constexpr (c == 0) g2 = w32_ranges(pv2);
+                if (more2) rows[c] = w32_row_of(perm, n, g2, 64 * (wave + W32_WAVES * c) + lane);
+            }
+        };
+
+        // this wave's taps for its 32 voxels
+        const int64_t s = tile * WIN_TILE + cb * 32 + col;
+        const bool valid = s < n;
+        const int32_t *tbl = (const int32_t *)(cur + WIN_SLOTS * W32_ROW) + (cb * 32 + col) * 27 + 14 * th;
+        int e[14];
+#pragma unroll
+        for (int j = 0; j < 14; ++j) e[j] = (th == 1 && j == 13) ? -1 : tbl[j];
+        floatx16 acc = {};
+        if (R0 >= 0) {
+            if (th == 0) w32_taps_lds<0, 14>(acc, cur, e, delta, valid, kh, wf, side);
+            else w32_taps_lds<14, 13>(acc, cur, e, delta, valid, kh, wf, side);
+        } else {
+            // neighbourhood too wide for the buffer: gather the rows from global memory
+            if (th == 0) w32_taps_global<0, 14>(acc, feats, perm, n, e, valid, kh, wf, side);
+            else w32_taps_global<14, 13>(acc, feats, perm, n, e, valid, kh, wf, side);
+        }
+        // combine the two tap halves through LDS (the current rows are no longer read)
+        lds_barrier();
+        float4 *red = (float4 *)(cur + cb * 4096) + lane;
+        if (th == 1) {  // the second tap half also adds the bias (once per output)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 bv = bias ? *(const float4 *)(bias + 8 * g + 4 * kh) : make_float4(0.f, 0.f, 0.f, 0.f);
+                red[64 * g] = make_float4(acc[4 * g] + bv.x, acc[4 * g + 1] + bv.y, acc[4 * g + 2] + bv.z,
+                                          acc[4 * g + 3] + bv.w);
+            }
+        }
+        lds_barrier();
+        pend_out = nullptr;
+        if (th == 0 && valid) {
+            // this lane holds output channels 8g + 4kh .. +3 of its voxel, g = 0..3
+            pend_out = out + (int64_t)((const int32_t *)(cur + W32_PERM))[cb * 32 + col] * 32 + 4 * kh;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 p = red[64 * g];
+                const floatx2 lo = {acc[4 * g] + p.x, acc[4 * g + 1] + p.y};
+                const floatx2 hi = {acc[4 * g + 2] + p.z, acc[4 * g + 3] + p.w};
+                pend[2 * g] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+                pend[2 * g + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+            }
+        }
+        pv0 = pv1;
+        pv1 = pv2;
+        pv2 = pv3;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    for (int64_t i = 0; i < count; i += 2) {
+        step(std::integral_constant<int, 0>{}, i);
+        if (i + 1 < count) step(std::integral_constant<int, 1>{}, i + 1);
+    }
+    if (pend_out) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *(uint2 *)(pend_out + 8 * g) = make_uint2(pend[2 * g], pend[2 * g + 1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+// Staging plan of a rulebook (part of the map build): PLAN_INTS per tile.
+int64_t win_plan_ints(int64_t n) { return (n + WIN_TILE - 1) / WIN_TILE * PLAN_INTS; }
+
+int win_plan_build(submconv_rulebook *rb, hipStream_t s)
+{
+    const int64_t ntiles = (rb->n + WIN_TILE - 1) / WIN_TILE;
+    if (ntiles == 0) return SUBMCONV_OK;
+    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, s, rb->gwin,
+                       rb->ngroups, ntiles, WIN_TILE / 32, WIN_CAP, rb->plan);
+    SC_LAUNCHED("win_plan");
+    return SUBMCONV_OK;
+}
+
+static int device_cus(int dev)
+{
+    static int cached[64] = {};
+    if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev >= 0 && dev < 64) cached[dev] = cus;
+    return cus;
+}
+
+bool window_supported(int cin, int cout, int dtype)
+{
+    return dtype == SUBMCONV_BF16 && cin == 32 && cout == 32;
+}
+
+int launch_window(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb,
+                  void *out, int cin, int cout, int dtype, int flip, hipStream_t s)
+{
+    if (!window_supported(cin, cout, dtype))
+        return fail(SUBMCONV_E_UNSUPPORTED, "window kernel: bf16 with Cin = Cout = 32 only");
+    const int64_t ntiles = (rb->n + WIN_TILE - 1) / WIN_TILE;
+    int blocks = device_cus(rb->device) & ~7;
+    if (blocks < 8) blocks = 8;
+    hipLaunchKernelGGL(k_conv_win32, dim3((unsigned)blocks), dim3(W32_WAVES * 64), 0, s, (const uint16_t *)feats,
+                       (const uint16_t *)w, bias, rb->nbr_sp, rb->perm, rb->plan, (uint16_t *)out, rb->n,
+                       ntiles, flip);
+    SC_LAUNCHED("conv_win32");
+    return SUBMCONV_OK;
+}
+
+}  // namespace sc

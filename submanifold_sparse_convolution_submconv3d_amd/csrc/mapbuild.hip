@@ -10,11 +10,11 @@
 // (b, z, y, x)):
 //   keys[s], perm[s] (the input row of sorted voxel s),
 //   nbr_sp[s][k]  the SORTED POSITION of the voxel at key[s] + offset(k), or -1,
-//   tile metadata  per tile of 256 sorted voxels: the merged ranges of sorted
-//                  positions that hold all the tile's neighbours, and for each
-//                  (dz, dy) row the offset from a sorted position to its place
-//                  in the concatenated ranges (so a kernel can stage the tile's
-//                  whole neighbourhood in LDS and index it directly).
+//   gwin[g]        per group of 32 consecutive sorted voxels and per (dz, dy)
+//                  row: the first and last sorted position the group's
+//                  neighbours in that row occupy.  A kernel merges the windows
+//                  of the groups it processes into a few ranges of sorted
+//                  positions, stages them in LDS and indexes them directly.
 // The input-order table nbr[i][k] (input rows) is derived from these on request.
 //
 // Dense key space (2^nbits bitmap bits affordable next to N):
@@ -85,129 +85,47 @@ __device__ __forceinline__ K add_sat(K a, int64_t delta)
 }
 
 // ---------------------------------------------------------------------------
-// tile metadata
+// group windows
 // ---------------------------------------------------------------------------
 
-// Fold one voxel's 27 sorted positions into the tile's per-row [lo, hi] in LDS.
-// Every lane of the block must call it, lanes in sorted order.
+// Write the row windows of the wave's two groups (lanes 0-31, 32-63) from each
+// lane's 27 sorted positions.  Every lane of the wave must call it, lanes in
+// sorted order; groups at or past `ngroups` are not written.
 //
 // For a fixed (dz, dy) row the window [first present, last present] of a voxel
 // is monotone in sorted order: a later voxel's cells are all >= the earlier
 // voxel's cell at dx = 0, which is present or else not before the earlier
-// voxel's first present cell.  So a wave's window for the row is the first
+// voxel's first present cell.  So a group's window for the row is the first
 // such lane's lo and the last such lane's hi: one ballot per row, no reduction.
-__device__ __forceinline__ void tile_windows_add(const int32_t (&p)[27], bool valid, int32_t *s_lo,
-                                                 int32_t *s_hi)
+__device__ __forceinline__ void group_windows_write(const int32_t (&p)[27], bool valid, int64_t group,
+                                                    int64_t ngroups, int32_t *__restrict__ gwin)
 {
-    const int lane = (int)(threadIdx.x & 63);
+    const int lane = (int)(threadIdx.x & 63), half = lane >> 5;
+    const bool owner = group < ngroups;
+    int32_t *w = gwin + group * GWIN_INTS;
 #pragma unroll
     for (int d = 0; d < 9; ++d) {
         const int32_t a = p[3 * d], b = p[3 * d + 1], c = p[3 * d + 2];
         const int32_t lo = a >= 0 ? a : (b >= 0 ? b : c);
         const int32_t hi = c >= 0 ? c : (b >= 0 ? b : a);
         const uint64_t mask = __ballot(valid && hi >= 0);
-        if (!mask) continue;
-        const int first = __ffsll((long long)mask) - 1;
-        const int last = 63 - __clzll((long long)mask);
-        if (lane == first) atomicMin(&s_lo[d], lo);
-        if (lane == last) atomicMax(&s_hi[d], hi);
+        const uint32_t m = (uint32_t)(mask >> (32 * half));
+        const int first = m ? __ffs((int)m) - 1 : 0;
+        const int last = m ? 31 - __clz((int)m) : 0;
+        if (owner && (lane & 31) == first) w[d] = m ? lo : GWIN_NONE;
+        if (owner && (lane & 31) == last) w[9 + d] = m ? hi : -1;
     }
 }
 
-// Merge the 9 row windows into disjoint ranges and write the tile's metadata.
-// One thread, all in registers: an unrolled compare-exchange sort with
-// compile-time indices and a straight-line merge (no private arrays indexed at
-// run time, no LDS round trips).  meta: [0] ranges, [1] total rows,
-// [2..10] range start, [11..19] range length, [20..28] per-row offset.
-__device__ void tile_meta_write(const int32_t *s_lo, const int32_t *s_hi, int32_t *meta)
-{
-    constexpr int32_t NONE = 0x7fffffff;
-    int32_t lo[9], hi[9], row[9];
-#pragma unroll
-    for (int d = 0; d < 9; ++d) {
-        hi[d] = s_hi[d];
-        lo[d] = hi[d] >= 0 ? s_lo[d] : NONE;  // absent rows sort last
-        row[d] = d;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8 - i; ++j) {
-            const bool sw = lo[j] > lo[j + 1];
-            const int32_t a = lo[j], b = hi[j], c = row[j];
-            lo[j] = sw ? lo[j + 1] : a;
-            hi[j] = sw ? hi[j + 1] : b;
-            row[j] = sw ? row[j + 1] : c;
-            lo[j + 1] = sw ? a : lo[j + 1];
-            hi[j + 1] = sw ? b : hi[j + 1];
-            row[j + 1] = sw ? c : row[j + 1];
-        }
-#pragma unroll
-    for (int d = 0; d < 9; ++d) meta[20 + d] = 0;
-    int nr = 0, total = 0;
-    int32_t cur_lo = 0, cur_hi = -2, cur_base = 0;
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-        if (lo[i] == NONE) continue;
-        if (nr == 0 || lo[i] > cur_hi + 1) {  // a new range starts here
-            if (nr > 0) {
-                meta[11 + nr - 1] = cur_hi - cur_lo + 1;
-                total += cur_hi - cur_lo + 1;
-            }
-            meta[2 + nr] = lo[i];
-            cur_lo = lo[i];
-            cur_hi = hi[i];
-            cur_base = total;
-            ++nr;
-        } else if (hi[i] > cur_hi) {
-            cur_hi = hi[i];
-        }
-        meta[20 + row[i]] = cur_base - cur_lo;
-    }
-    if (nr > 0) {
-        meta[11 + nr - 1] = cur_hi - cur_lo + 1;
-        total += cur_hi - cur_lo + 1;
-    }
-    for (int r = nr; r < 9; ++r) meta[2 + r] = meta[11 + r] = 0;
-    meta[0] = nr;
-    meta[1] = total;
-    meta[29] = meta[30] = meta[31] = 0;
-}
-
-// Per-tile record written by the resolve kernels for the merge kernel: the 9 row
-// windows (lo, hi) and the tile's present-entry count.
-constexpr int WREC = 20;
-
-// Table rows of one tile from LDS to global (contiguous run), the tile's record
-// stored.  Called by every thread after its row of s_rows and its share of
-// s_lo / s_hi / *s_taps are written.  No device-scope atomic here: thousands of
-// blocks adding to one address serialise at the memory side.
-__device__ __forceinline__ void tile_finish(const int32_t *s_rows, int count, int32_t *dst,
-                                            const uint32_t *s_taps, const int32_t *s_lo,
-                                            const int32_t *s_hi, int32_t *rec)
-{
-    __syncthreads();
-    if (threadIdx.x < 9) {
-        rec[threadIdx.x] = s_lo[threadIdx.x];
-        rec[9 + threadIdx.x] = s_hi[threadIdx.x];
-    } else if (threadIdx.x == 9) {
-        rec[18] = (int32_t)*s_taps;
-    }
-    for (int e = threadIdx.x; e < count * 27; e += 256) dst[e] = s_rows[e];
-}
-
-// One thread per tile: merge its row windows into the tile metadata; the tiles'
-// present counts are summed per block and added to st->taps once per block.
-__global__ __launch_bounds__(256) void k_tile_merge(const int32_t *__restrict__ rec, int64_t ntiles,
-                                                    int32_t *__restrict__ meta, DevStatus *st)
+// Present-entry counts: one per block of 256 voxels, summed here per 256
+// blocks and added to st->taps once per block (thousands of blocks adding to
+// one address would serialise at the memory side).
+__global__ __launch_bounds__(256) void k_taps_sum(const uint32_t *__restrict__ counts, int64_t nblk,
+                                                  DevStatus *st)
 {
     __shared__ unsigned long long s_sum[4];
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    unsigned long long taps = 0;
-    if (t < ntiles) {
-        tile_meta_write(rec + t * WREC, rec + t * WREC + 9, meta + t * 32);
-        taps = (uint32_t)rec[t * WREC + 18];
-    }
+    unsigned long long taps = t < nblk ? counts[t] : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) taps += __shfl_xor(taps, off, 64);
     if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = taps;
@@ -216,6 +134,17 @@ __global__ __launch_bounds__(256) void k_tile_merge(const int32_t *__restrict__ 
         const unsigned long long sum = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
         if (sum) atomicAdd(&st->taps, sum);
     }
+}
+
+// Table rows of one block from LDS to global (a contiguous run) and the block's
+// present count.  Called by every thread after its row of s_rows is written and
+// its count is added to *s_taps.
+__device__ __forceinline__ void block_finish(const int32_t *s_rows, int count, int32_t *dst,
+                                             const uint32_t *s_taps, uint32_t *blk_taps)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) blk_taps[blockIdx.x] = *s_taps;
+    for (int e = threadIdx.x; e < count * 27; e += 256) dst[e] = s_rows[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -325,18 +254,14 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
                                                     int batch, const unsigned long long *__restrict__ bm,
                                                     const uint32_t *__restrict__ prefix,
                                                     int32_t *__restrict__ nbr_sp,
-                                                    int32_t *__restrict__ windows)
+                                                    int32_t *__restrict__ gwin,
+                                                    uint32_t *__restrict__ blk_taps)
 {
     __shared__ int32_t s_rows[256 * 27];
-    __shared__ int32_t s_lo[9], s_hi[9];
     __shared__ uint32_t s_taps;
     const int tid = threadIdx.x;
     const int64_t s0 = (int64_t)blockIdx.x * 256;
     const int count = (int)((n - s0) < 256 ? (n - s0) : 256);
-    if (tid < 9) {
-        s_lo[tid] = 0x7fffffff;
-        s_hi[tid] = -1;
-    }
     if (tid == 0) s_taps = 0;
     __syncthreads();
     int32_t p[27];
@@ -403,8 +328,8 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
         }
     }
     if (present) atomicAdd(&s_taps, present);
-    tile_windows_add(p, valid, s_lo, s_hi);
-    tile_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, s_lo, s_hi, windows + blockIdx.x * WREC);
+    group_windows_write(p, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
+    block_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, blk_taps);
 }
 
 // ---------------------------------------------------------------------------
@@ -429,12 +354,12 @@ __global__ __launch_bounds__(256) void k_pack(const int4 *__restrict__ coords, i
 template <typename K>
 __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, int64_t n, int res,
                                                      int rb, int32_t *__restrict__ nbr_sp,
-                                                     int32_t *__restrict__ windows, DevStatus *st)
+                                                     int32_t *__restrict__ gwin,
+                                                     uint32_t *__restrict__ blk_taps, DevStatus *st)
 {
     __shared__ K s_win[WIN_MAX];
     __shared__ int32_t s_rows[256 * 27];
     __shared__ int64_t s_wlo[8], s_whi[8];
-    __shared__ int32_t s_lo[9], s_hi[9];
     __shared__ uint32_t s_taps;
 
     const int tid = threadIdx.x;
@@ -446,10 +371,6 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
     const K key = valid ? sk[s] : K(0);
     const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
     const K bpart = (key >> (3 * rb)) << (3 * rb);
-    if (tid < 9) {
-        s_lo[tid] = 0x7fffffff;
-        s_hi[tid] = -1;
-    }
     if (tid == 0) s_taps = 0;
     // window bounds of the 8 off-centre (dz, dy) rows: 16 binary searches, one per thread
     if (tid < 16) {
@@ -520,8 +441,8 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
     }
     if (dup) atomicOr(&st->flags, FLAG_DUPLICATE);
     if (present) atomicAdd(&s_taps, present);
-    tile_windows_add(p, valid, s_lo, s_hi);
-    tile_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, s_lo, s_hi, windows + blockIdx.x * WREC);
+    group_windows_write(p, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
+    block_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, blk_taps);
 }
 
 // ---------------------------------------------------------------------------
@@ -699,30 +620,16 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
     if (tid == 0 && s_red[0]) atomicAdd(&st->taps, (unsigned long long)s_red[0]);
 }
 
-// Row windows of every tile from a finished table (used after the single-block builds).
-__global__ __launch_bounds__(256) void k_tile_windows(const int32_t *__restrict__ nbr_sp, int64_t n,
-                                                      int32_t *__restrict__ windows)
+// Group windows from a finished table (used after the single-block builds).
+__global__ __launch_bounds__(256) void k_group_windows(const int32_t *__restrict__ nbr_sp, int64_t n,
+                                                       int32_t *__restrict__ gwin)
 {
-    __shared__ int32_t s_lo[9], s_hi[9];
-    const int tid = threadIdx.x;
-    const int64_t s = (int64_t)blockIdx.x * 256 + tid;
-    if (tid < 9) {
-        s_lo[tid] = 0x7fffffff;
-        s_hi[tid] = -1;
-    }
-    __syncthreads();
+    const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
     int32_t p[27];
     const bool valid = s < n;
 #pragma unroll
     for (int k = 0; k < 27; ++k) p[k] = valid ? nbr_sp[s * 27 + k] : -1;
-    tile_windows_add(p, valid, s_lo, s_hi);
-    __syncthreads();
-    if (tid < 9) {
-        windows[blockIdx.x * WREC + tid] = s_lo[tid];
-        windows[blockIdx.x * WREC + 9 + tid] = s_hi[tid];
-    } else if (tid == 9) {
-        windows[blockIdx.x * WREC + 18] = 0;  // the single-block builds count their taps themselves
-    }
+    group_windows_write(p, valid, s >> 5, (n + 31) >> 5, gwin);
 }
 
 // ---------------------------------------------------------------------------
@@ -765,6 +672,8 @@ static bool use_bitmap(int64_t n, int nbits)
     return bytes <= 64 * n + (int64_t(4) << 20);
 }
 
+static int64_t grid_blocks(int64_t n) { return (n + 255) / 256; }
+
 template <typename K>
 static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStream_t stream)
 {
@@ -773,8 +682,8 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
     const int64_t words = rb->nbits > 6 ? (int64_t(1) << (rb->nbits - 6)) : 1;  // 64-bit bitmap words
     size_t off = 0, o_keys = 0, o_vals = 0, o_bm = 0, o_pre = 0, o_aux = 0;
-    const size_t o_win = off;  // per tile: row windows and tap count, merged after the resolve
-    off += up((size_t)rb->ntiles * WREC * 4);
+    const size_t o_cnt = off;  // present count per block of 256 voxels
+    off += up((size_t)grid_blocks(n) * 4);
     if (path == 2) {
         o_keys = off; off += up((size_t)n * sizeof(K));
         o_bm = off; off += up((size_t)(words + 1) * 8);  // +1: a 3-cell window may touch the next word
@@ -790,7 +699,7 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     char *scratch = nullptr;
     SC_CHECK(dev_alloc((void **)&scratch, off, stream));
     DevStatus *st = (DevStatus *)(scratch + o_stat);
-    int32_t *windows = (int32_t *)(scratch + o_win);
+    uint32_t *blk_taps = (uint32_t *)(scratch + o_cnt);
     int status = SUBMCONV_OK;
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
@@ -802,7 +711,7 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
             else
                 hipLaunchKernelGGL(k_build_small<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
                                    (int)n, rb->res, rb->batch, rb->rb, (K *)rb->keys, rb->perm, rb->nbr_sp, st);
-            hipLaunchKernelGGL(k_tile_windows, dim3(grid), dim3(256), 0, stream, rb->nbr_sp, n, windows);
+            hipLaunchKernelGGL(k_group_windows, dim3(grid), dim3(256), 0, stream, rb->nbr_sp, n, rb->gwin);
         } else if (path == 2) {
             K *tmp = (K *)(scratch + o_keys);
             unsigned long long *bm = (unsigned long long *)(scratch + o_bm);
@@ -816,7 +725,7 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
             hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n, bm, pre,
                                (K *)rb->keys, rb->perm);
             hipLaunchKernelGGL(k_resolve_bm<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
-                               rb->res, rb->rb, rb->batch, bm, pre, rb->nbr_sp, windows);
+                               rb->res, rb->rb, rb->batch, bm, pre, rb->nbr_sp, rb->gwin, blk_taps);
         } else {
             K *keys_b = (K *)(scratch + o_keys);
             int32_t *vals_b = (int32_t *)(scratch + o_vals);
@@ -827,10 +736,11 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
             if ((status = radix_sort_pairs<K>((K *)rb->keys, rb->perm, keys_b, vals_b, n, rb->nbits,
                                               scratch + o_aux, stream, in_b)) != SUBMCONV_OK) break;
             hipLaunchKernelGGL(k_resolve_win<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
-                               rb->res, rb->rb, rb->nbr_sp, windows, st);
+                               rb->res, rb->rb, rb->nbr_sp, rb->gwin, blk_taps, st);
         }
-        hipLaunchKernelGGL(k_tile_merge, dim3((unsigned)((rb->ntiles + 255) / 256)), dim3(256), 0, stream,
-                           windows, rb->ntiles, rb->meta, st);
+        if (path >= 2)
+            hipLaunchKernelGGL(k_taps_sum, dim3((unsigned)((grid + 255) / 256)), dim3(256), 0, stream,
+                               blk_taps, (int64_t)grid, st);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "kernel launch in build_map failed"); break; }
         DevStatus h;
         if ((status = read_status(st, &h, stream)) != SUBMCONV_OK) break;

@@ -177,7 +177,8 @@ def test_map_deterministic():
 
 # ---------------------------------------------------------------- forward
 
-KERNELS = {"generic": sc.KERNEL_GENERIC, "lowc": sc.KERNEL_LOWC, "mfma": sc.KERNEL_MFMA}
+KERNELS = {"generic": sc.KERNEL_GENERIC, "lowc": sc.KERNEL_LOWC, "mfma": sc.KERNEL_MFMA,
+           "window": sc.KERNEL_WINDOW}
 
 
 def run_forward(c, res, batch, cin, cout, dtype, kernel, flip, seed=0, bias="uniform", std=None):
@@ -204,9 +205,63 @@ def test_forward_random_set(dtype, flip, kernel, cin, cout):
     assert_close(got, expect, dtype, "%s %d->%d %s flip=%d" % (kernel, cin, cout, dtype, flip))
 
 
+def _cube(res, batch=1):
+    g = np.stack(np.meshgrid(np.arange(batch), np.arange(res), np.arange(res), np.arange(res),
+                             indexing="ij"), -1).reshape(-1, 4)
+    return np.ascontiguousarray(g.astype(np.int32))
+
+
+# the windowed kernel (bf16, 32 -> 32): tiles of 128 sorted voxels staged in LDS,
+# tiles whose neighbourhood does not fit gathered from global memory instead
+@pytest.mark.parametrize("case", ["sparse", "cube16", "cube16_ragged", "shell", "mixed", "tiny1", "tiny33",
+                                  "tiny129", "batches"])
+@pytest.mark.parametrize("flip", [0, 1])
+def test_forward_window_sets(case, flip):
+    if case == "sparse":        # wide windows: every tile takes the global-gather path
+        c, res, batch = synth.random_coords(3001, 64, 1, 11), 64, 1
+    elif case == "cube16":      # dense: every tile staged in LDS
+        c, res, batch = _cube(16), 16, 1
+    elif case == "cube16_ragged":
+        c, res, batch = _cube(16)[:4000], 16, 1
+    elif case == "shell":
+        w, c = synth.workload(3)
+        res, batch = w.res, w.batch
+        c = c[:30001]
+    elif case == "mixed":       # a dense cube next to scattered voxels: both paths in one call
+        cube = _cube(12) + np.array([0, 2, 2, 2], np.int32)
+        far = synth.random_coords(700, 64, 1, 12)
+        far = far[(far[:, 1:] >= 20).any(axis=1)]
+        c, res, batch = np.ascontiguousarray(np.concatenate([cube, far])), 64, 1
+    elif case == "tiny1":
+        c, res, batch = np.array([[0, 3, 3, 3]], np.int32), 8, 1
+    elif case == "tiny33":
+        c, res, batch = _cube(4)[:33], 4, 1
+    elif case == "tiny129":
+        c, res, batch = _cube(6)[:129], 6, 1
+    else:
+        c, res, batch = _cube(8, 3), 8, 3
+    got, expect = run_forward(c, res, batch, 32, 32, "bf16", "window", flip, seed=4)
+    assert_close(got, expect, "bf16", "window %s flip=%d" % (case, flip))
+
+
+def test_forward_window_shuffled_and_f32_rejected():
+    w, c = synth.workload(2)
+    p = synth.shuffle_rows(len(c), 5)
+    got, expect = run_forward(np.ascontiguousarray(c[p]), w.res, w.batch, 32, 32, "bf16", "window", 0, seed=2)
+    assert_close(got, expect, "bf16", "window shuffled")
+    rb = build(c, w.res, w.batch)
+    f = torch.zeros((len(c), 32), device=DEV)
+    note("window f32 rejected")
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.submconv_forward(f, torch.zeros((32, 3, 3, 3, 32), device=DEV), None, rb, variant=sc.KERNEL_WINDOW)
+    assert e.value.status == -4
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("kernel,c", [("generic", 8), ("lowc", 16), ("mfma", 32), ("mfma", 128)])
+@pytest.mark.parametrize("kernel,c", [("generic", 8), ("lowc", 16), ("mfma", 32), ("mfma", 128), ("window", 32)])
 def test_forward_identity_kernel_exact(dtype, kernel, c):
+    if kernel == "window" and dtype == "f32":
+        pytest.skip("the windowed kernel takes bf16 only")
     _, coords = synth.workload(2)
     feats = np.random.default_rng(3).standard_normal((len(coords), c)).astype(np.float32)
     weight = np.zeros((c, 3, 3, 3, c), np.float32)
@@ -221,12 +276,14 @@ def test_forward_identity_kernel_exact(dtype, kernel, c):
 @pytest.mark.parametrize("idx,dtype", [(1, "f32"), (2, "f32"), (3, "f32"), (3, "bf16")])
 def test_forward_workloads_full(idx, dtype):
     w, c = synth.workload(idx)
-    got, expect = run_forward(c, w.res, w.batch, w.cin, w.cout, dtype, _auto_kernel(w.cin, w.cout), 0,
+    got, expect = run_forward(c, w.res, w.batch, w.cin, w.cout, dtype, _auto_kernel(w.cin, w.cout, dtype), 0,
                               w.value_seed, w.bias, w.weight_std)
     assert_close(got, expect, dtype, "workload %d %s" % (idx, dtype))
 
 
-def _auto_kernel(cin, cout):
+def _auto_kernel(cin, cout, dtype="f32"):
+    if cin == 32 and cout == 32 and dtype == "bf16":
+        return "window"
     if cin in (32, 64, 128) and cout in (32, 64, 128):
         return "mfma"
     return "lowc" if cin <= 32 and cout <= 32 else "generic"
