@@ -29,7 +29,7 @@ METRIC = "SubMConv3d fwd active-voxels/s + TFLOP/s at 128^3/128ch; map-build ms"
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_submconv3d_amd", "csrc")
-CONV_SRCS = [os.path.join(CSRC, f) for f in ("conv.hip", "conv_win.hip")]
+CONV_SRCS = [os.path.join(CSRC, f) for f in ("conv.hip", "conv_win.hip", "conv_big.hip")]
 MAP_SRCS = [os.path.join(CSRC, f) for f in ("mapbuild.hip", "sort_scan.hip", "conv_win.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 BOUND = {1: "hbm", 2: "mfma", 3: "mfma", 4: "mfma", 5: "hbm"}
@@ -99,7 +99,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--dtype", default=None, choices=[None, "f32", "bf16"])
-    ap.add_argument("--variant", default="auto", choices=["auto", "generic", "lowc", "mfma", "window"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "generic", "lowc", "mfma", "window", "persistent"])
     ap.add_argument("--shuffled", action="store_true", help="seeded random row order")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -117,7 +117,8 @@ def main():
     import submanifold_sparse_convolution_submconv3d_amd as sc
 
     variant = {"auto": sc.KERNEL_AUTO, "generic": sc.KERNEL_GENERIC, "lowc": sc.KERNEL_LOWC,
-               "mfma": sc.KERNEL_MFMA, "window": sc.KERNEL_WINDOW}[args.variant]
+               "mfma": sc.KERNEL_MFMA, "window": sc.KERNEL_WINDOW,
+               "persistent": sc.KERNEL_PERSISTENT}[args.variant]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sc.load_library()

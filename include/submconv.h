@@ -69,6 +69,8 @@ extern "C" {
 #define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128} */
 #define SUBMCONV_KERNEL_WINDOW 4  /* matrix cores fed from a tile's neighbourhood staged in LDS
                                      (bf16, Cin = Cout = 32) */
+#define SUBMCONV_KERNEL_PERSISTENT 5 /* persistent matrix-core kernel, weights streamed through LDS,
+                                        operands gathered into registers (bf16, 64->64 or 128->128) */
 
 typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
 

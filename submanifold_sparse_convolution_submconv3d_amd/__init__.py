@@ -32,14 +32,14 @@ __all__ = [
     "SubmconvError", "Rulebook", "RulebookCache", "lib_path", "load_library",
     "submconv_build_map", "submconv_forward", "submconv_subdivide",
     "submconv_space_to_depth", "submconv_depth_to_space",
-    "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA", "KERNEL_WINDOW",
+    "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA", "KERNEL_WINDOW", "KERNEL_PERSISTENT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_lib", "libsubmconv.so")
 
 F32, BF16 = 0, 1
-KERNEL_AUTO, KERNEL_GENERIC, KERNEL_LOWC, KERNEL_MFMA, KERNEL_WINDOW = 0, 1, 2, 3, 4
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_LOWC, KERNEL_MFMA, KERNEL_WINDOW, KERNEL_PERSISTENT = 0, 1, 2, 3, 4, 5
 
 _lib = None
 

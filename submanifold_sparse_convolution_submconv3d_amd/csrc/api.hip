@@ -225,7 +225,7 @@ int submconv_forward_variant(const void *feats, const void *weight, const float 
     if (cin < 1 || cin > 1024 || cout < 1 || cout > 1024)
         return fail(SUBMCONV_E_UNSUPPORTED, "channel counts %d -> %d outside 1..1024", cin, cout);
     if (flip != 0 && flip != 1) return fail(SUBMCONV_E_INVALID_ARG, "flip must be 0 or 1");
-    if (variant < SUBMCONV_KERNEL_AUTO || variant > SUBMCONV_KERNEL_WINDOW)
+    if (variant < SUBMCONV_KERNEL_AUTO || variant > SUBMCONV_KERNEL_PERSISTENT)
         return fail(SUBMCONV_E_INVALID_ARG, "unknown kernel variant %d", variant);
     const int64_t n = rb->n;
     if (n == 0) return SUBMCONV_OK;

@@ -169,6 +169,16 @@ __device__ __forceinline__ void stage_nbr(const int32_t *nbr, int64_t n, int64_t
     }
 }
 
+// Block index remapped so that each of the 8 XCDs (workgroup id mod 8) takes a
+// contiguous run of blocks: consecutive sorted voxels share neighbours, so the
+// run's gathers stay within one L2 instead of every L2 seeing the whole set.
+__device__ __forceinline__ int64_t xcd_block()
+{
+    const int64_t g = gridDim.x, b = blockIdx.x;
+    const int64_t q = g >> 3, r = g & 7, x = b & 7;
+    return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {
     static __device__ __forceinline__ void step(floatx16 &acc, const uint4 &a, const uint4 &b)
@@ -231,7 +241,8 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t vbase = ((int64_t)blockIdx.x * 4 + wave) * (VT * 32);
+    const int64_t blk = xcd_block();
+    const int64_t vbase = (blk * 4 + wave) * (VT * 32);
 
     // copy weight tap k (kernel tap k' = flip ? 26-k : k) into LDS buffer `buf`
     auto stage_w = [&](int k, int buf) {
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     } else {
         stage_w(0, 0);
     }
-    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, (int64_t)blockIdx.x * S::VOX_PER_BLOCK, (char *)sN, wave, lane);
+    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK, (char *)sN, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     bool any0 = load_tap(0, j0, F0), any1 = false;
@@ -395,7 +406,8 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     char *sF = lds + S::WBUF * S::W_TAP + wave * ROWS * RB;     // this wave's [ROWS][RB]
     const int32_t *sN = (const int32_t *)(lds + S::WBUF * S::W_TAP + 4 * ROWS * RB);  // [block voxels][27]
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t vbase = ((int64_t)blockIdx.x * 4 + wave) * ROWS;
+    const int64_t blk = xcd_block();
+    const int64_t vbase = (blk * 4 + wave) * ROWS;
 
     // weight tap k -> LDS buffer buf, whole rows, swizzled
     auto stage_w = [&](int k, int buf) {
@@ -444,7 +456,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     } else {
         stage_w(0, 0);
     }
-    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, (int64_t)blockIdx.x * S::VOX_PER_BLOCK,
+    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK,
                                 lds + S::WBUF * S::W_TAP + 4 * ROWS * RB, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -616,12 +628,18 @@ static int launch_mfma(const void *f, const void *w, const float *b, const int32
 }
 
 bool window_supported(int cin, int cout, int dtype);
+bool big_supported(int cin, int cout, int dtype);
+int launch_big(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb, void *out,
+               int cin, int cout, int dtype, int flip, hipStream_t s);
 int launch_window(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb,
                   void *out, int cin, int cout, int dtype, int flip, hipStream_t s);
 
 int choose_forward_kernel(int cin, int cout, int dtype)
 {
     if (window_supported(cin, cout, dtype)) return SUBMCONV_KERNEL_WINDOW;
+    // the persistent kernel wins at 128 channels; at 64 the row-gathered kernel is
+    // faster (gathering 128-byte rows into registers is the persistent kernel's limit)
+    if (big_supported(cin, cout, dtype) && cin == 128) return SUBMCONV_KERNEL_PERSISTENT;
     if (mfma_size(cin) && mfma_size(cout)) return SUBMCONV_KERNEL_MFMA;
     if (pow2_le32(cin) && pow2_le32(cout)) return SUBMCONV_KERNEL_LOWC;
     (void)dtype;
@@ -648,6 +666,8 @@ int launch_forward(const void *feats, const void *w, const float *bias, const su
         return launch_mfma(feats, w, bias, nbr, perm, out, n, cin, cout, dtype, flip, s);
     case SUBMCONV_KERNEL_WINDOW:
         return launch_window(feats, w, bias, rb, out, cin, cout, dtype, flip, s);
+    case SUBMCONV_KERNEL_PERSISTENT:
+        return launch_big(feats, w, bias, rb, out, cin, cout, dtype, flip, s);
     }
     return fail(SUBMCONV_E_INVALID_ARG, "unknown forward kernel variant %d", variant);
 }

@@ -178,7 +178,7 @@ def test_map_deterministic():
 # ---------------------------------------------------------------- forward
 
 KERNELS = {"generic": sc.KERNEL_GENERIC, "lowc": sc.KERNEL_LOWC, "mfma": sc.KERNEL_MFMA,
-           "window": sc.KERNEL_WINDOW}
+           "window": sc.KERNEL_WINDOW, "persistent": sc.KERNEL_PERSISTENT}
 
 
 def run_forward(c, res, batch, cin, cout, dtype, kernel, flip, seed=0, bias="uniform", std=None):
@@ -198,8 +198,11 @@ def run_forward(c, res, batch, cin, cout, dtype, kernel, flip, seed=0, bias="uni
 @pytest.mark.parametrize("kernel,cin,cout", [("generic", 16, 16), ("generic", 3, 5), ("generic", 24, 40),
                                              ("lowc", 16, 16), ("lowc", 8, 32), ("lowc", 32, 16), ("lowc", 32, 32),
                                              ("mfma", 32, 32), ("mfma", 64, 64), ("mfma", 128, 128),
-                                             ("mfma", 32, 128), ("mfma", 128, 64)])
+                                             ("mfma", 32, 128), ("mfma", 128, 64),
+                                             ("persistent", 64, 64), ("persistent", 128, 128)])
 def test_forward_random_set(dtype, flip, kernel, cin, cout):
+    if kernel == "persistent" and dtype == "f32":
+        pytest.skip("the persistent kernel takes bf16 only")
     c = synth.random_coords(3001, 14, 2, 5)      # ragged: not a multiple of any tile
     got, expect = run_forward(c, 14, 2, cin, cout, dtype, kernel, flip)
     assert_close(got, expect, dtype, "%s %d->%d %s flip=%d" % (kernel, cin, cout, dtype, flip))
@@ -244,6 +247,24 @@ def test_forward_window_sets(case, flip):
     assert_close(got, expect, "bf16", "window %s flip=%d" % (case, flip))
 
 
+# the persistent kernel: units of 512 (128 ch) or 1024 (64 ch) sorted voxels per block
+@pytest.mark.parametrize("c", [64, 128])
+@pytest.mark.parametrize("case", ["one", "unit_plus_one", "shell", "batches"])
+def test_forward_persistent_sets(c, case):
+    if case == "one":
+        coords, res, batch = np.array([[0, 2, 3, 4]], np.int32), 8, 1
+    elif case == "unit_plus_one":   # a ragged last unit
+        coords, res, batch = _cube(11)[: (512 if c == 128 else 1024) + 1], 11, 1
+    elif case == "shell":
+        w, coords = synth.workload(3)
+        coords, res, batch = coords[:20001], w.res, w.batch
+    else:
+        coords, res, batch = _cube(9, 3), 9, 3
+    for flip in (0, 1):
+        got, expect = run_forward(coords, res, batch, c, c, "bf16", "persistent", flip, seed=6)
+        assert_close(got, expect, "bf16", "persistent %d %s flip=%d" % (c, case, flip))
+
+
 def test_forward_window_shuffled_and_f32_rejected():
     w, c = synth.workload(2)
     p = synth.shuffle_rows(len(c), 5)
@@ -258,10 +279,11 @@ def test_forward_window_shuffled_and_f32_rejected():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("kernel,c", [("generic", 8), ("lowc", 16), ("mfma", 32), ("mfma", 128), ("window", 32)])
+@pytest.mark.parametrize("kernel,c", [("generic", 8), ("lowc", 16), ("mfma", 32), ("mfma", 128), ("window", 32),
+                                      ("persistent", 64), ("persistent", 128)])
 def test_forward_identity_kernel_exact(dtype, kernel, c):
-    if kernel == "window" and dtype == "f32":
-        pytest.skip("the windowed kernel takes bf16 only")
+    if kernel in ("window", "persistent") and dtype == "f32":
+        pytest.skip("this kernel takes bf16 only")
     _, coords = synth.workload(2)
     feats = np.random.default_rng(3).standard_normal((len(coords), c)).astype(np.float32)
     weight = np.zeros((c, 3, 3, 3, c), np.float32)
@@ -284,6 +306,8 @@ def test_forward_workloads_full(idx, dtype):
 def _auto_kernel(cin, cout, dtype="f32"):
     if cin == 32 and cout == 32 and dtype == "bf16":
         return "window"
+    if dtype == "bf16" and (cin, cout) == (128, 128):
+        return "persistent"
     if cin in (32, 64, 128) and cout in (32, 64, 128):
         return "mfma"
     return "lowc" if cin <= 32 and cout <= 32 else "generic"
