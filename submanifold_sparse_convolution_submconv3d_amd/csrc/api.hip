@@ -14,7 +14,6 @@ int launch_forward(const void *feats, const void *w, const float *bias,
                    int variant, hipStream_t s);
 int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s);
 int64_t win_plan_ints(int64_t n);
-int win_plan_build(submconv_rulebook *rb, hipStream_t s);
 int choose_forward_kernel(int cin, int cout, int dtype);
 int subdivide(const int32_t *coords, const void *feats, int64_t n, int c, int dtype,
               int32_t *out_coords, void *out_feats, hipStream_t s);
@@ -160,7 +159,6 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     r->plan = (int32_t *)((char *)r->block + kbytes + pbytes + nbytes + mbytes);
     if (n > 0) {
         st = build_map(coords, r, s);
-        if (st == SUBMCONV_OK) st = win_plan_build(r, s);
         if (st != SUBMCONV_OK) {
             dev_free(r->block, s);
             delete r;

@@ -87,10 +87,14 @@ int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int
 // Exclusive scan of n uint32 values (in place allowed), or of the set-bit counts of
 // n 32-bit / 64-bit words; writes the total to *total_dev if non-null.  `scratch`
 // must hold scan_scratch_bytes(n) bytes.
+// With add_back false the last pass is skipped: out[i] is then the prefix within
+// i's tile of SCAN_TILE_ITEMS, and the caller adds the tile's offset, which the
+// scan leaves in ((uint32_t *)scratch)[i / SCAN_TILE_ITEMS].
 enum { SCAN_VALUES = 0, SCAN_POPC32 = 1, SCAN_POPC64 = 2 };
+constexpr int SCAN_TILE_ITEMS = 2048;
 size_t scan_scratch_bytes(int64_t n);
 int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *total_dev,
-                       void *scratch, hipStream_t stream, int input_mode = SCAN_VALUES);
+                       void *scratch, hipStream_t stream, int input_mode = SCAN_VALUES, bool add_back = true);
 
 // --------------------------------------------------------------------------
 // bf16 helpers (bf16 values travel as uint16_t bit patterns)

@@ -59,12 +59,23 @@ constexpr int WIN_SLOTS = 1024;  // row slots per buffer; the last one always ho
 constexpr int WIN_CAP = WIN_SLOTS - 1;
 
 // One thread per tile: union of its groups' row windows, sorted and merged.
-// Straight-line code with compile-time indices (registers only).
-__global__ __launch_bounds__(256) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
-                                                  int64_t ntiles, int gpt, int cap,
-                                                  int32_t *__restrict__ plan)
+// Straight-line code with compile-time indices (registers only).  When blk_taps
+// is given, the kernel also sums those per-block present counts into st->taps
+// (one device-scope atomic per block of this kernel).
+__global__ __launch_bounds__(64) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
+                                                 int64_t ntiles, int gpt, int cap,
+                                                 int32_t *__restrict__ plan,
+                                                 const uint32_t *__restrict__ blk_taps, int64_t nblk,
+                                                 DevStatus *st)
 {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (blk_taps) {
+        unsigned long long taps = 0;
+        for (int64_t b = t; b < nblk; b += (int64_t)gridDim.x * 64) taps += blk_taps[b];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) taps += __shfl_xor(taps, off, 64);
+        if (threadIdx.x == 0 && taps) atomicAdd(&st->taps, taps);
+    }
     if (t >= ntiles) return;
     int32_t lo[9], hi[9], row[9];
 #pragma unroll
@@ -493,12 +504,14 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
 // Staging plan of a rulebook (part of the map build): PLAN_INTS per tile.
 int64_t win_plan_ints(int64_t n) { return (n + WIN_TILE - 1) / WIN_TILE * PLAN_INTS; }
 
-int win_plan_build(submconv_rulebook *rb, hipStream_t s)
+int win_plan_build(submconv_rulebook *rb, const uint32_t *blk_taps, int64_t nblk, DevStatus *st, hipStream_t s)
 {
     const int64_t ntiles = (rb->n + WIN_TILE - 1) / WIN_TILE;
     if (ntiles == 0) return SUBMCONV_OK;
-    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, s, rb->gwin,
-                       rb->ngroups, ntiles, WIN_TILE / 32, WIN_CAP, rb->plan);
+    // one thread per tile, small blocks: the work is a short serial merge per tile,
+    // so spreading the tiles over every CU is what matters
+    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + 63) / 64)), dim3(64), 0, s, rb->gwin,
+                       rb->ngroups, ntiles, WIN_TILE / 32, WIN_CAP, rb->plan, blk_taps, nblk, st);
     SC_LAUNCHED("win_plan");
     return SUBMCONV_OK;
 }

@@ -117,25 +117,6 @@ __device__ __forceinline__ void group_windows_write(const int32_t (&p)[27], bool
     }
 }
 
-// Present-entry counts: one per block of 256 voxels, summed here per 256
-// blocks and added to st->taps once per block (thousands of blocks adding to
-// one address would serialise at the memory side).
-__global__ __launch_bounds__(256) void k_taps_sum(const uint32_t *__restrict__ counts, int64_t nblk,
-                                                  DevStatus *st)
-{
-    __shared__ unsigned long long s_sum[4];
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    unsigned long long taps = t < nblk ? counts[t] : 0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) taps += __shfl_xor(taps, off, 64);
-    if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = taps;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned long long sum = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
-        if (sum) atomicAdd(&st->taps, sum);
-    }
-}
-
 // Table rows of one block from LDS to global (a contiguous run) and the block's
 // present count.  Called by every thread after its row of s_rows is written and
 // its count is added to *s_taps.
@@ -151,65 +132,56 @@ __device__ __forceinline__ void block_finish(const int32_t *s_rows, int count, i
 // dense key space: occupancy bitmap + rank
 // ---------------------------------------------------------------------------
 
-constexpr int MARK_ROWS = 1;  // rows per thread in k_mark
+constexpr int MARK_ROWS = 4;        // rows per thread in k_mark
+constexpr int MARK_SLOTS = 2048;    // LDS hash slots per block (2 x the block's rows)
+constexpr unsigned long long MARK_EMPTY = ~0ull;
 
+// Validate and pack each row's key, and set its bit in the occupancy bitmap.  A
+// block first ORs its rows' bits into an LDS hash table keyed by bitmap word, so
+// each distinct word costs one device-scope atomic per block instead of one per
+// row (device-scope atomics execute at the memory side on this chip).  Ordered
+// inputs touch few words per block.
 template <typename K>
 __global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, int64_t n, int res,
                                               int batch, int rb, K *__restrict__ keys,
                                               unsigned long long *__restrict__ bm, DevStatus *st)
 {
-    const unsigned lane = threadIdx.x & 63;
+    __shared__ unsigned long long s_word[MARK_SLOTS], s_bits[MARK_SLOTS];
+    for (int i = threadIdx.x; i < MARK_SLOTS; i += 256) {
+        s_word[i] = MARK_EMPTY;
+        s_bits[i] = 0ull;
+    }
+    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * (256 * MARK_ROWS) + threadIdx.x;
-    uint64_t word[MARK_ROWS];
-    unsigned long long bit[MARK_ROWS];
-    bool live[MARK_ROWS];
     bool bad_any = false;
 #pragma unroll
     for (int q = 0; q < MARK_ROWS; ++q) {
         const int64_t i = base + q * 256;  // consecutive threads read consecutive rows
-        live[q] = false;
+        if (i >= n) continue;
+        const int4 c = coords[i];
+        const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
+                         (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
+        bad_any |= bad;
         K key = (K)~K(0);  // marks an invalid row for the rank pass
-        if (i < n) {
-            const int4 c = coords[i];
-            const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
-                             (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
-            bad_any |= bad;
-            if (!bad) {
-                key = pack_key<K>(c.x, c.y, c.z, c.w, rb);
-                live[q] = true;
+        if (!bad) {
+            key = pack_key<K>(c.x, c.y, c.z, c.w, rb);
+            const unsigned long long w = (unsigned long long)(key >> 6);
+            uint32_t h = ((uint32_t)w * 0x9E3779B1u) >> (32 - 11);
+            // linear probing; the table has twice the block's rows, so it never fills
+            for (;;) {
+                const unsigned long long prev = atomicCAS(&s_word[h], MARK_EMPTY, w);
+                if (prev == MARK_EMPTY || prev == w) break;
+                h = (h + 1) & (MARK_SLOTS - 1);
             }
-            keys[i] = key;
+            atomicOr(&s_bits[h], 1ull << (uint32_t)(key & 63));
         }
-        word[q] = (uint64_t)(key >> 6);
-        bit[q] = 1ull << (uint32_t)(key & 63);
+        keys[i] = key;
     }
     if (bad_any) atomicOr(&st->flags, FLAG_RANGE);
-    // The wave's 256 rows are grouped by bitmap word (one ballot round per distinct
-    // word, led by the lowest lane that still holds an unwritten row) and each
-    // word gets one no-return atomic: ordered inputs touch only a few words.
-    for (;;) {
-        int have = -1;
-#pragma unroll
-        for (int q = MARK_ROWS - 1; q >= 0; --q)
-            if (live[q]) have = q;
-        const uint64_t pending = __ballot(have >= 0);
-        if (!pending) break;
-        const int leader = __ffsll((long long)pending) - 1;
-        uint64_t mine_w = 0;
-#pragma unroll
-        for (int q = 0; q < MARK_ROWS; ++q)
-            if (q == have) mine_w = word[q];
-        const uint64_t lw = __shfl(mine_w, leader, 64);
-        unsigned long long acc = 0ull;
-#pragma unroll
-        for (int q = 0; q < MARK_ROWS; ++q)
-            if (live[q] && word[q] == lw) {
-                acc |= bit[q];
-                live[q] = false;
-            }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc |= __shfl_xor(acc, off, 64);
-        if ((int)lane == leader) atomicOr(&bm[lw], acc);
+    __syncthreads();
+    for (int i = threadIdx.x; i < MARK_SLOTS; i += 256) {
+        const unsigned long long w = s_word[i];
+        if (w != MARK_EMPTY) atomicOr(&bm[w], s_bits[i]);
     }
 }
 
@@ -217,6 +189,7 @@ template <typename K>
 __global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys, int64_t n,
                                               const unsigned long long *__restrict__ bm,
                                               const uint32_t *__restrict__ prefix,
+                                              const uint32_t *__restrict__ tsum,
                                               K *__restrict__ sk, int32_t *__restrict__ perm)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -224,35 +197,20 @@ __global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys, int64_
     const K key = keys[i];
     if (key == (K)~K(0)) return;  // out-of-range row (the build reports it)
     const unsigned long long word = bm[key >> 6];
-    const int64_t r = (int64_t)prefix[key >> 6] + __popcll(word & ((1ull << (uint32_t)(key & 63)) - 1ull));
+    const uint64_t w = (uint64_t)(key >> 6);
+    const int64_t r = (int64_t)prefix[w] + tsum[w / SCAN_TILE_ITEMS] +
+                      __popcll(word & ((1ull << (uint32_t)(key & 63)) - 1ull));
     if (r < n) {
         sk[r] = key;
         perm[r] = (int32_t)i;
     }
 }
 
-// Occupancy bits of cells c, c+1, c+2 (bit 0 = c) from the 64-bit bitmap words.
-__device__ __forceinline__ uint32_t three_bits(const unsigned long long *bm, uint64_t c)
-{
-    const uint64_t w = c >> 6;
-    const uint32_t b = (uint32_t)(c & 63);
-    unsigned long long v = bm[w] >> b;
-    if (b > 61) v |= bm[w + 1] << (64 - b);  // cells c+1 / c+2 spill into the next word
-    return (uint32_t)(v & 7ull);
-}
-
-// Number of keys below cell c (its sorted position if present).
-__device__ __forceinline__ int64_t rank_below(const unsigned long long *bm, const uint32_t *prefix, uint64_t c)
-{
-    const uint64_t w = c >> 6;
-    const uint32_t b = (uint32_t)(c & 63);
-    return (int64_t)prefix[w] + __popcll(bm[w] & ((1ull << b) - 1ull));
-}
-
 template <typename K>
 __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, int64_t n, int res, int rb,
                                                     int batch, const unsigned long long *__restrict__ bm,
                                                     const uint32_t *__restrict__ prefix,
+                                                    const uint32_t *__restrict__ tsum,
                                                     int32_t *__restrict__ nbr_sp,
                                                     int32_t *__restrict__ gwin,
                                                     uint32_t *__restrict__ blk_taps)
@@ -303,7 +261,7 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
         for (int d = 0; d < 9; ++d) {
             lo_w[d] = bm[wd[d]];
             hi_w[d] = bm[wd[d] + 1];  // the bitmap has one word of padding
-            pre[d] = prefix[wd[d]];
+            pre[d] = prefix[wd[d]] + tsum[wd[d] / SCAN_TILE_ITEMS];
         }
 #pragma unroll
         for (int d = 0; d < 9; ++d) {
@@ -665,6 +623,16 @@ int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s)
 
 // Bitmap bytes are affordable when they stay within a small multiple of the
 // per-voxel data (a 512^3 grid of 3M voxels: 16 MB).
+int win_plan_build(submconv_rulebook *rb, const uint32_t *blk_taps, int64_t nblk, DevStatus *st,
+                   hipStream_t s);  // conv_win.hip
+
+// Zero the status block and `words` 64-bit words (the bitmap); grid-stride.
+__global__ __launch_bounds__(256) void k_clear(DevStatus *st, unsigned long long *__restrict__ w, int64_t words)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0) *st = DevStatus{};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) w[i] = 0ull;
+}
+
 static bool use_bitmap(int64_t n, int nbits)
 {
     if (nbits > 31) return false;
@@ -703,7 +671,10 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     int status = SUBMCONV_OK;
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
-        if (hipMemsetAsync(st, 0, sizeof(DevStatus), stream) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
+        // one launch clears the status block and (dense path) the bitmap
+        const int64_t clear_words = path == 2 ? words + 1 : 0;
+        hipLaunchKernelGGL(k_clear, dim3((unsigned)(clear_words > 0 ? (clear_words + 2047) / 2048 : 1)), dim3(256), 0,
+                           stream, st, (unsigned long long *)(scratch + o_bm), clear_words);
         if (path == 0 || path == 1) {
             if (path == 0)
                 hipLaunchKernelGGL(k_build_small_bm<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
@@ -716,16 +687,17 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
             K *tmp = (K *)(scratch + o_keys);
             unsigned long long *bm = (unsigned long long *)(scratch + o_bm);
             uint32_t *pre = (uint32_t *)(scratch + o_pre);
-            if (hipMemsetAsync(bm, 0, (size_t)(words + 1) * 8, stream) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "bitmap clear failed"); break; }
             hipLaunchKernelGGL(k_mark<K>, dim3((unsigned)((n + 256 * MARK_ROWS - 1) / (256 * MARK_ROWS))), dim3(256),
                                0, stream, (const int4 *)coords, n, rb->res, rb->batch, rb->rb, tmp, bm, st);
-            // the total number of set bits lands in st->count: below n means a duplicate
+            // the total number of set bits lands in st->count: below n means a duplicate.  The
+            // scan leaves per-tile prefixes; rank and resolve add the tile offsets (tsum).
             if ((status = exclusive_scan_u32((const uint32_t *)bm, pre, words, (uint32_t *)&st->count,
-                                             scratch + o_aux, stream, SCAN_POPC64)) != SUBMCONV_OK) break;
-            hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n, bm, pre,
+                                             scratch + o_aux, stream, SCAN_POPC64, false)) != SUBMCONV_OK) break;
+            const uint32_t *tsum = (const uint32_t *)(scratch + o_aux);
+            hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n, bm, pre, tsum,
                                (K *)rb->keys, rb->perm);
             hipLaunchKernelGGL(k_resolve_bm<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
-                               rb->res, rb->rb, rb->batch, bm, pre, rb->nbr_sp, rb->gwin, blk_taps);
+                               rb->res, rb->rb, rb->batch, bm, pre, tsum, rb->nbr_sp, rb->gwin, blk_taps);
         } else {
             K *keys_b = (K *)(scratch + o_keys);
             int32_t *vals_b = (int32_t *)(scratch + o_vals);
@@ -738,10 +710,10 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
             hipLaunchKernelGGL(k_resolve_win<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
                                rb->res, rb->rb, rb->nbr_sp, rb->gwin, blk_taps, st);
         }
-        if (path >= 2)
-            hipLaunchKernelGGL(k_taps_sum, dim3((unsigned)((grid + 255) / 256)), dim3(256), 0, stream,
-                               blk_taps, (int64_t)grid, st);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "kernel launch in build_map failed"); break; }
+        // The staging plan is queued before the status read so it runs under the host
+        // round trip; it also sums the per-block tap counts of the large-set paths.
+        if ((status = win_plan_build(rb, path >= 2 ? blk_taps : nullptr, (int64_t)grid, st, stream)) != SUBMCONV_OK) break;
         DevStatus h;
         if ((status = read_status(st, &h, stream)) != SUBMCONV_OK) break;
         if (path == 2 && !(h.flags & FLAG_RANGE) && (int64_t)(uint32_t)h.count != n) h.flags |= FLAG_DUPLICATE;

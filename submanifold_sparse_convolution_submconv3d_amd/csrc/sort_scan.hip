@@ -202,6 +202,7 @@ template int radix_sort_pairs<uint64_t>(uint64_t *, int32_t *, uint64_t *, int32
 
 constexpr int SCAN_ITEMS = 8;
 constexpr int SCAN_TILE = 256 * SCAN_ITEMS;
+static_assert(SCAN_TILE == SCAN_TILE_ITEMS, "tile size exported in common.h");
 
 size_t scan_scratch_bytes(int64_t n)
 {
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256) void k_scan_add(uint32_t *__restrict__ out, in
 }
 
 int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *total_dev,
-                       void *scratch, hipStream_t stream, int input_mode)
+                       void *scratch, hipStream_t stream, int input_mode, bool add_back)
 {
     if (n <= 0) {
         if (total_dev) SC_HIP(hipMemsetAsync(total_dev, 0, sizeof(uint32_t), stream));
@@ -288,7 +289,7 @@ int exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *t
     SC_LAUNCHED("scan_tiles");
     hipLaunchKernelGGL(k_scan_sums, dim3(1), dim3(256), 0, stream, sums, tiles, total_dev);
     SC_LAUNCHED("scan_sums");
-    if (tiles > 1) {
+    if (tiles > 1 && add_back) {
         hipLaunchKernelGGL(k_scan_add, dim3((unsigned)tiles), dim3(256), 0, stream, out, n, sums);
         SC_LAUNCHED("scan_add");
     }
