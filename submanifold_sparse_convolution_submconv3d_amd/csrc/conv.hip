@@ -576,11 +576,10 @@ static int launch_lowc(const void *f, const void *w, const float *b, const int32
     return fail(SUBMCONV_E_UNSUPPORTED, "lowc kernel: Cin must be a power of two <= 32");
 }
 
-template <typename T, int CIN, int COUT>
-static int launch_mfma_tt(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
-                          int64_t n, int flip, hipStream_t s)
+template <typename T, int CIN, int COUT, int VT>
+static void launch_mfma_vt(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm,
+                           void *o, int64_t n, int flip, hipStream_t s)
 {
-    constexpr int VT = (sizeof(T) == 4 && (CIN >= 128 || COUT >= 128)) ? 1 : 2;
     if constexpr (RowShape<T, CIN, COUT, VT>::LDS <= 160 * 1024) {
         constexpr int per_block = RowShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
         const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
@@ -592,6 +591,20 @@ static int launch_mfma_tt(const void *f, const void *w, const float *b, const in
         hipLaunchKernelGGL((k_conv_mfma<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
                            (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     }
+}
+
+template <typename T, int CIN, int COUT>
+static int launch_mfma_tt(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
+                          int64_t n, int flip, hipStream_t s)
+{
+    // Two 32-voxel columns per wave share each weight fragment, except at fp32 with
+    // 128 channels (registers) and on small sets, where 64 voxels per wave would
+    // leave most CUs without a block (256 voxels per block; 2 blocks per CU wanted).
+    constexpr bool one = sizeof(T) == 4 && (CIN >= 128 || COUT >= 128);
+    if (one || n < (int64_t)256 * 2 * 256)
+        launch_mfma_vt<T, CIN, COUT, 1>(f, w, b, nbr, perm, o, n, flip, s);
+    else
+        launch_mfma_vt<T, CIN, COUT, (one ? 1 : 2)>(f, w, b, nbr, perm, o, n, flip, s);
     SC_LAUNCHED("conv_mfma");
     return SUBMCONV_OK;
 }
