@@ -4,24 +4,31 @@
 // summary): out[i, o] = bias[o] + sum_k sum_c W[o, k', c] * feats[nbr[i, k], c],
 // k' = k or 26 - k (mirrored kernel), weights KRSC [Cout, 27, Cin].
 //
-// Implicit GEMM, transposed (out^T = W_k . F_k^T) on v_mfma_f32_32x32x16_bf16:
-// the A operand is a 32-output-channel x 16-input-channel weight fragment, the
-// B operand 16 input channels x 32 voxels of gathered neighbour rows.
+// Implicit GEMM, transposed (out^T = W_k . F_k^T) on v_mfma_f32_16x16x32_bf16:
+// the A operand is a 16-output-channel x 32-input-channel weight fragment, the
+// B operand 32 input channels x 16 voxels of gathered neighbour rows.  With 16
+// voxels per operand, four lanes read 64 contiguous bytes of each row, so a
+// gather instruction touches half as many cache lines as with 32-voxel operands.
 //
-// One block per CU, 8 waves (two per SIMD), looping over units of sorted voxels
-// (XCD-contiguous runs).  Per unit, each wave owns VT columns of 32 voxels x all
-// Cout in AGPR accumulators and walks the 27 taps:
-//   * weight tap k+1 is copied into the other of two LDS buffers (direct loads)
-//     while tap k computes; the two buffers are two objects so the compiler
-//     does not make tap k's reads wait for that copy;
-//   * the B fragments are loaded straight from global memory into registers; a
-//     fragment is reloaded with tap k+1's data as soon as tap k's MFMAs have
-//     consumed it, so one register set serves as both operand and prefetch;
-//   * neighbour rows are resolved two taps ahead (table entry, then perm).
-// Every load is issued unconditionally (a missing neighbour reads a zero row),
-// so the number of loads a wave issues after a weight copy is fixed; each tap
-// ends by waiting until that copy has landed (vmcnt) and an LDS-only barrier,
-// leaving the next tap's operand loads in flight.
+// One block per CU, 8 waves (two per SIMD).  Each block owns a contiguous run of
+// 16-voxel columns (runs are split per XCD first) and walks it in rounds.  In a
+// full round each wave owns CWF columns x all Cout in accumulators; the last,
+// partial round splits the output tiles among the waves instead, so that a
+// block's work is within a quarter column of its share.  Per round the 27 taps
+// are walked with:
+//   * weight tap k+1 copied into the other of two LDS buffers (direct loads) while
+//     tap k computes; each copy reads whole rows, stored with a 16-byte-chunk XOR
+//     swizzle so that operand reads spread over the banks; the two buffers are two
+//     objects, so the compiler does not make tap k's reads wait for that copy;
+//   * the round's block of the neighbour table in LDS, copied during the previous
+//     round's last taps;
+//   * B fragments loaded straight from global memory into registers, each
+//     reloaded with tap k+1's data as soon as tap k's MFMAs have consumed it;
+//   * neighbour rows resolved two taps ahead (table entry from LDS, then perm).
+// Every global load is issued unconditionally (a missing neighbour reads a zero
+// row, an out-of-range copy re-reads an in-range chunk), so the number of loads a
+// wave issues after a weight copy is fixed; each tap ends by waiting until that
+// copy has landed (vmcnt) and an LDS-only barrier.
 #include <type_traits>
 
 #include "common.h"
@@ -29,7 +36,7 @@
 namespace sc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -39,15 +46,31 @@ __device__ uint4 g_big_zero[16] = {};  // a zero feature row (up to 128 bf16 cha
 
 template <int CIN, int COUT>
 struct BigShape {
-    static constexpr int G = CIN / 16;             // K slices of 16 input channels
-    static constexpr int RT = COUT / 32;           // output row tiles of 32 channels
-    static constexpr int VT = 4 / RT > 0 ? 4 / RT : 1;  // 32-voxel columns per wave
-    static constexpr int NFRAG = RT * G;           // weight fragments per tap (1 KB each)
+    static constexpr int G = CIN / 32;          // K slices of 32 input channels per tap
+    static constexpr int RT = COUT / 16;        // output tiles of 16 channels
+    static constexpr int CWF = 16 / RT;         // 16-voxel columns per wave in a full round
+    static constexpr int LOG_CWF = CWF >= 4 ? 2 : (CWF >= 2 ? 1 : 0);
     static constexpr int WAVES = 8;
-    static constexpr int UNIT = WAVES * VT * 32;   // voxels per unit
-    static constexpr int WCOPY = NFRAG / WAVES;    // weight copies per wave per tap
-    static_assert(NFRAG % WAVES == 0, "weight copies split evenly over the waves");
-    static_assert(VT * G <= 8 && RT * VT <= 4, "register budget: 32 B-operand VGPRs, 64 accumulators");
+    static constexpr int ROUND = WAVES * CWF;   // columns of a full round
+    static constexpr int ROWCH = CIN / 8;       // 16-byte chunks per weight row
+    static constexpr int WCH = COUT * ROWCH;    // chunks per weight tap
+    static constexpr int WCOPY = WCH / (64 * WAVES);
+    static constexpr int TCH = ROUND * 16 * 27 / 4;  // table chunks of a full round
+    static constexpr int TCOPY = (TCH + 64 * WAVES - 1) / (64 * WAVES);
+    static_assert(CIN % 32 == 0 && COUT % 16 == 0 && 16 % RT == 0, "tile shape");
+    static_assert(WCH % (64 * WAVES) == 0, "weight copies split evenly over the waves");
+    static_assert(CWF * RT <= 16 && CWF * G <= 8, "register budget: 64 accumulators, 32 B-operand VGPRs");
+};
+
+// Work split of one round: each wave takes CW columns x RW output tiles; PARTS
+// waves share a column group; CAP columns fit in one round.
+template <class S, int M>
+struct BigMode {
+    static constexpr int CW = (S::CWF >> M) > 0 ? (S::CWF >> M) : 1;
+    static constexpr int RW = M > S::LOG_CWF ? (S::RT >> (M - S::LOG_CWF)) : S::RT;
+    static constexpr int PARTS = S::RT / RW;
+    static constexpr int CAP = S::WAVES / PARTS * CW;
+    static_assert(RW >= 1 && S::WAVES % PARTS == 0, "mode shape");
 };
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding)
@@ -71,95 +94,105 @@ __device__ __forceinline__ void big_unroll(F &&f)
 __device__ __forceinline__ void big_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int CIN, int COUT>
-__global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict__ feats,
-                                                     const uint16_t *__restrict__ w,
-                                                     const float *__restrict__ bias,
-                                                     const int32_t *__restrict__ nbr_sp,
-                                                     const int32_t *__restrict__ perm,
-                                                     uint16_t *__restrict__ out, int64_t n,
-                                                     int64_t nunits, int flip)
-{
+struct BigCtx {
     using S = BigShape<CIN, COUT>;
-    constexpr int G = S::G, RT = S::RT, VT = S::VT, NFRAG = S::NFRAG;
-    __shared__ uint4 sW0[NFRAG * 64];
-    __shared__ uint4 sW1[NFRAG * 64];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = lane >> 5, l32 = lane & 31;
+    const uint16_t *feats;
+    const uint16_t *w;
+    const float *bias;
+    const int32_t *nbr_sp;
+    const int32_t *perm;
+    uint16_t *out;
+    int64_t n;
+    int flip;
+    uint4 *sW0, *sW1, *sT;
+    int wave, lane, s16, h;
+    int32_t wofs[S::WCOPY];  // per-lane part of each weight copy's source offset
+    int32_t aoff[S::G];      // per-lane chunk offset of each K slice's A fragment
+    int64_t tlast;           // last 16-byte chunk that starts inside the table
 
-    // units of this block: the XCD's contiguous run, dealt round-robin to its blocks
-    const int xcd = blockIdx.x & 7, bpx = gridDim.x >> 3, jb = blockIdx.x >> 3;
-    const int64_t u_begin = nunits * xcd / 8, u_end = nunits * (xcd + 1) / 8;
-
-    // weight tap k -> LDS: fragment f = r G + g, lane l holds W[32 r + l%32][k'][16 g + 8 (l/32) .. +7].
-    // The per-lane part of each copy's source offset is formed once; the tap part is
-    // made opaque at each use, or the compiler hoists the offsets of all 27 taps and
-    // holds them in registers for the whole kernel.
-    int32_t wofs[S::WCOPY];
-#pragma unroll
-    for (int c = 0; c < S::WCOPY; ++c) {
-        const int f = wave + S::WAVES * c;
-        const int r = f / G, g = f - r * G;
-        wofs[c] = (32 * r + l32) * 27 * CIN + 16 * g + 8 * half;
-    }
-    auto stage_w = [&](int k, uint4 *buf) {
+    // weight tap k -> buf (row-major, chunk j of row o at o * ROWCH + (j ^ (o % ROWCH)))
+    __device__ __forceinline__ void stage_w(int k, uint4 *buf) const
+    {
         int32_t kofs = (flip ? 26 - k : k) * CIN;
-        asm volatile("" : "+s"(kofs));
+        asm volatile("" : "+s"(kofs));  // keeps the 27 taps' offsets from being hoisted into registers
 #pragma unroll
-        for (int c = 0; c < S::WCOPY; ++c) {
-            const int f = wave + S::WAVES * c;
-            __builtin_amdgcn_global_load_lds((gbl_void *)(w + (uint32_t)(wofs[c] + kofs)), (lds_void *)&buf[f * 64], 16, 0, 0);
+        for (int c = 0; c < S::WCOPY; ++c)
+            __builtin_amdgcn_global_load_lds((gbl_void *)(w + (uint32_t)(wofs[c] + kofs)),
+                                             (lds_void *)&buf[(wave + S::WAVES * c) * 64], 16, 0, 0);
+    }
+    // table rows of columns [col, col + ROUND) -> sT
+    __device__ __forceinline__ void stage_t(int64_t col) const
+    {
+        const int64_t base = col * 16 * 27 / 4;
+#pragma unroll
+        for (int c = 0; c < S::TCOPY; ++c) {
+            int64_t q = base + (wave + S::WAVES * c) * 64 + lane;
+            q = q < tlast ? q : tlast;
+            __builtin_amdgcn_global_load_lds((gbl_void *)(nbr_sp + 4 * q), (lds_void *)&sT[(wave + S::WAVES * c) * 64],
+                                             16, 0, 0);
         }
-    };
+    }
 
-    for (int64_t u = u_begin + jb; u < u_end; u += bpx) {
-        const int64_t vbase = (u * S::WAVES + wave) * (VT * 32);
-        int64_t vrow[VT];  // clamped voxel index of each column (always a valid address)
-        bool vok[VT];
+    template <int M>
+    __device__ __forceinline__ void round(int64_t col, int ncols, int64_t col_next) const
+    {
+        using D = BigMode<S, M>;
+        constexpr int CW = D::CW, RW = D::RW, G = S::G;
+        const int cg = wave / D::PARTS, r0 = (wave - cg * D::PARTS) * RW;
+        const int32_t *tbl = (const int32_t *)sT;
+
+        int vloc[CW];
+        int64_t vrow[CW];
+        bool vok[CW];
 #pragma unroll
-        for (int t = 0; t < VT; ++t) {
-            const int64_t v = vbase + 32 * t + l32;
-            vok[t] = v < n;
-            vrow[t] = vok[t] ? v : n - 1;
+        for (int c = 0; c < CW; ++c) {
+            const int colr = cg * CW + c;
+            vloc[c] = colr * 16 + s16;
+            const int64_t v = col * 16 + vloc[c];
+            vok[c] = colr < ncols && v < n;
+            vrow[c] = vok[c] ? v : 0;
         }
-        // table entry of tap k (sorted position or -1), row of a sorted position (or -1)
-        auto entry = [&](int k, int t) -> int32_t {
-            const int32_t e = nbr_sp[vrow[t] * 27 + k];
-            return vok[t] ? e : -1;
+        auto entry = [&](int k, int c) -> int32_t {
+            const int32_t e = tbl[vloc[c] * 27 + k];
+            return vok[c] ? e : -1;
         };
         auto row_of = [&](int32_t e) -> int32_t {
-            const int32_t r = perm[(uint32_t)e < (uint64_t)n ? e : 0];
-            return (uint32_t)e < (uint64_t)n ? r : -1;
+            const bool ok = (uint32_t)e < (uint64_t)n;
+            const int32_t r = perm[ok ? e : 0];
+            return ok ? r : -1;
         };
         auto fptr = [&](int32_t row, int g) -> const uint4 * {
-            return (uint32_t)row < (uint64_t)n ? (const uint4 *)(feats + (int64_t)row * CIN + 16 * g + 8 * half)
-                                               : &g_big_zero[2 * g + half];
+            return (uint32_t)row < (uint64_t)n ? (const uint4 *)(feats + (int64_t)row * CIN + 32 * g + 8 * h)
+                                               : &g_big_zero[4 * g + h];
         };
 
-        floatx16 acc[RT][VT];
+        floatx4 acc[RW][CW];
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RW; ++r)
 #pragma unroll
-            for (int t = 0; t < VT; ++t)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[r][t][q] = 0.f;
+            for (int c = 0; c < CW; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-        uint4 F[VT][G];
-        int32_t row1[VT], e2[VT];
-        // prologue: weights of tap 0, operands of tap 0, rows of tap 1, entries of tap 2
+        // prologue: the table block has landed (copied before this round)
+        wait_vmcnt<0>();
+        big_lds_barrier();
         stage_w(0, sW0);
+        int32_t orow[CW], row1[CW], e2[CW];
+        uint4 F[CW][G];
         {
-            int32_t row0[VT];
+            int32_t row0[CW];
 #pragma unroll
-            for (int t = 0; t < VT; ++t) row0[t] = row_of(entry(0, t));
+            for (int c = 0; c < CW; ++c) {
+                orow[c] = perm[vrow[c]];
+                row0[c] = row_of(entry(0, c));
+            }
 #pragma unroll
-            for (int t = 0; t < VT; ++t)
+            for (int c = 0; c < CW; ++c)
 #pragma unroll
-                for (int g = 0; g < G; ++g) F[t][g] = *fptr(row0[t], g);
+                for (int g = 0; g < G; ++g) F[c][g] = *fptr(row0[c], g);
 #pragma unroll
-            for (int t = 0; t < VT; ++t) {
-                row1[t] = row_of(entry(1, t));
-                e2[t] = entry(2, t);
+            for (int c = 0; c < CW; ++c) {
+                row1[c] = row_of(entry(1, c));
+                e2[c] = entry(2, c);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -167,62 +200,116 @@ __global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict_
 
         auto tap = [&](auto kc) {
             constexpr int k = decltype(kc)::value;
-            const uint4 *cur = (k & 1) ? sW1 : sW0;
+            const uint4 *cur = ((k & 1) ? sW1 : sW0) + r0 * 16 * S::ROWCH;
             uint4 *nxt = (k & 1) ? sW0 : sW1;
             if constexpr (k + 1 < 27) stage_w(k + 1, nxt);
-            __builtin_amdgcn_sched_barrier(0);  // everything below is issued after the weight copy
-            int32_t row2[VT];
+            if constexpr (k == 24) stage_t(col_next);  // every read of this round's table is done
+            __builtin_amdgcn_sched_barrier(0);         // everything below is issued after the copies
+            int32_t row2[CW];
 #pragma unroll
-            for (int t = 0; t < VT; ++t) {
-                if constexpr (k + 2 < 27) row2[t] = row_of(e2[t]);
-                if constexpr (k + 3 < 27) e2[t] = entry(k + 3, t);
+            for (int c = 0; c < CW; ++c) {
+                if constexpr (k + 2 < 27) row2[c] = row_of(e2[c]);
+                if constexpr (k + 3 < 27) e2[c] = entry(k + 3, c);
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
 #pragma unroll
-                for (int r = 0; r < RT; ++r) {
-                    const uint4 a = cur[(r * G + g) * 64 + lane];
+                for (int r = 0; r < RW; ++r) {
+                    const uint4 a = cur[r * 16 * S::ROWCH + aoff[g]];
 #pragma unroll
-                    for (int t = 0; t < VT; ++t)
-                        acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                            __builtin_bit_cast(bf16x8_t, F[t][g]),
-                                                                            acc[r][t], 0, 0, 0);
+                    for (int c = 0; c < CW; ++c)
+                        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                            __builtin_bit_cast(bf16x8_t, F[c][g]),
+                                                                            acc[r][c], 0, 0, 0);
                 }
                 if constexpr (k + 1 < 27) {
 #pragma unroll
-                    for (int t = 0; t < VT; ++t) F[t][g] = *fptr(row1[t], g);
+                    for (int c = 0; c < CW; ++c) F[c][g] = *fptr(row1[c], g);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // bound how far weight reads are hoisted (registers)
             }
 #pragma unroll
-            for (int t = 0; t < VT; ++t)
-                if constexpr (k + 2 < 27) row1[t] = row2[t];
+            for (int c = 0; c < CW; ++c)
+                if constexpr (k + 2 < 27) row1[c] = row2[c];
             // the weight copy of tap k+1 has landed once at most the loads issued after it are pending
-            constexpr int after = ((k + 2 < 27) ? VT : 0) + ((k + 3 < 27) ? VT : 0) + ((k + 1 < 27) ? VT * G : 0);
+            constexpr int after = ((k + 1 < 27) ? CW * G : 0) + ((k + 2 < 27) ? CW : 0) + (k == 24 ? S::TCOPY : 0);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<after>();
             big_lds_barrier();
         };
         big_unroll<0, 27>(tap);
 
-        // epilogue: lane holds output channels 32 r + 8 q + 4 half .. +3 of voxel column t
+        // epilogue: lane holds output channels 16 (r0 + r) + 4 h .. +3 of its voxel in column c
 #pragma unroll
-        for (int t = 0; t < VT; ++t) {
-            if (!vok[t]) continue;
-            const int64_t orow = perm[vrow[t]];
+        for (int c = 0; c < CW; ++c) {
+            if (!vok[c]) continue;
 #pragma unroll
-            for (int r = 0; r < RT; ++r)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int o = 32 * r + 8 * q + 4 * half;
-                    const float4 b = bias ? *(const float4 *)(bias + o) : make_float4(0.f, 0.f, 0.f, 0.f);
-                    const floatx2 lo = {acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y};
-                    const floatx2 hi = {acc[r][t][4 * q + 2] + b.z, acc[r][t][4 * q + 3] + b.w};
-                    *(uint2 *)(out + orow * COUT + o) =
-                        make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
-                                   __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
-                }
+            for (int r = 0; r < RW; ++r) {
+                const int o = 16 * (r0 + r) + 4 * h;
+                const float4 b = bias ? *(const float4 *)(bias + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const floatx2 lo = {acc[r][c][0] + b.x, acc[r][c][1] + b.y};
+                const floatx2 hi = {acc[r][c][2] + b.z, acc[r][c][3] + b.w};
+                *(uint2 *)(out + (int64_t)orow[c] * COUT + o) =
+                    make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
+            }
         }
+    }
+};
+
+template <int CIN, int COUT>
+__global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict__ feats,
+                                                     const uint16_t *__restrict__ w,
+                                                     const float *__restrict__ bias,
+                                                     const int32_t *__restrict__ nbr_sp,
+                                                     const int32_t *__restrict__ perm,
+                                                     uint16_t *__restrict__ out, int64_t n, int64_t ncols,
+                                                     int flip)
+{
+    using S = BigShape<CIN, COUT>;
+    __shared__ uint4 sW0[S::WCH];
+    __shared__ uint4 sW1[S::WCH];
+    __shared__ uint4 sT[S::TCOPY * 64 * S::WAVES];
+
+    // this block's columns: the XCD's contiguous share, split evenly among its blocks
+    const int xcd = blockIdx.x & 7, bpx = gridDim.x >> 3, jb = blockIdx.x >> 3;
+    const int64_t xs = ncols * xcd / 8, xe = ncols * (xcd + 1) / 8;
+    const int64_t cb = xs + (xe - xs) * jb / bpx, ce = xs + (xe - xs) * (jb + 1) / bpx;
+    if (cb >= ce) return;
+
+    BigCtx<CIN, COUT> x;
+    x.feats = feats; x.w = w; x.bias = bias; x.nbr_sp = nbr_sp; x.perm = perm; x.out = out;
+    x.n = n; x.flip = flip; x.sW0 = sW0; x.sW1 = sW1; x.sT = sT;
+    const int tid = threadIdx.x;
+    x.lane = tid & 63;
+    x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    x.s16 = x.lane & 15;
+    x.h = x.lane >> 4;
+#pragma unroll
+    for (int c = 0; c < S::WCOPY; ++c) {
+        const int q = (x.wave + S::WAVES * c) * 64 + x.lane;
+        const int o = q / S::ROWCH, p = q % S::ROWCH;
+        x.wofs[c] = o * 27 * CIN + 8 * (p ^ (o % S::ROWCH));
+    }
+    {
+        const int xr = x.h ^ (x.s16 % S::ROWCH);
+#pragma unroll
+        for (int g = 0; g < S::G; ++g) x.aoff[g] = x.s16 * S::ROWCH + ((4 * g) ^ xr);
+    }
+    x.tlast = (n * 27 + 3) / 4 - 1;
+
+    x.stage_t(cb);
+    for (int64_t col = cb; col < ce; col += S::ROUND) {
+        const int nc = (int)(ce - col < S::ROUND ? ce - col : S::ROUND);
+        const int64_t nxt = col + S::ROUND < ce ? col + S::ROUND : col;
+        if (nc > BigMode<S, 1>::CAP)
+            x.template round<0>(col, nc, nxt);
+        else if (nc > BigMode<S, 2>::CAP)
+            x.template round<1>(col, nc, nxt);
+        else if (nc > BigMode<S, 3>::CAP)
+            x.template round<2>(col, nc, nxt);
+        else
+            x.template round<3>(col, nc, nxt);
     }
 }
 
@@ -241,13 +328,13 @@ static int launch_big_t(const void *f, const void *w, const float *b, const subm
                         hipStream_t s)
 {
     using S = BigShape<CIN, COUT>;
-    const int64_t nunits = (rb->n + S::UNIT - 1) / S::UNIT;
+    const int64_t ncols = (rb->n + 15) / 16;
     int64_t blocks = big_device_cus(rb->device) & ~7;
     if (blocks < 8) blocks = 8;
-    if (blocks > ((nunits + 7) & ~int64_t(7))) blocks = (nunits + 7) & ~int64_t(7);
+    if (blocks > ((ncols + 7) & ~int64_t(7))) blocks = (ncols + 7) & ~int64_t(7);
     hipLaunchKernelGGL((k_conv_big<CIN, COUT>), dim3((unsigned)blocks), dim3(S::WAVES * 64), 0, s,
                        (const uint16_t *)f, (const uint16_t *)w, b, rb->nbr_sp, rb->perm, (uint16_t *)o, rb->n,
-                       nunits, flip);
+                       ncols, flip);
     SC_LAUNCHED("conv_big");
     return SUBMCONV_OK;
 }
