@@ -16,19 +16,19 @@
 // partial round splits the output tiles among the waves instead, so that a
 // block's work is within a quarter column of its share.  Per round the 27 taps
 // are walked with:
-//   * weight tap k+1 copied into the other of two LDS buffers (direct loads) while
-//     tap k computes; each copy reads whole rows, stored with a 16-byte-chunk XOR
-//     swizzle so that operand reads spread over the banks; the two buffers are two
-//     objects, so the compiler does not make tap k's reads wait for that copy;
-//   * the round's block of the neighbour table in LDS, copied during the previous
-//     round's last taps;
+//   * weight tap k+1 loaded into registers at the start of tap k and written into
+//     the other of two LDS buffers at its end.  Each wave reads whole rows; rows are
+//     stored with a 16-byte-chunk XOR swizzle so that operand reads spread over the
+//     banks.  These are ordinary loads, not direct-to-LDS copies: while such a copy
+//     is in flight the compiler stops counting loads in order and waits for all of
+//     them before any register operand is used;
+//   * the round's block of the neighbour table in LDS (a direct copy issued after
+//     the previous round's last tap, waited for before the first);
 //   * B fragments loaded straight from global memory into registers, each
 //     reloaded with tap k+1's data as soon as tap k's MFMAs have consumed it;
 //   * neighbour rows resolved two taps ahead (table entry from LDS, then perm).
-// Every global load is issued unconditionally (a missing neighbour reads a zero
-// row, an out-of-range copy re-reads an in-range chunk), so the number of loads a
-// wave issues after a weight copy is fixed; each tap ends by waiting until that
-// copy has landed (vmcnt) and an LDS-only barrier.
+// Features, perm and weights are read as bounds-checked buffers: a missing
+// neighbour is an offset past the end, which loads zeros.
 #include <type_traits>
 
 #include "common.h"
@@ -42,23 +42,29 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-__device__ uint4 g_big_zero[16] = {};  // a zero feature row (up to 128 bf16 channels)
+#ifndef BIG_WAVES
+#define BIG_WAVES 8
+#endif
+#ifndef BIG_AHEAD
+#define BIG_AHEAD 2
+#endif
 
-template <int CIN, int COUT>
+template <int CIN, int COUT, int NW>
 struct BigShape {
     static constexpr int G = CIN / 32;          // K slices of 32 input channels per tap
     static constexpr int RT = COUT / 16;        // output tiles of 16 channels
     static constexpr int CWF = 16 / RT;         // 16-voxel columns per wave in a full round
     static constexpr int LOG_CWF = CWF >= 4 ? 2 : (CWF >= 2 ? 1 : 0);
-    static constexpr int WAVES = 8;
+    static constexpr int WAVES = NW;
     static constexpr int ROUND = WAVES * CWF;   // columns of a full round
     static constexpr int ROWCH = CIN / 8;       // 16-byte chunks per weight row
     static constexpr int WCH = COUT * ROWCH;    // chunks per weight tap
-    static constexpr int WCOPY = WCH / (64 * WAVES);
+    static constexpr int WCOPY = (WCH + 64 * WAVES - 1) / (64 * WAVES);
+    static constexpr int WBUF = WCOPY * 64 * WAVES;  // chunks per buffer (copies past WCH land in padding)
+    static constexpr int AHEAD = BIG_AHEAD;        // weight fragments read ahead of their MFMAs
     static constexpr int TCH = ROUND * 16 * 27 / 4;  // table chunks of a full round
     static constexpr int TCOPY = (TCH + 64 * WAVES - 1) / (64 * WAVES);
     static_assert(CIN % 32 == 0 && COUT % 16 == 0 && 16 % RT == 0, "tile shape");
-    static_assert(WCH % (64 * WAVES) == 0, "weight copies split evenly over the waves");
     static_assert(CWF * RT <= 16 && CWF * G <= 8, "register budget: 64 accumulators, 32 B-operand VGPRs");
 };
 
@@ -93,9 +99,9 @@ __device__ __forceinline__ void big_unroll(F &&f)
 
 __device__ __forceinline__ void big_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int CIN, int COUT>
+template <int CIN, int COUT, int NW>
 struct BigCtx {
-    using S = BigShape<CIN, COUT>;
+    using S = BigShape<CIN, COUT, NW>;
     const uint16_t *feats;
     const uint16_t *w;
     const float *bias;
@@ -106,19 +112,26 @@ struct BigCtx {
     int flip;
     uint4 *sW0, *sW1, *sT;
     int wave, lane, s16, h;
-    int32_t wofs[S::WCOPY];  // per-lane part of each weight copy's source offset
+    int32_t wofs[S::WCOPY];  // byte offset of each weight chunk this lane copies, tap 0
     int32_t aoff[S::G];      // per-lane chunk offset of each K slice's A fragment
     int64_t tlast;           // last 16-byte chunk that starts inside the table
+    __amdgpu_buffer_rsrc_t rf, rp, rw;  // feats, perm and weights as bounds-checked buffers
 
-    // weight tap k -> buf (row-major, chunk j of row o at o * ROWCH + (j ^ (o % ROWCH)))
-    __device__ __forceinline__ void stage_w(int k, uint4 *buf) const
+    // weight tap k -> registers -> buf (row-major, chunk j of row o at o * ROWCH + (j ^ (o % ROWCH))).
+    // Ordinary loads, not direct-to-LDS copies: with a direct copy in flight the compiler
+    // stops counting loads in order and waits for every load before using any register
+    // operand.
+    __device__ __forceinline__ void load_w(int k, uint4 (&wr)[S::WCOPY]) const
     {
-        int32_t kofs = (flip ? 26 - k : k) * CIN;
-        asm volatile("" : "+s"(kofs));  // keeps the 27 taps' offsets from being hoisted into registers
+        const int32_t kofs = (flip ? 26 - k : k) * (CIN * 2);
 #pragma unroll
         for (int c = 0; c < S::WCOPY; ++c)
-            __builtin_amdgcn_global_load_lds((gbl_void *)(w + (uint32_t)(wofs[c] + kofs)),
-                                             (lds_void *)&buf[(wave + S::WAVES * c) * 64], 16, 0, 0);
+            wr[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wofs[c], kofs, 0));
+    }
+    __device__ __forceinline__ void store_w(uint4 *buf, const uint4 (&wr)[S::WCOPY]) const
+    {
+#pragma unroll
+        for (int c = 0; c < S::WCOPY; ++c) buf[(wave + S::WAVES * c) * 64 + lane] = wr[c];
     }
     // table rows of columns [col, col + ROUND) -> sT
     __device__ __forceinline__ void stage_t(int64_t col) const
@@ -156,14 +169,18 @@ struct BigCtx {
             const int32_t e = tbl[vloc[c] * 27 + k];
             return vok[c] ? e : -1;
         };
-        auto row_of = [&](int32_t e) -> int32_t {
-            const bool ok = (uint32_t)e < (uint64_t)n;
-            const int32_t r = perm[ok ? e : 0];
-            return ok ? r : -1;
+        // perm entry of a sorted position (the buffer load returns 0 for e = -1), and the
+        // byte offset of this lane's part of that row in feats, or an offset past the end
+        // for a missing neighbour (the buffer load of the row then returns zeros).  The
+        // offset is formed in the tap after the perm load was issued, so its wait covers
+        // that load alone, not the operand loads issued after it.
+        auto perm_of = [&](int32_t e) -> int32_t { return __builtin_amdgcn_raw_buffer_load_b32(rp, e * 4, 0, 0); };
+        auto offset_of = [&](int32_t r, int32_t e) -> uint32_t {
+            const uint32_t miss = (uint32_t)e < (uint64_t)n ? 0u : 0x80000000u;
+            return ((uint32_t)r * (CIN * 2) + 16 * h) | miss;
         };
-        auto fptr = [&](int32_t row, int g) -> const uint4 * {
-            return (uint32_t)row < (uint64_t)n ? (const uint4 *)(feats + (int64_t)row * CIN + 32 * g + 8 * h)
-                                               : &g_big_zero[4 * g + h];
+        auto fload = [&](uint32_t off, int g) -> uint4 {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rf, off + 64 * g, 0, 0));
         };
 
         floatx4 acc[RW][CW];
@@ -175,66 +192,73 @@ struct BigCtx {
         // prologue: the table block has landed (copied before this round)
         wait_vmcnt<0>();
         big_lds_barrier();
-        stage_w(0, sW0);
-        int32_t orow[CW], row1[CW], e2[CW];
+        uint4 wr[S::WCOPY];
+        load_w(0, wr);
+        int32_t orow[CW], p1[CW], e1[CW], e2[CW];  // perm and entry of tap k+1, entry of tap k+2
         uint4 F[CW][G];
-        {
-            int32_t row0[CW];
 #pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                orow[c] = perm[vrow[c]];
-                row0[c] = row_of(entry(0, c));
-            }
+        for (int c = 0; c < CW; ++c) {
+            orow[c] = perm[vrow[c]];
+            asm volatile("" ::"v"(orow[c]));  // loaded here, where the prologue waits anyway
+            const int32_t e0 = entry(0, c);
+            const uint32_t off0 = offset_of(perm_of(e0), e0);
 #pragma unroll
-            for (int c = 0; c < CW; ++c)
-#pragma unroll
-                for (int g = 0; g < G; ++g) F[c][g] = *fptr(row0[c], g);
-#pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                row1[c] = row_of(entry(1, c));
-                e2[c] = entry(2, c);
-            }
+            for (int g = 0; g < G; ++g) F[c][g] = fload(off0, g);
+            e1[c] = entry(1, c);
+            p1[c] = perm_of(e1[c]);
+            e2[c] = entry(2, c);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        store_w(sW0, wr);
         big_lds_barrier();
 
         auto tap = [&](auto kc) {
             constexpr int k = decltype(kc)::value;
             const uint4 *cur = ((k & 1) ? sW1 : sW0) + r0 * 16 * S::ROWCH;
             uint4 *nxt = (k & 1) ? sW0 : sW1;
-            if constexpr (k + 1 < 27) stage_w(k + 1, nxt);
-            if constexpr (k == 24) stage_t(col_next);  // every read of this round's table is done
-            __builtin_amdgcn_sched_barrier(0);         // everything below is issued after the copies
-            int32_t row2[CW];
+            if constexpr (k + 1 < 27) load_w(k + 1, wr);
+            __builtin_amdgcn_sched_barrier(0);  // the weight loads go first: they have the whole tap to land
+            uint32_t off1[CW];
+            int32_t p2[CW], ep2[CW];
 #pragma unroll
             for (int c = 0; c < CW; ++c) {
-                if constexpr (k + 2 < 27) row2[c] = row_of(e2[c]);
+                if constexpr (k + 1 < 27) off1[c] = offset_of(p1[c], e1[c]);
+                if constexpr (k + 2 < 27) {
+                    p2[c] = perm_of(e2[c]);
+                    ep2[c] = e2[c];
+                }
                 if constexpr (k + 3 < 27) e2[c] = entry(k + 3, c);
             }
+            // A fragments i = g * RW + r, read AHEAD steps before their MFMAs
+            constexpr int NA = G * RW, AHEAD = S::AHEAD;
+            uint4 a[AHEAD + 1];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int i = 0; i < AHEAD && i < NA; ++i) a[i] = cur[(i % RW) * 16 * S::ROWCH + aoff[i / RW]];
 #pragma unroll
-                for (int r = 0; r < RW; ++r) {
-                    const uint4 a = cur[r * 16 * S::ROWCH + aoff[g]];
+            for (int i = 0; i < NA; ++i) {
+                const int g = i / RW, r = i % RW;
+                if (i + AHEAD < NA)
+                    a[(i + AHEAD) % (AHEAD + 1)] = cur[((i + AHEAD) % RW) * 16 * S::ROWCH + aoff[(i + AHEAD) / RW]];
 #pragma unroll
-                    for (int c = 0; c < CW; ++c)
-                        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                            __builtin_bit_cast(bf16x8_t, F[c][g]),
-                                                                            acc[r][c], 0, 0, 0);
-                }
+                for (int c = 0; c < CW; ++c)
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i % (AHEAD + 1)]),
+                                                                        __builtin_bit_cast(bf16x8_t, F[c][g]),
+                                                                        acc[r][c], 0, 0, 0);
                 if constexpr (k + 1 < 27) {
+                    if (r == RW - 1) {
 #pragma unroll
-                    for (int c = 0; c < CW; ++c) F[c][g] = *fptr(row1[c], g);
+                        for (int c = 0; c < CW; ++c) F[c][g] = fload(off1[c], g);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);  // bound how far weight reads are hoisted (registers)
             }
 #pragma unroll
             for (int c = 0; c < CW; ++c)
-                if constexpr (k + 2 < 27) row1[c] = row2[c];
-            // the weight copy of tap k+1 has landed once at most the loads issued after it are pending
-            constexpr int after = ((k + 1 < 27) ? CW * G : 0) + ((k + 2 < 27) ? CW : 0) + (k == 24 ? S::TCOPY : 0);
+                if constexpr (k + 2 < 27) {
+                    p1[c] = p2[c];
+                    e1[c] = ep2[c];
+                }
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<after>();
+            if constexpr (k + 1 < 27) store_w(nxt, wr);
             big_lds_barrier();
         };
         big_unroll<0, 27>(tap);
@@ -254,11 +278,12 @@ struct BigCtx {
                                __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
             }
         }
+        stage_t(col_next);  // every read of this round's table is done (barrier after tap 23)
     }
 };
 
-template <int CIN, int COUT>
-__global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict__ feats,
+template <int CIN, int COUT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void k_conv_big(const uint16_t *__restrict__ feats,
                                                      const uint16_t *__restrict__ w,
                                                      const float *__restrict__ bias,
                                                      const int32_t *__restrict__ nbr_sp,
@@ -266,18 +291,19 @@ __global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict_
                                                      uint16_t *__restrict__ out, int64_t n, int64_t ncols,
                                                      int flip)
 {
-    using S = BigShape<CIN, COUT>;
-    __shared__ uint4 sW0[S::WCH];
-    __shared__ uint4 sW1[S::WCH];
+    using S = BigShape<CIN, COUT, NW>;
+    __shared__ uint4 sW0[S::WBUF];
+    __shared__ uint4 sW1[S::WBUF];
     __shared__ uint4 sT[S::TCOPY * 64 * S::WAVES];
 
     // this block's columns: the XCD's contiguous share, split evenly among its blocks
+    // (contiguous runs measured faster than dealing rounds in turn among an XCD's blocks)
     const int xcd = blockIdx.x & 7, bpx = gridDim.x >> 3, jb = blockIdx.x >> 3;
     const int64_t xs = ncols * xcd / 8, xe = ncols * (xcd + 1) / 8;
     const int64_t cb = xs + (xe - xs) * jb / bpx, ce = xs + (xe - xs) * (jb + 1) / bpx;
     if (cb >= ce) return;
 
-    BigCtx<CIN, COUT> x;
+    BigCtx<CIN, COUT, NW> x;
     x.feats = feats; x.w = w; x.bias = bias; x.nbr_sp = nbr_sp; x.perm = perm; x.out = out;
     x.n = n; x.flip = flip; x.sW0 = sW0; x.sW1 = sW1; x.sT = sT;
     const int tid = threadIdx.x;
@@ -287,9 +313,9 @@ __global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict_
     x.h = x.lane >> 4;
 #pragma unroll
     for (int c = 0; c < S::WCOPY; ++c) {
-        const int q = (x.wave + S::WAVES * c) * 64 + x.lane;
+        const int q = ((x.wave + S::WAVES * c) * 64 + x.lane) % S::WCH;
         const int o = q / S::ROWCH, p = q % S::ROWCH;
-        x.wofs[c] = o * 27 * CIN + 8 * (p ^ (o % S::ROWCH));
+        x.wofs[c] = 2 * (o * 27 * CIN + 8 * (p ^ (o % S::ROWCH)));
     }
     {
         const int xr = x.h ^ (x.s16 % S::ROWCH);
@@ -297,6 +323,9 @@ __global__ __launch_bounds__(512, 1) void k_conv_big(const uint16_t *__restrict_
         for (int g = 0; g < S::G; ++g) x.aoff[g] = x.s16 * S::ROWCH + ((4 * g) ^ xr);
     }
     x.tlast = (n * 27 + 3) / 4 - 1;
+    x.rf = __builtin_amdgcn_make_buffer_rsrc((void *)feats, (short)0, (int)(n * CIN * 2), 0x00020000);
+    x.rp = __builtin_amdgcn_make_buffer_rsrc((void *)perm, (short)0, (int)(n * 4), 0x00020000);
+    x.rw = __builtin_amdgcn_make_buffer_rsrc((void *)w, (short)0, 27 * CIN * COUT * 2, 0x00020000);
 
     x.stage_t(cb);
     for (int64_t col = cb; col < ce; col += S::ROUND) {
@@ -323,16 +352,16 @@ static int big_device_cus(int dev)
     return cus;
 }
 
-template <int CIN, int COUT>
+template <int CIN, int COUT, int NW>
 static int launch_big_t(const void *f, const void *w, const float *b, const submconv_rulebook *rb, void *o, int flip,
                         hipStream_t s)
 {
-    using S = BigShape<CIN, COUT>;
+    using S = BigShape<CIN, COUT, NW>;
     const int64_t ncols = (rb->n + 15) / 16;
     int64_t blocks = big_device_cus(rb->device) & ~7;
     if (blocks < 8) blocks = 8;
     if (blocks > ((ncols + 7) & ~int64_t(7))) blocks = (ncols + 7) & ~int64_t(7);
-    hipLaunchKernelGGL((k_conv_big<CIN, COUT>), dim3((unsigned)blocks), dim3(S::WAVES * 64), 0, s,
+    hipLaunchKernelGGL((k_conv_big<CIN, COUT, NW>), dim3((unsigned)blocks), dim3(S::WAVES * 64), 0, s,
                        (const uint16_t *)f, (const uint16_t *)w, b, rb->nbr_sp, rb->perm, (uint16_t *)o, rb->n,
                        ncols, flip);
     SC_LAUNCHED("conv_big");
@@ -349,8 +378,8 @@ int launch_big(const void *feats, const void *w, const float *bias, const submco
 {
     if (!big_supported(cin, cout, dtype))
         return fail(SUBMCONV_E_UNSUPPORTED, "persistent kernel: bf16 with 64->64 or 128->128 channels only");
-    if (cin == 128) return launch_big_t<128, 128>(feats, w, bias, rb, out, flip, s);
-    return launch_big_t<64, 64>(feats, w, bias, rb, out, flip, s);
+    if (cin == 128) return launch_big_t<128, 128, BIG_WAVES>(feats, w, bias, rb, out, flip, s);
+    return launch_big_t<64, 64, BIG_WAVES>(feats, w, bias, rb, out, flip, s);
 }
 
 }  // namespace sc
