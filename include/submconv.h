@@ -63,14 +63,15 @@ extern "C" {
 #define SUBMCONV_BF16 1
 
 /* Forward kernel selection (submconv_forward_variant). */
-#define SUBMCONV_KERNEL_AUTO 0    /* pick by (Cin, Cout, dtype) */
+#define SUBMCONV_KERNEL_AUTO 0    /* pick by (Cin, Cout, dtype, N) */
 #define SUBMCONV_KERNEL_GENERIC 1 /* one thread per output element, any channel counts */
 #define SUBMCONV_KERNEL_LOWC 2    /* narrow channels (<= 32), wave shuffles, no matrix cores */
 #define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128} */
 #define SUBMCONV_KERNEL_WINDOW 4  /* matrix cores fed from a tile's neighbourhood staged in LDS
                                      (bf16, Cin = Cout = 32) */
 #define SUBMCONV_KERNEL_PERSISTENT 5 /* persistent matrix-core kernel, weights streamed through LDS,
-                                        operands gathered into registers (bf16, 64->64 or 128->128) */
+                                        operands gathered into registers (bf16, 64->64 or 128->128,
+                                        N * Cin * 2 <= 2^31 - 1; otherwise SUBMCONV_E_UNSUPPORTED) */
 
 typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
 

@@ -14,7 +14,6 @@ int launch_forward(const void *feats, const void *w, const float *bias,
                    int variant, hipStream_t s);
 int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s);
 int64_t win_plan_ints(int64_t n);
-int choose_forward_kernel(int cin, int cout, int dtype);
 int subdivide(const int32_t *coords, const void *feats, int64_t n, int c, int dtype,
               int32_t *out_coords, void *out_feats, hipStream_t s);
 int space_to_depth(const int32_t *coords, const void *feats, int64_t n, int c, int dtype, int res,

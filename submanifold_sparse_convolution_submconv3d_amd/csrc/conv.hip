@@ -641,18 +641,16 @@ static int launch_mfma(const void *f, const void *w, const float *b, const int32
 }
 
 bool window_supported(int cin, int cout, int dtype);
-bool big_supported(int cin, int cout, int dtype);
+bool big_supported(int cin, int cout, int dtype, int64_t n);
 int launch_big(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb, void *out,
                int cin, int cout, int dtype, int flip, hipStream_t s);
 int launch_window(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb,
                   void *out, int cin, int cout, int dtype, int flip, hipStream_t s);
 
-int choose_forward_kernel(int cin, int cout, int dtype)
+int choose_forward_kernel(int cin, int cout, int dtype, int64_t n)
 {
     if (window_supported(cin, cout, dtype)) return SUBMCONV_KERNEL_WINDOW;
-    // the persistent kernel wins at 128 channels; at 64 the row-gathered kernel is
-    // faster (gathering 128-byte rows into registers is the persistent kernel's limit)
-    if (big_supported(cin, cout, dtype) && cin == 128) return SUBMCONV_KERNEL_PERSISTENT;
+    if (big_supported(cin, cout, dtype, n)) return SUBMCONV_KERNEL_PERSISTENT;
     if (mfma_size(cin) && mfma_size(cout)) return SUBMCONV_KERNEL_MFMA;
     if (pow2_le32(cin) && pow2_le32(cout)) return SUBMCONV_KERNEL_LOWC;
     (void)dtype;
@@ -665,7 +663,7 @@ int launch_forward(const void *feats, const void *w, const float *bias, const su
     const int64_t n = rb->n;
     const int32_t *nbr = rb->nbr_sp, *perm = rb->perm;
     if (n == 0) return SUBMCONV_OK;
-    if (variant == SUBMCONV_KERNEL_AUTO) variant = choose_forward_kernel(cin, cout, dtype);
+    if (variant == SUBMCONV_KERNEL_AUTO) variant = choose_forward_kernel(cin, cout, dtype, n);
     switch (variant) {
     case SUBMCONV_KERNEL_GENERIC:
         return dtype == SUBMCONV_F32

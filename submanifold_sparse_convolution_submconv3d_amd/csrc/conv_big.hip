@@ -45,6 +45,9 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 #ifndef BIG_WAVES
 #define BIG_WAVES 8
 #endif
+#ifndef BIG_QUAD
+#define BIG_QUAD 1
+#endif
 #ifndef BIG_AHEAD
 #define BIG_AHEAD 2
 #endif
@@ -154,20 +157,26 @@ struct BigCtx {
         const int cg = wave / D::PARTS, r0 = (wave - cg * D::PARTS) * RW;
         const int32_t *tbl = (const int32_t *)sT;
 
-        int vloc[CW];
-        int64_t vrow[CW];
-        bool vok[CW];
+        // Gathers use the quad layout (lane l reads 16 bytes of voxel l/4's row: four
+        // consecutive lanes cover 64 contiguous bytes, half the cache-line lookups of the
+        // operand layout); each fragment is then moved into the operand layout (lane l:
+        // voxel l%16, chunk l/16) by four ds_bpermute.  gv* is the gathering voxel of this
+        // lane, ov* the voxel whose outputs this lane holds.
+        int gvloc[CW];
+        bool gvok[CW], ovok[CW];
+        int64_t ovrow[CW];
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
             const int colr = cg * CW + c;
-            vloc[c] = colr * 16 + s16;
-            const int64_t v = col * 16 + vloc[c];
-            vok[c] = colr < ncols && v < n;
-            vrow[c] = vok[c] ? v : 0;
+            gvloc[c] = colr * 16 + (BIG_QUAD ? (lane >> 2) : s16);
+            gvok[c] = colr < ncols && col * 16 + gvloc[c] < n;
+            const int64_t ov = col * 16 + colr * 16 + s16;
+            ovok[c] = colr < ncols && ov < n;
+            ovrow[c] = ovok[c] ? ov : 0;
         }
         auto entry = [&](int k, int c) -> int32_t {
-            const int32_t e = tbl[vloc[c] * 27 + k];
-            return vok[c] ? e : -1;
+            const int32_t e = tbl[gvloc[c] * 27 + k];
+            return gvok[c] ? e : -1;
         };
         // perm entry of a sorted position (the buffer load returns 0 for e = -1), and the
         // byte offset of this lane's part of that row in feats, or an offset past the end
@@ -177,10 +186,18 @@ struct BigCtx {
         auto perm_of = [&](int32_t e) -> int32_t { return __builtin_amdgcn_raw_buffer_load_b32(rp, e * 4, 0, 0); };
         auto offset_of = [&](int32_t r, int32_t e) -> uint32_t {
             const uint32_t miss = (uint32_t)e < (uint64_t)n ? 0u : 0x80000000u;
-            return ((uint32_t)r * (CIN * 2) + 16 * h) | miss;
+            return ((uint32_t)r * (CIN * 2) + 16 * (BIG_QUAD ? (lane & 3) : h)) | miss;
         };
         auto fload = [&](uint32_t off, int g) -> uint4 {
             return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rf, off + 64 * g, 0, 0));
+        };
+        const int tsrc = 4 * (4 * s16 + h);  // operand lane l takes quad lane 4 (l % 16) + l / 16
+        auto tr = [&](const uint4 v) -> uint4 {
+            if constexpr (!BIG_QUAD) return v;
+            return uint4{(uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.x),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.y),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.z),
+                         (uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.w)};
         };
 
         floatx4 acc[RW][CW];
@@ -198,7 +215,7 @@ struct BigCtx {
         uint4 F[CW][G];
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
-            orow[c] = perm[vrow[c]];
+            orow[c] = perm[ovrow[c]];
             asm volatile("" ::"v"(orow[c]));  // loaded here, where the prologue waits anyway
             const int32_t e0 = entry(0, c);
             const uint32_t off0 = offset_of(perm_of(e0), e0);
@@ -228,9 +245,12 @@ struct BigCtx {
                 }
                 if constexpr (k + 3 < 27) e2[c] = entry(k + 3, c);
             }
-            // A fragments i = g * RW + r, read AHEAD steps before their MFMAs
+            // A fragments i = g * RW + r, read AHEAD steps before their MFMAs; B fragments
+            // of slice g + 1 moved into the operand layout while slice g computes
             constexpr int NA = G * RW, AHEAD = S::AHEAD;
-            uint4 a[AHEAD + 1];
+            uint4 a[AHEAD + 1], T[2][CW];
+#pragma unroll
+            for (int c = 0; c < CW; ++c) T[0][c] = tr(F[c][0]);
 #pragma unroll
             for (int i = 0; i < AHEAD && i < NA; ++i) a[i] = cur[(i % RW) * 16 * S::ROWCH + aoff[i / RW]];
 #pragma unroll
@@ -238,10 +258,14 @@ struct BigCtx {
                 const int g = i / RW, r = i % RW;
                 if (i + AHEAD < NA)
                     a[(i + AHEAD) % (AHEAD + 1)] = cur[((i + AHEAD) % RW) * 16 * S::ROWCH + aoff[(i + AHEAD) / RW]];
+                if (r == 0 && g + 1 < G) {
+#pragma unroll
+                    for (int c = 0; c < CW; ++c) T[(g + 1) & 1][c] = tr(F[c][g + 1]);
+                }
 #pragma unroll
                 for (int c = 0; c < CW; ++c)
                     acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i % (AHEAD + 1)]),
-                                                                        __builtin_bit_cast(bf16x8_t, F[c][g]),
+                                                                        __builtin_bit_cast(bf16x8_t, T[g & 1][c]),
                                                                         acc[r][c], 0, 0, 0);
                 if constexpr (k + 1 < 27) {
                     if (r == RW - 1) {
@@ -266,7 +290,7 @@ struct BigCtx {
         // epilogue: lane holds output channels 16 (r0 + r) + 4 h .. +3 of its voxel in column c
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
-            if (!vok[c]) continue;
+            if (!ovok[c]) continue;
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
                 const int o = 16 * (r0 + r) + 4 * h;
@@ -368,16 +392,19 @@ static int launch_big_t(const void *f, const void *w, const float *b, const subm
     return SUBMCONV_OK;
 }
 
-bool big_supported(int cin, int cout, int dtype)
+// Features are addressed through a buffer resource with 32-bit byte offsets.
+bool big_supported(int cin, int cout, int dtype, int64_t n)
 {
-    return dtype == SUBMCONV_BF16 && ((cin == 128 && cout == 128) || (cin == 64 && cout == 64));
+    return dtype == SUBMCONV_BF16 && ((cin == 128 && cout == 128) || (cin == 64 && cout == 64)) &&
+           n * cin * 2 <= INT32_MAX;
 }
 
 int launch_big(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb, void *out,
                int cin, int cout, int dtype, int flip, hipStream_t s)
 {
-    if (!big_supported(cin, cout, dtype))
-        return fail(SUBMCONV_E_UNSUPPORTED, "persistent kernel: bf16 with 64->64 or 128->128 channels only");
+    if (!big_supported(cin, cout, dtype, rb->n))
+        return fail(SUBMCONV_E_UNSUPPORTED,
+                    "persistent kernel: bf16 with 64->64 or 128->128 channels and at most 2^31 feature bytes");
     if (cin == 128) return launch_big_t<128, 128, BIG_WAVES>(feats, w, bias, rb, out, flip, s);
     return launch_big_t<64, 64, BIG_WAVES>(feats, w, bias, rb, out, flip, s);
 }

@@ -306,7 +306,7 @@ def test_forward_workloads_full(idx, dtype):
 def _auto_kernel(cin, cout, dtype="f32"):
     if cin == 32 and cout == 32 and dtype == "bf16":
         return "window"
-    if dtype == "bf16" and (cin, cout) == (128, 128):
+    if dtype == "bf16" and (cin, cout) in ((64, 64), (128, 128)):
         return "persistent"
     if cin in (32, 64, 128) and cout in (32, 64, 128):
         return "mfma"
