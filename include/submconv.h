@@ -184,6 +184,43 @@ int submconv_depth_to_space(const int32_t *coarse_coords, const void *coarse_fea
                             const uint8_t *mask, int64_t m, int32_t c, int32_t dtype,
                             int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream);
 
+/*
+ * Masked upsample (trellis_sparse_mrp_mlx commits, the commit closing the op gap
+ * for Pixal3D: a masked expansion, distinct from subdivide): voxel i emits child
+ * slot s iff mask[i, s] != 0, s ascending, child (b, 2z + s%2, 2y + (s/2)%2,
+ * 2x + s/4) -- axis 0 fastest, the reverse of subdivide's C order -- whose
+ * feature row is a copy of feats[i].  A voxel with no flagged slot emits nothing.
+ *   coords device int32 [n,4] (0 <= z,y,x < 2^30), feats device [n,c] of dtype,
+ *   mask device uint8 [n,8]; out_coords [capacity >= 8n, 4], out_feats
+ *   [capacity >= 8n, c]; out_n host int64, receives the number of children
+ *   (children of voxel i follow those of voxel i-1).
+ * Synchronises `stream` once to read the count.  Outputs must not overlap inputs
+ * (E_ALIAS).
+ */
+int submconv_upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int32_t c,
+                             int32_t dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream);
+
+/* Pooling modes of submconv_downsample. */
+#define SUBMCONV_POOL_MAX 0
+#define SUBMCONV_POOL_MEAN 1
+
+/*
+ * Sparse downsample by 2 (same commit: the mode differs between models and must be
+ * explicit): every coarse voxel (b, z/2, y/2, x/2) that holds a fine voxel gets the
+ * channel-wise maximum (SUBMCONV_POOL_MAX, exact) or mean (SUBMCONV_POOL_MEAN: fp32
+ * sum over its occupied children in slot order, divided by their count, one rounding
+ * to the output type) of its children's feature rows.
+ *   coords [n,4], feats [n,c]: fine set, validated like submconv_build_map against
+ *            res and batch (E_COORD_RANGE, E_DUPLICATE).
+ *   out_coords : [capacity >= n, 4] -> coarse coords, ascending (b, z, y, x).
+ *   out_feats  : [capacity >= n, c] -> pooled rows.
+ *   out_m      : host int64, receives M, the number of coarse voxels.
+ * Synchronises `stream` to read M and the status.
+ */
+int submconv_downsample(const int32_t *coords, const void *feats, int64_t n, int32_t c, int32_t dtype, int32_t res,
+                        int32_t batch, int32_t mode, int32_t *out_coords, void *out_feats, int64_t *out_m,
+                        void *stream);
+
 /* Name of a status code (static string). */
 const char *submconv_status_string(int status);
 

@@ -15,6 +15,8 @@ Functions carry the C names:
     submconv_subdivide(coords, feats=None)          -> (coords8, feats8)
     submconv_space_to_depth(coords, feats, res, batch) -> (coarse, feats8c, mask)
     submconv_depth_to_space(coarse, feats8c, mask=None) -> (coords, feats)
+    submconv_upsample_masked(coords, feats, mask)   -> (coords, feats)
+    submconv_downsample(coords, feats, res, batch, mode) -> (coarse, feats)
 
 `RulebookCache` keeps one rulebook per coordinate set, keyed like the
 upstream library's indice_key, so every convolution on a set reuses its map
@@ -31,7 +33,8 @@ import torch
 __all__ = [
     "SubmconvError", "Rulebook", "RulebookCache", "lib_path", "load_library",
     "submconv_build_map", "submconv_forward", "submconv_subdivide",
-    "submconv_space_to_depth", "submconv_depth_to_space",
+    "submconv_space_to_depth", "submconv_depth_to_space", "submconv_upsample_masked", "submconv_downsample",
+    "POOL_MAX", "POOL_MEAN",
     "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA", "KERNEL_WINDOW", "KERNEL_PERSISTENT",
 ]
 
@@ -78,6 +81,8 @@ def load_library():
         "submconv_subdivide": [vp, vp, i64, i32, i32, vp, vp, vp],
         "submconv_space_to_depth": [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, i64p, vp],
         "submconv_depth_to_space": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
+        "submconv_upsample_masked": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
+        "submconv_downsample": [vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64p, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -305,3 +310,45 @@ class RulebookCache:
 
     def __len__(self):
         return len(self._maps)
+
+
+POOL_MAX, POOL_MEAN = 0, 1  # submconv_downsample modes (SUBMCONV_POOL_*)
+
+
+def submconv_upsample_masked(coords: torch.Tensor, feats: torch.Tensor, mask: torch.Tensor):
+    """Masked expansion: voxel i emits child s iff mask[i, s] (axis 0 fastest), feats copied -> (coords, feats)."""
+    _dev(coords, "coords", torch.int32)
+    _dev(feats, "feats")
+    _dev(mask, "mask", torch.uint8)
+    n, c = feats.shape
+    if tuple(mask.shape) != (n, 8) or coords.shape[0] != n:
+        raise ValueError("coords [N,4], feats [N,C] and mask uint8 [N,8] must agree")
+    out_c = torch.empty((max(8 * n, 1), 4), dtype=torch.int32, device=coords.device)
+    out_f = torch.empty((max(8 * n, 1), c), dtype=feats.dtype, device=feats.device)
+    cnt = ctypes.c_int64()
+    with torch.cuda.device(coords.device):
+        _check(load_library().submconv_upsample_masked(
+            ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(feats.data_ptr()), ctypes.c_void_p(mask.data_ptr()),
+            n, c, _dtype_code(feats), ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(out_f.data_ptr()),
+            ctypes.byref(cnt), _stream(coords.device)), "submconv_upsample_masked")
+    k = cnt.value
+    return out_c[:k], out_f[:k]
+
+
+def submconv_downsample(coords: torch.Tensor, feats: torch.Tensor, res: int, batch: int, mode: str):
+    """Factor-2 pooling of each coarse voxel's children, mode 'max' or 'mean' -> (coarse int32 [M,4], feats [M,C])."""
+    if mode not in ("max", "mean"):
+        raise ValueError("mode must be 'max' or 'mean' (it differs between models, so it has no default)")
+    _dev(coords, "coords", torch.int32)
+    _dev(feats, "feats")
+    n, c = feats.shape
+    out_c = torch.empty((max(n, 1), 4), dtype=torch.int32, device=coords.device)
+    out_f = torch.empty((max(n, 1), c), dtype=feats.dtype, device=feats.device)
+    m = ctypes.c_int64()
+    with torch.cuda.device(coords.device):
+        _check(load_library().submconv_downsample(
+            ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(feats.data_ptr()), n, c, _dtype_code(feats),
+            int(res), int(batch), POOL_MAX if mode == "max" else POOL_MEAN, ctypes.c_void_p(out_c.data_ptr()),
+            ctypes.c_void_p(out_f.data_ptr()), ctypes.byref(m), _stream(coords.device)), "submconv_downsample")
+    k = m.value
+    return out_c[:k], out_f[:k]

@@ -21,6 +21,10 @@ int space_to_depth(const int32_t *coords, const void *feats, int64_t n, int c, i
                    int64_t *out_m, hipStream_t s);
 int depth_to_space(const int32_t *cc, const void *cf, const uint8_t *mask, int64_t m, int c,
                    int dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
+int upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int c, int dtype,
+                    int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
+int downsample(const int32_t *coords, const void *feats, int64_t n, int c, int dtype, int res, int batch,
+               int mean, int32_t *out_coords, void *out_feats, int64_t *out_m, hipStream_t s);
 
 static thread_local char g_err[512];
 
@@ -309,6 +313,48 @@ int submconv_depth_to_space(const int32_t *coarse_coords, const void *coarse_fea
         return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
     return depth_to_space(coarse_coords, coarse_feats, mask, m, c, dtype, out_coords, out_feats,
                           out_n, (hipStream_t)stream);
+}
+
+int submconv_upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int32_t c,
+                             int32_t dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream)
+{
+    if (!out_n) return fail(SUBMCONV_E_INVALID_ARG, "out_n is NULL");
+    *out_n = 0;
+    if (n < 0 || n >= (int64_t(1) << 28)) return fail(SUBMCONV_E_INVALID_ARG, "n = %lld outside [0, 2^28)", (long long)n);
+    if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+    if (c < 1 || c > 65536) return fail(SUBMCONV_E_INVALID_ARG, "c = %d", c);
+    if (n == 0) return SUBMCONV_OK;
+    if (!coords || !feats || !mask || !out_coords || !out_feats) return fail(SUBMCONV_E_INVALID_ARG, "NULL pointer");
+    if (!aligned16(coords) || !aligned16(out_coords)) return fail(SUBMCONV_E_INVALID_ARG, "coordinate pointers must be 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    if (overlaps(out_feats, (size_t)n * 8 * c * es, feats, (size_t)n * c * es) ||
+        overlaps(out_coords, (size_t)n * 128, coords, (size_t)n * 16) ||
+        overlaps(out_feats, (size_t)n * 8 * c * es, mask, (size_t)n * 8) ||
+        overlaps(out_coords, (size_t)n * 128, mask, (size_t)n * 8))
+        return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
+    return upsample_masked(coords, feats, mask, n, c, dtype, out_coords, out_feats, out_n, (hipStream_t)stream);
+}
+
+int submconv_downsample(const int32_t *coords, const void *feats, int64_t n, int32_t c, int32_t dtype, int32_t res,
+                        int32_t batch, int32_t mode, int32_t *out_coords, void *out_feats, int64_t *out_m,
+                        void *stream)
+{
+    if (!out_m) return fail(SUBMCONV_E_INVALID_ARG, "out_m is NULL");
+    *out_m = 0;
+    if (n < 0 || n >= (int64_t(1) << 31)) return fail(SUBMCONV_E_INVALID_ARG, "n = %lld outside [0, 2^31)", (long long)n);
+    if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+    if (mode != SUBMCONV_POOL_MAX && mode != SUBMCONV_POOL_MEAN) return fail(SUBMCONV_E_INVALID_ARG, "mode %d", mode);
+    if (c < 1 || c > 65536) return fail(SUBMCONV_E_INVALID_ARG, "c = %d", c);
+    if (res < 1 || batch < 1) return fail(SUBMCONV_E_INVALID_ARG, "res and batch must be >= 1");
+    if (n == 0) return SUBMCONV_OK;
+    if (!coords || !feats || !out_coords || !out_feats) return fail(SUBMCONV_E_INVALID_ARG, "NULL pointer");
+    if (!aligned16(coords) || !aligned16(out_coords)) return fail(SUBMCONV_E_INVALID_ARG, "coordinate pointers must be 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    if (overlaps(out_feats, (size_t)n * c * es, feats, (size_t)n * c * es) ||
+        overlaps(out_coords, (size_t)n * 16, coords, (size_t)n * 16))
+        return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
+    return downsample(coords, feats, n, c, dtype, res, batch, mode == SUBMCONV_POOL_MEAN, out_coords, out_feats,
+                      out_m, (hipStream_t)stream);
 }
 
 }  // extern "C"

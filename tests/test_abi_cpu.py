@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("submconv_build_map", "submconv_forward", "submconv_rulebook_neighbors",
                      "submconv_rulebook_free", "submconv_subdivide", "submconv_space_to_depth",
-                     "submconv_depth_to_space", "submconv_status_string"):
+                     "submconv_depth_to_space", "submconv_upsample_masked", "submconv_downsample",
+                     "submconv_status_string"):
         assert required in names
 
 
@@ -87,6 +88,14 @@ def test_helper_argument_errors(lib):
     assert lib.submconv_space_to_depth(fake, fake, 4, 0, 0, 16, 1, fake, fake, None, ctypes.byref(m), None) == E_INVALID_ARG
     assert lib.submconv_depth_to_space(fake, fake, None, 4, 8, 0, fake, fake, None, None) == E_INVALID_ARG
     assert lib.submconv_depth_to_space(fake, fake, None, -2, 8, 0, fake, fake, ctypes.byref(m), None) == E_INVALID_ARG
+    assert lib.submconv_upsample_masked(fake, fake, fake, 4, 8, 0, fake, fake, None, None) == E_INVALID_ARG
+    assert lib.submconv_upsample_masked(fake, fake, None, 4, 8, 0, fake, fake, ctypes.byref(m), None) == E_INVALID_ARG
+    assert lib.submconv_upsample_masked(fake, fake, fake, 4, 8, 3, fake, fake, ctypes.byref(m), None) == E_UNSUPPORTED
+    assert lib.submconv_upsample_masked(fake, fake, fake, 4, 8, 0, fake, fake, ctypes.byref(m), None) == E_ALIAS
+    assert lib.submconv_downsample(fake, fake, 4, 8, 0, 16, 1, 0, fake, fake, None, None) == E_INVALID_ARG
+    assert lib.submconv_downsample(fake, fake, 4, 8, 0, 16, 1, 2, fake, fake, ctypes.byref(m), None) == E_INVALID_ARG
+    assert lib.submconv_downsample(fake, fake, 4, 8, 0, 0, 1, 0, fake, fake, ctypes.byref(m), None) == E_INVALID_ARG
+    assert lib.submconv_downsample(fake, fake, 4, 8, 0, 16, 1, 1, fake, fake, ctypes.byref(m), None) == E_ALIAS
     assert lib.submconv_rulebook_neighbors(None, None, None, None) == E_INVALID_ARG
     assert lib.submconv_rulebook_info(None, None, None, None, None) == E_INVALID_ARG
     assert lib.submconv_rulebook_free(None, None) == 0
@@ -99,6 +108,12 @@ def test_empty_inputs_are_no_ops(lib):
     assert m.value == 0
     m.value = 5
     assert lib.submconv_depth_to_space(None, None, None, 0, 4, 0, None, None, ctypes.byref(m), None) == 0
+    assert m.value == 0
+    m.value = 5
+    assert lib.submconv_upsample_masked(None, None, None, 0, 4, 0, None, None, ctypes.byref(m), None) == 0
+    assert m.value == 0
+    m.value = 5
+    assert lib.submconv_downsample(None, None, 0, 4, 1, 16, 1, 0, None, None, ctypes.byref(m), None) == 0
     assert m.value == 0
 
 

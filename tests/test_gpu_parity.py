@@ -425,6 +425,60 @@ def test_space_to_depth_errors():
     assert e.value.status == -2
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n,c", [(1, 8), (900, 5), (900, 8), (5000, 32), (20000, 64)])
+def test_upsample_masked(dtype, n, c):
+    """Masked expansion (a copy): bit-exact against the oracle, including voxels that
+    flag no child and voxels that flag all eight; c = 5 takes the per-element path,
+    the others whole 16-byte vectors."""
+    coords = synth.random_coords(n, 64, 2, 21)
+    feats, _, _ = synth.make_values(n, c, 1, 21)
+    rng = np.random.default_rng(21)
+    mask = (rng.random((n, 8)) < 0.4).astype(np.uint8)
+    mask[::7] = 0
+    mask[3::11] = 1
+    tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, c), np.float32), None, dtype)
+    note("upsample_masked %s n=%d c=%d" % (dtype, n, c))
+    kc, kf = sc.submconv_upsample_masked(coords_dev(coords), tf, torch.from_numpy(mask).to(DEV))
+    ec, ef = ref.upsample_masked(coords, f64, mask)
+    assert len(ec) == int(mask.astype(bool).sum())
+    np.testing.assert_array_equal(kc.cpu().numpy(), ec)
+    np.testing.assert_array_equal(to_f64(kf), ef)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["max", "mean"])
+@pytest.mark.parametrize("n,res,batch,c", [(1, 2, 1, 4), (900, 12, 2, 5), (5000, 33, 1, 32), (60000, 64, 2, 64)])
+def test_downsample(dtype, mode, n, res, batch, c):
+    """Pooling by 2: coarse coords exact and ascending; max exact; mean within the
+    feature tolerance (fp32 sum in slot order vs the oracle's fp64 mean)."""
+    coords = synth.random_coords(n, res, batch, 22)
+    coords = coords[synth.shuffle_rows(len(coords), 22)]
+    feats, _, _ = synth.make_values(len(coords), c, 1, 22)
+    tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, c), np.float32), None, dtype)
+    note("downsample %s %s n=%d res=%d c=%d" % (dtype, mode, len(coords), res, c))
+    gc, gf = sc.submconv_downsample(coords_dev(coords), tf, res, batch, mode)
+    ec, ef = ref.downsample(coords, f64, mode)
+    np.testing.assert_array_equal(gc.cpu().numpy(), ec)
+    if mode == "max":
+        np.testing.assert_array_equal(to_f64(gf), ef)
+    else:
+        assert_close(to_f64(gf), ef, dtype, "downsample mean")
+
+
+def test_downsample_errors():
+    note("downsample errors")
+    f = torch.zeros((2, 4), device=DEV)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1], [0, 1, 1, 1]], np.int32)), f, 4, 1, "max")
+    assert e.value.status == -3
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.submconv_downsample(coords_dev(np.array([[0, 9, 1, 1]], np.int32)), f[:1], 4, 1, "mean")
+    assert e.value.status == -2
+    with pytest.raises(ValueError):
+        sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1]], np.int32)), f[:1], 4, 1, "sum")
+
+
 def test_rulebook_neighbors_pointer_matches_copy():
     """submconv_rulebook_neighbors builds the input-order table once and hands out
     a device pointer; its bytes equal the copy API's and the oracle's."""
