@@ -95,6 +95,98 @@ def cpu_baseline(coords, feats, weight, bias, res, batch, budget_s):
     }
 
 
+def bench_helpers(args):
+    """The coordinate-set helpers on the 256^3 noisy-sphere parent shell (32 channels
+    bf16) and its 512^3 subdivision: each op's mean event time over the reps, its
+    algorithmic HBM bytes (inputs read once, outputs written once) against 8 TB/s,
+    and the oracle on a bounded sample of the same input."""
+    import numpy as np
+    import torch
+
+    import synth
+    import submanifold_sparse_convolution_submconv3d_amd as sc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sc.load_library()
+    w, parent = synth.workload(5)
+    c, s_el = w.cin, 2
+    pc = torch.from_numpy(parent).to(dev)
+    np_ = len(parent)
+    pf_h, _, _ = synth.make_values(np_, c, 1, 31)
+    pf = torch.from_numpy(synth.bf16_bits(pf_h).view(np.int16)).view(torch.bfloat16).to(dev)
+    mask_h = (np.random.default_rng(31).random((np_, 8)) < 0.4).astype(np.uint8)
+    mask = torch.from_numpy(mask_h).to(dev)
+    kids, kf = sc.submconv_subdivide(pc, pf)
+    nk = kids.shape[0]
+    res = w.res
+    reps, warm = max(3, args.steps), max(1, args.warmup)
+
+    def timed(fn):
+        for _ in range(warm):
+            out = fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.mean(ts)), out
+
+    def rec(ms, nbytes, n_in, n_out, host_s=None, host_n=None):
+        r = {"ms": ms, "voxels_in": n_in, "voxels_out": n_out, "algorithmic_bytes": nbytes,
+             "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                          "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+        if host_s is not None:
+            r["oracle"] = {"voxels_per_s": host_n / host_s, "sample_voxels": host_n, "cores": 1,
+                           "kind": "oracle (Python reference)"}
+        return r
+
+    def host_time(fn, *a):
+        t0 = time.perf_counter()
+        fn(*a)
+        return time.perf_counter() - t0
+
+    from oracle import reference as ref
+    sample = 20000
+    ops = {}
+    ms, _ = timed(lambda: sc.submconv_subdivide(pc, pf))
+    ops["subdivide"] = rec(ms, np_ * (16 + c * s_el) + nk * (16 + c * s_el), np_, nk,
+                           host_time(ref.subdivide, parent[:sample], pf_h[:sample]), sample)
+    ms, (uc, _) = timed(lambda: sc.submconv_upsample_masked(pc, pf, mask))
+    nu = uc.shape[0]
+    ops["upsample_masked"] = rec(ms, np_ * (16 + 8 + c * s_el) + nu * (16 + c * s_el), np_, nu,
+                                 host_time(ref.upsample_masked, parent[:sample], pf_h[:sample], mask_h[:sample]),
+                                 sample)
+    kids_h, kf_h = kids.cpu().numpy(), pf_h.repeat(8, axis=0)
+    for mode in ("max", "mean"):
+        ms, (dc, _) = timed(lambda: sc.submconv_downsample(kids, kf, res, 1, mode))
+        nd = dc.shape[0]
+        ops["downsample_" + mode] = rec(ms, nk * (16 + c * s_el) + nd * (16 + c * s_el), nk, nd,
+                                        host_time(ref.downsample, kids_h[:8 * sample], kf_h[:8 * sample], mode),
+                                        8 * sample)
+    ms, (cc, cf, cm) = timed(lambda: sc.submconv_space_to_depth(kids, kf, res, 1))
+    ncs = cc.shape[0]
+    ops["space_to_depth"] = rec(ms, nk * (16 + c * s_el) + ncs * (16 + 8 * c * s_el + 8), nk, ncs)
+    ms, (bc, _) = timed(lambda: sc.submconv_depth_to_space(cc, cf, cm))
+    ops["depth_to_space_masked"] = rec(ms, ncs * (16 + 8 * c * s_el + 8) + bc.shape[0] * (16 + c * s_el), ncs,
+                                       bc.shape[0])
+    total = sum(o["ms"] for o in ops.values())
+    out = {
+        "metric": "sparse helper ops on the 512^3 subdivided shell: total ms (each op's ms and HBM fraction inside)",
+        "value": total, "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": warm, "ms_per_step": total,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "subdiv512_c32_bf16 helpers", "parent_voxels": np_, "voxels": nk, "channels": c,
+                   "upsample_mask": "seeded Bernoulli(0.4) per child slot"},
+        "ops": ops,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,11 +199,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the second dtype and the cold-cache pass")
+    ap.add_argument("--helpers", action="store_true",
+                    help="time the coordinate-set helpers on the 512^3 subdivided shell instead (own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         return 2
+    if args.helpers:
+        return bench_helpers(args)
 
     import numpy as np
     import torch

@@ -221,6 +221,33 @@ int submconv_downsample(const int32_t *coords, const void *feats, int64_t n, int
                         int32_t batch, int32_t mode, int32_t *out_coords, void *out_feats, int64_t *out_m,
                         void *stream);
 
+/* Weight layouts of a 3x3x3 kernel. */
+#define SUBMCONV_LAYOUT_UNKNOWN (-1)
+#define SUBMCONV_LAYOUT_KRSC 0  /* [Cout, kz, ky, kx, Cin] (spconv; what the forward takes) */
+#define SUBMCONV_LAYOUT_OIDHW 1 /* [Cout, Cin, kz, ky, kx] (torch Conv3d) */
+
+/*
+ * Which layout a 5-D weight shape is (lato.2_mrp_mlx working notes, "Key facts": both
+ * layouts are 5-D, so the rank decides nothing).  Host only, no device work.
+ *   shape  : host int64 [5].
+ *   hint   : SUBMCONV_LAYOUT_UNKNOWN, or the layout the caller's module implies
+ *            (a sparse conv module: KRSC; a dense nn.Conv3d: OIDHW).
+ *   layout : host, receives SUBMCONV_LAYOUT_KRSC or SUBMCONV_LAYOUT_OIDHW.
+ * E_UNSUPPORTED when neither reading is a 3x3x3 kernel; E_INVALID_ARG when the shape
+ * fits both ([O,3,3,3,3]) and no hint is given, or the hint contradicts the shape.
+ */
+int submconv_classify_5d(const int64_t *shape, int32_t hint, int32_t *layout);
+
+/*
+ * KRSC weights from either layout, optionally mirrored (flip != 0: tap k of dst is
+ * tap 26 - k of src, the kernel the forward's flip option stands for; same page,
+ * "Unresolved").  src device [cout,3,3,3,cin] (KRSC) or [cout,cin,3,3,3] (OIDHW) of
+ * dtype; dst device KRSC [cout,3,3,3,cin], must not overlap src (E_ALIAS).
+ * Asynchronous on `stream`.
+ */
+int submconv_weight_convert(const void *src, int32_t layout, int32_t cout, int32_t cin, int32_t dtype, int32_t flip,
+                            void *dst, void *stream);
+
 /* Name of a status code (static string). */
 const char *submconv_status_string(int status);
 

@@ -99,6 +99,18 @@ def weight_tap(weight: np.ndarray, k: int, flip: bool) -> np.ndarray:
     return weight[:, dz + 1, dy + 1, dx + 1, :]
 
 
+def conv3d_to_krsc(weight: np.ndarray) -> np.ndarray:
+    """A torch Conv3d weight [Cout, Cin, kz, ky, kx] as KRSC [Cout, kz, ky, kx, Cin]
+    (lato.2_mrp_mlx working notes, "Key facts": both layouts are 5-D)."""
+    return np.ascontiguousarray(np.transpose(np.asarray(weight), (0, 2, 3, 4, 1)))
+
+
+def mirror_krsc(weight: np.ndarray) -> np.ndarray:
+    """The mirrored KRSC kernel W'[o, kz, ky, kx, c] = W[o, 2-kz, 2-ky, 2-kx, c] (tap k -> 26 - k),
+    the weights the flip option stands for (same page, "Unresolved")."""
+    return np.ascontiguousarray(np.asarray(weight)[:, ::-1, ::-1, ::-1, :])
+
+
 def forward(feats: np.ndarray, weight: np.ndarray, bias, nbr: np.ndarray, flip: bool = False) -> np.ndarray:
     """out[i] = bias + sum over present taps k of W_k @ feats[nbr[i,k]], in float64.
 

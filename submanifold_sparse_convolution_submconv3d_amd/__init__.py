@@ -17,6 +17,9 @@ Functions carry the C names:
     submconv_depth_to_space(coarse, feats8c, mask=None) -> (coords, feats)
     submconv_upsample_masked(coords, feats, mask)   -> (coords, feats)
     submconv_downsample(coords, feats, res, batch, mode) -> (coarse, feats)
+    classify_5d(shape, hint=None)                   -> "krsc" | "oidhw"
+    weight_to_krsc(weight, layout=None, hint=None, flip=False) -> KRSC weight
+    flip_ab(feats, weight, bias, rb)                -> {"corr": out, "conv": out} for an A/B
 
 `RulebookCache` keeps one rulebook per coordinate set, keyed like the
 upstream library's indice_key, so every convolution on a set reuses its map
@@ -34,7 +37,7 @@ __all__ = [
     "SubmconvError", "Rulebook", "RulebookCache", "lib_path", "load_library",
     "submconv_build_map", "submconv_forward", "submconv_subdivide",
     "submconv_space_to_depth", "submconv_depth_to_space", "submconv_upsample_masked", "submconv_downsample",
-    "POOL_MAX", "POOL_MEAN",
+    "POOL_MAX", "POOL_MEAN", "classify_5d", "weight_to_krsc", "flip_ab",
     "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA", "KERNEL_WINDOW", "KERNEL_PERSISTENT",
 ]
 
@@ -83,6 +86,8 @@ def load_library():
         "submconv_depth_to_space": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
         "submconv_upsample_masked": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
         "submconv_downsample": [vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64p, vp],
+        "submconv_classify_5d": [i64p, i32, i32p],
+        "submconv_weight_convert": [vp, i32, i32, i32, i32, i32, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -352,3 +357,47 @@ def submconv_downsample(coords: torch.Tensor, feats: torch.Tensor, res: int, bat
             ctypes.c_void_p(out_f.data_ptr()), ctypes.byref(m), _stream(coords.device)), "submconv_downsample")
     k = m.value
     return out_c[:k], out_f[:k]
+
+
+_LAYOUTS = {"krsc": 0, "oidhw": 1}
+
+
+def classify_5d(shape, hint: Optional[str] = None) -> str:
+    """"krsc" ([O,kz,ky,kx,I], spconv) or "oidhw" ([O,I,kz,ky,kx], torch Conv3d) for a
+    5-D 3x3x3 weight shape; `hint` is the layout the caller's module implies, needed
+    when the shape fits both ([O,3,3,3,3])."""
+    if len(shape) != 5:
+        raise ValueError("a 5-D weight shape is expected")
+    arr = (ctypes.c_int64 * 5)(*[int(d) for d in shape])
+    out = ctypes.c_int32(-1)
+    h = -1 if hint is None else _LAYOUTS[hint]
+    _check(load_library().submconv_classify_5d(arr, h, ctypes.byref(out)), "submconv_classify_5d")
+    return "krsc" if out.value == 0 else "oidhw"
+
+
+def weight_to_krsc(weight: torch.Tensor, layout: Optional[str] = None, hint: Optional[str] = None,
+                   flip: bool = False) -> torch.Tensor:
+    """KRSC copy of a 3x3x3 weight in either layout (classified from its shape when
+    `layout` is None), mirrored (tap k -> 26 - k) when `flip`."""
+    _dev(weight, "weight")
+    if weight.dim() != 5:
+        raise ValueError("a 5-D weight is expected")
+    layout = layout or classify_5d(tuple(weight.shape), hint)
+    if layout == "krsc":
+        cout, cin = weight.shape[0], weight.shape[4]
+    else:
+        cout, cin = weight.shape[0], weight.shape[1]
+    out = torch.empty((cout, 3, 3, 3, cin), dtype=weight.dtype, device=weight.device)
+    with torch.cuda.device(weight.device):
+        _check(load_library().submconv_weight_convert(
+            ctypes.c_void_p(weight.data_ptr()), _LAYOUTS[layout], cout, cin, _dtype_code(weight), int(bool(flip)),
+            ctypes.c_void_p(out.data_ptr()), _stream(weight.device)), "submconv_weight_convert")
+    return out
+
+
+def flip_ab(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], rb: "Rulebook") -> dict:
+    """Both kernel orientations on the same input, for an end-to-end A/B (the caller
+    compares them downstream): "corr" reads feats[c + d] (flip 0), "conv" feats[c - d]
+    (flip 1, the mirrored kernel)."""
+    return {"corr": submconv_forward(feats, weight, bias, rb, flip=False),
+            "conv": submconv_forward(feats, weight, bias, rb, flip=True)}

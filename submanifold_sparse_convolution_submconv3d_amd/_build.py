@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libsubmconv.so")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["api.hip", "sort_scan.hip", "mapbuild.hip", "conv.hip", "conv_win.hip", "conv_big.hip", "helpers.hip"]
+SOURCES = ["api.hip", "sort_scan.hip", "mapbuild.hip", "conv.hip", "conv_win.hip", "conv_big.hip", "helpers.hip", "weights.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

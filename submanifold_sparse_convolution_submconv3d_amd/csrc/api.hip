@@ -25,6 +25,8 @@ int upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mas
                     int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
 int downsample(const int32_t *coords, const void *feats, int64_t n, int c, int dtype, int res, int batch,
                int mean, int32_t *out_coords, void *out_feats, int64_t *out_m, hipStream_t s);
+int classify_5d(const int64_t *shape, int hint, int *layout);
+int weight_convert(const void *src, int layout, int cout, int cin, int dtype, int flip, void *dst, hipStream_t s);
 
 static thread_local char g_err[512];
 
@@ -355,6 +357,29 @@ int submconv_downsample(const int32_t *coords, const void *feats, int64_t n, int
         return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
     return downsample(coords, feats, n, c, dtype, res, batch, mode == SUBMCONV_POOL_MEAN, out_coords, out_feats,
                       out_m, (hipStream_t)stream);
+}
+
+int submconv_classify_5d(const int64_t *shape, int32_t hint, int32_t *layout)
+{
+    if (!shape || !layout) return fail(SUBMCONV_E_INVALID_ARG, "NULL pointer");
+    int l = SUBMCONV_LAYOUT_UNKNOWN;
+    const int status = classify_5d(shape, hint, &l);
+    *layout = l;
+    return status;
+}
+
+int submconv_weight_convert(const void *src, int32_t layout, int32_t cout, int32_t cin, int32_t dtype, int32_t flip,
+                            void *dst, void *stream)
+{
+    if (layout != SUBMCONV_LAYOUT_KRSC && layout != SUBMCONV_LAYOUT_OIDHW)
+        return fail(SUBMCONV_E_INVALID_ARG, "layout %d", layout);
+    if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
+    if (cout < 1 || cin < 1 || (int64_t)cout * cin > (int64_t(1) << 24))
+        return fail(SUBMCONV_E_INVALID_ARG, "cout = %d, cin = %d", cout, cin);
+    if (!src || !dst) return fail(SUBMCONV_E_INVALID_ARG, "NULL pointer");
+    const size_t bytes = (size_t)cout * 27 * cin * elem_size(dtype);
+    if (overlaps(dst, bytes, src, bytes)) return fail(SUBMCONV_E_ALIAS, "dst overlaps src");
+    return weight_convert(src, layout, cout, cin, dtype, flip, dst, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -37,10 +37,11 @@ __global__ __launch_bounds__(256) void k_subdivide_coords(const int4 *__restrict
     out[e] = make_int4(c.x, 2 * c.y + (q >> 2), 2 * c.z + ((q >> 1) & 1), 2 * c.w + (q & 1));
 }
 
-// Copy each parent row to its 8 children, in 4-byte words (rows are whole words).
-__global__ __launch_bounds__(256) void k_subdivide_feats(const uint32_t *__restrict__ in,
-                                                         int64_t n, int words,
-                                                         uint32_t *__restrict__ out)
+// Copy each parent row to its 8 children in units V (16-byte vectors or 4-byte words;
+// rows are whole units).
+template <typename V>
+__global__ __launch_bounds__(256) void k_subdivide_feats(const V *__restrict__ in, int64_t n, int words,
+                                                         V *__restrict__ out)
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over 8n rows x words
     if (e >= 8 * n * words) return;
@@ -71,10 +72,15 @@ int subdivide(const int32_t *coords, const void *feats, int64_t n, int c, int dt
     SC_LAUNCHED("subdivide_coords");
     if (feats) {
         const int64_t row_bytes = (int64_t)c * (dtype == SUBMCONV_F32 ? 4 : 2);
-        if (row_bytes % 4 == 0) {
+        if (row_bytes % 16 == 0 && ((uintptr_t)feats & 15) == 0 && ((uintptr_t)out_feats & 15) == 0) {
+            const int vecs = (int)(row_bytes / 16);
+            const int64_t total = kids * vecs;
+            hipLaunchKernelGGL(k_subdivide_feats<uint4>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                               s, (const uint4 *)feats, n, vecs, (uint4 *)out_feats);
+        } else if (row_bytes % 4 == 0) {
             const int words = (int)(row_bytes / 4);
             const int64_t total = kids * words;
-            hipLaunchKernelGGL(k_subdivide_feats, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+            hipLaunchKernelGGL(k_subdivide_feats<uint32_t>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                                s, (const uint32_t *)feats, n, words, (uint32_t *)out_feats);
         } else {
             const int64_t total = kids * c;

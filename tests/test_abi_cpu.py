@@ -117,6 +117,32 @@ def test_empty_inputs_are_no_ops(lib):
     assert m.value == 0
 
 
+def test_classify_5d(lib):
+    """Host-only: the layout of a 5-D 3x3x3 weight shape, and the ambiguous [O,3,3,3,3]."""
+    def cls(shape, hint=-1):
+        arr = (ctypes.c_int64 * 5)(*shape)
+        out = ctypes.c_int32(-9)
+        return lib.submconv_classify_5d(arr, hint, ctypes.byref(out)), out.value
+    assert cls((64, 3, 3, 3, 32)) == (0, 0)          # KRSC
+    assert cls((64, 32, 3, 3, 3)) == (0, 1)          # Conv3d
+    assert cls((64, 3, 3, 3, 32), 0) == (0, 0)
+    assert cls((64, 3, 3, 3, 3))[0] == E_INVALID_ARG  # fits both: needs the module's hint
+    assert cls((64, 3, 3, 3, 3), 1) == (0, 1)
+    assert cls((64, 3, 3, 3, 3), 0) == (0, 0)
+    assert cls((64, 3, 3, 3, 32), 1)[0] == E_INVALID_ARG  # hint contradicts the shape
+    assert cls((64, 5, 5, 5, 32))[0] == E_UNSUPPORTED
+    assert cls((64, 0, 3, 3, 3))[0] == E_INVALID_ARG
+    assert cls((64, 3, 3, 3, 32), 7)[0] == E_INVALID_ARG
+    assert sc.classify_5d((16, 8, 3, 3, 3)) == "oidhw"
+    assert sc.classify_5d((16, 3, 3, 3, 3), hint="krsc") == "krsc"
+    with pytest.raises(sc.SubmconvError):
+        sc.classify_5d((16, 3, 3, 3, 3))
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.submconv_weight_convert(fake, 2, 4, 4, 0, 0, fake, None) == E_INVALID_ARG
+    assert lib.submconv_weight_convert(fake, 0, 4, 4, 5, 0, fake, None) == E_UNSUPPORTED
+    assert lib.submconv_weight_convert(fake, 0, 4, 4, 0, 0, fake, None) == E_ALIAS
+
+
 def test_binding_requires_device_tensors():
     with pytest.raises(TypeError):
         sc.submconv_build_map(torch.zeros((3, 4), dtype=torch.int32), 16, 1)

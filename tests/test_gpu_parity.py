@@ -378,11 +378,12 @@ def test_rulebook_cache_reuse():
 # ---------------------------------------------------------------- helpers
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_subdivide(dtype):
+@pytest.mark.parametrize("ch", [6, 32])
+def test_subdivide(dtype, ch):
     c = synth.random_coords(777, 16, 2, 4)
-    feats, _, _ = synth.make_values(777, 6, 1, 4)
-    tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, 6), np.float32), None, dtype)
-    note("subdivide %s" % dtype)
+    feats, _, _ = synth.make_values(777, ch, 1, 4)
+    tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, ch), np.float32), None, dtype)
+    note("subdivide %s c=%d" % (dtype, ch))
     kc, kf = sc.submconv_subdivide(coords_dev(c), tf)
     ec, ef = ref.subdivide(c, f64)
     np.testing.assert_array_equal(kc.cpu().numpy(), ec)
@@ -477,6 +478,43 @@ def test_downsample_errors():
     assert e.value.status == -2
     with pytest.raises(ValueError):
         sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1]], np.int32)), f[:1], 4, 1, "sum")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("flip", [False, True])
+def test_weight_convert(dtype, flip):
+    """Conv3d [O,I,kz,ky,kx] and KRSC weights to KRSC, optionally mirrored: a copy, so
+    bit-exact against the oracle's layout definitions."""
+    rng = np.random.default_rng(61)
+    wc = rng.standard_normal((16, 8, 3, 3, 3)).astype(np.float32)
+    krsc = ref.conv3d_to_krsc(wc)
+    note("weight_convert %s flip=%d" % (dtype, flip))
+    for src, layout in ((wc, "oidhw"), (krsc, "krsc")):
+        if dtype == "f32":
+            t = torch.from_numpy(np.ascontiguousarray(src)).to(DEV)
+        else:
+            t = torch.from_numpy(synth.bf16_bits(np.ascontiguousarray(src)).view(np.int16)).view(torch.bfloat16).to(DEV)
+        got = sc.weight_to_krsc(t, layout=layout if layout == "krsc" else None, flip=flip)
+        expect = ref.mirror_krsc(krsc) if flip else krsc
+        if dtype == "bf16":
+            expect = synth.bf16_to_f32(synth.bf16_bits(expect))
+        np.testing.assert_array_equal(got.float().cpu().numpy(), expect)
+
+
+def test_flip_ab_orientations():
+    """flip_ab's two outputs are the oracle's correlation and convolution forwards, and
+    the convolution one equals the correlation forward with the mirrored weights."""
+    w, c = synth.workload(1)
+    feats, weight, bias = synth.make_values(len(c), 16, 16, 71)
+    tf, tw, tb, f64, w64 = device_values(feats, weight, bias, "f32")
+    note("flip_ab workload 1")
+    rb = build(c, w.res, 1)
+    ab = sc.flip_ab(tf, tw, tb, rb)
+    nbr = dense.neighbor_table(c, w.res, 1)
+    assert_close(to_f64(ab["corr"]), ref.forward(f64, w64, bias, nbr, flip=False), "f32", "corr")
+    assert_close(to_f64(ab["conv"]), ref.forward(f64, w64, bias, nbr, flip=True), "f32", "conv")
+    mirrored = sc.submconv_forward(tf, sc.weight_to_krsc(tw, layout="krsc", flip=True), tb, rb)
+    assert_close(to_f64(mirrored), to_f64(ab["conv"]), "f32", "mirror vs flip")
 
 
 def test_rulebook_neighbors_pointer_matches_copy():

@@ -87,3 +87,21 @@ def _drop_tap(feats, weight, bias, nbr, flip=False):
 def test_planted_mistake_is_caught(monkeypatch, name, attr, impl):
     monkeypatch.setattr(ref, attr, impl)
     assert not _pins_pass(), name
+
+
+@pytest.mark.parametrize("perm", [(0, 4, 3, 2, 1), (0, 3, 2, 4, 1), (0, 2, 4, 3, 1)])
+def test_weight_layout_mutations_are_caught(monkeypatch, perm):
+    """A Conv3d -> KRSC conversion with two kernel axes swapped keeps every shape valid;
+    the dense conv3d pin must reject it."""
+    import test_oracle_pins as pins
+    monkeypatch.setattr(ref, "conv3d_to_krsc", lambda w: np.ascontiguousarray(np.transpose(np.asarray(w), perm)))
+    with pytest.raises(AssertionError):
+        pins.test_weight_layouts_against_dense_conv3d()
+
+
+def test_partial_mirror_is_caught(monkeypatch):
+    """A mirror over two of the three kernel axes must fail the mirror pin."""
+    import test_oracle_pins as pins
+    monkeypatch.setattr(ref, "mirror_krsc", lambda w: np.ascontiguousarray(np.asarray(w)[:, ::-1, ::-1, :, :]))
+    with pytest.raises(AssertionError):
+        pins.test_weight_layouts_against_dense_conv3d()

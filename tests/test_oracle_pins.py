@@ -234,6 +234,33 @@ def test_i9_flip_consistency():
     np.testing.assert_allclose(dense.forward(feats, weight, bias, nbr, flip=True), b, rtol=1e-13, atol=1e-13)
 
 
+def test_weight_layouts_against_dense_conv3d():
+    """conv3d_to_krsc: a torch Conv3d weight [O, I, kz, ky, kx], converted, drives the
+    oracle forward to torch's conv3d with the unconverted weight (library routine).
+    mirror_krsc: tap k of the mirror is tap 26 - k, and it is torch.flip of the
+    Conv3d weight over the three kernel axes, converted."""
+    coords = random_set(500, 9, 1, 51)
+    n = len(coords)
+    rng = np.random.default_rng(51)
+    feats = rng.standard_normal((n, 5))
+    wc = rng.standard_normal((4, 5, 3, 3, 3))
+    krsc = ref.conv3d_to_krsc(wc)
+    assert krsc.shape == (4, 3, 3, 3, 5)
+    c = torch.from_numpy(coords.astype(np.int64))
+    vol = torch.zeros((1, 5, 9, 9, 9), dtype=torch.float64)
+    vol[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]] = torch.from_numpy(feats)
+    dense_out = torch.nn.functional.conv3d(vol, torch.from_numpy(wc), None, padding=1)
+    expect = dense_out[c[:, 0], :, c[:, 1], c[:, 2], c[:, 3]].numpy()
+    nbr = ref.neighbor_table(coords, 9, 1)
+    np.testing.assert_allclose(ref.forward(feats, krsc, None, nbr), expect, rtol=1e-12, atol=1e-12)
+    mirror = ref.mirror_krsc(krsc)
+    for k in range(27):
+        np.testing.assert_array_equal(ref.weight_tap(mirror, k, False), ref.weight_tap(krsc, 26 - k, False))
+    np.testing.assert_array_equal(ref.conv3d_to_krsc(np.flip(wc, (2, 3, 4))), mirror)
+    np.testing.assert_allclose(ref.forward(feats, mirror, None, nbr), ref.forward(feats, krsc, None, nbr, flip=True),
+                               rtol=1e-13, atol=1e-13)
+
+
 def test_i10_equivariances():
     _, coords = synth.workload(1)
     n = len(coords)
