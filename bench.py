@@ -187,6 +187,100 @@ def bench_helpers(args):
     return 0
 
 
+def bench_chain(args):
+    """A decoder-like chain on one GPU: per level, build the map of the level's set, run
+    its SubMConv3d layers on that one map, then subdivide (features replicated) into the
+    next level; 64^3 -> 512^3, 18 layers, bf16.  Reports the whole chain's time, the
+    share of it spent building maps, and the layers' throughput (voxel-layers/s and
+    algorithmic TFLOP/s over present taps)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import submanifold_sparse_convolution_submconv3d_amd as sc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sc.load_library()
+    levels = synth.CHAIN_LEVELS
+    c0 = synth.chain_start(levels[0][0])
+    feats, layers = synth.chain_values(levels, len(c0))
+
+    def bf(a):
+        return torch.from_numpy(synth.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0, coords0 = bf(feats), torch.from_numpy(c0).to(dev)
+    dw = [(li, bf(w), torch.from_numpy(b).to(dev)) for li, w, b in layers]
+    stream = torch.cuda.current_stream()
+
+    def chain(record):
+        coords, x = coords0, x0
+        ev = []
+        info = []
+        for li, (res, ch, convs) in enumerate(levels):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            rb = sc.submconv_build_map(coords, res, 1)
+            e[1].record(stream)
+            for lj, w, b in dw:
+                if lj == li:
+                    x = sc.submconv_forward(x, w, b, rb)
+            e[2].record(stream)
+            n, p = rb.n, rb.taps_present
+            rb.free()
+            if li + 1 < len(levels):
+                coords, x = sc.submconv_subdivide(coords, x)
+            e[3].record(stream)
+            ev.append(e)
+            info.append((n, p))
+        torch.cuda.synchronize()
+        if record:
+            return [(e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])) for e in ev], info
+        return None, info
+
+    steps, warm = max(2, args.steps), max(1, args.warmup)
+    for _ in range(warm):
+        chain(False)
+    per = []
+    wall = 0.0
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        t, info = chain(True)
+        wall += time.perf_counter() - t0
+        per.append(t)
+    per = np.array(per)  # steps x levels x (map, convs, subdivide)
+    mean = per.mean(axis=0)
+    total = float(mean.sum())
+    vl, flops, lv = 0.0, 0.0, []
+    cin = levels[0][1]
+    for li, (res, ch, convs) in enumerate(levels):
+        n, p = info[li]
+        fl = 0.0
+        for j in range(convs):
+            fl += 2.0 * cin * ch * p
+            cin = ch
+        vl += n * convs
+        flops += fl
+        lv.append({"grid": "%d^3" % res, "voxels": n, "taps_present": p, "channels": ch, "convs": convs,
+                   "map_build_ms": float(mean[li, 0]), "convs_ms": float(mean[li, 1]),
+                   "subdivide_ms": float(mean[li, 2]), "conv_tflops": fl / (mean[li, 1] * 1e-3) / 1e12})
+    conv_ms = float(mean[:, 1].sum())
+    out = {
+        "metric": "decoder-like chain 64^3 -> 512^3 (18 SubMConv3d, bf16): voxel-layers/s over the whole chain",
+        "value": vl / (total * 1e-3), "unit": "voxel-layers/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": total, "host_ms_per_step": wall * 1e3 / steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "chain64to512_bf16", "levels": [list(l) for l in levels], "start_voxels": len(c0),
+                   "weights": "LeCun-normal, seeded"},
+        "chain_ms": total, "convs_ms": conv_ms, "map_build_ms": float(mean[:, 0].sum()),
+        "subdivide_ms": float(mean[:, 2].sum()), "map_build_share": float(mean[:, 0].sum()) / total,
+        "conv_tflops": flops / (conv_ms * 1e-3) / 1e12, "chain_tflops": flops / (total * 1e-3) / 1e12,
+        "levels": lv,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +293,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the second dtype and the cold-cache pass")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the decoder-like chain 64^3 -> 512^3 (18 convolutions) instead (own JSON line)")
     ap.add_argument("--helpers", action="store_true",
                     help="time the coordinate-set helpers on the 512^3 subdivided shell instead (own JSON line)")
     args = ap.parse_args()
@@ -208,6 +304,8 @@ def main():
         return 2
     if args.helpers:
         return bench_helpers(args)
+    if args.chain:
+        return bench_chain(args)
 
     import numpy as np
     import torch

@@ -248,6 +248,15 @@ int submconv_classify_5d(const int64_t *shape, int32_t hint, int32_t *layout);
 int submconv_weight_convert(const void *src, int32_t layout, int32_t cout, int32_t cin, int32_t dtype, int32_t flip,
                             void *dst, void *stream);
 
+/*
+ * The library keeps device blocks it has freed (rulebooks, scratch) for reuse on the
+ * same device and stream, up to 16 GiB per device, so that repeated builds make no
+ * driver allocation calls.  This returns the cached blocks of `device` (all devices
+ * when device < 0) to the driver, stream-ordered on the streams they were freed on.
+ * Blocks in use are not affected.
+ */
+int submconv_release_cache(int32_t device);
+
 /* Name of a status code (static string). */
 const char *submconv_status_string(int status);
 

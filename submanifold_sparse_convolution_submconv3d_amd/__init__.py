@@ -37,7 +37,7 @@ __all__ = [
     "SubmconvError", "Rulebook", "RulebookCache", "lib_path", "load_library",
     "submconv_build_map", "submconv_forward", "submconv_subdivide",
     "submconv_space_to_depth", "submconv_depth_to_space", "submconv_upsample_masked", "submconv_downsample",
-    "POOL_MAX", "POOL_MEAN", "classify_5d", "weight_to_krsc", "flip_ab",
+    "POOL_MAX", "POOL_MEAN", "classify_5d", "weight_to_krsc", "flip_ab", "release_cache",
     "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA", "KERNEL_WINDOW", "KERNEL_PERSISTENT",
 ]
 
@@ -87,6 +87,7 @@ def load_library():
         "submconv_upsample_masked": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
         "submconv_downsample": [vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64p, vp],
         "submconv_classify_5d": [i64p, i32, i32p],
+        "submconv_release_cache": [i32],
         "submconv_weight_convert": [vp, i32, i32, i32, i32, i32, vp, vp],
     }
     for name, args in sig.items():
@@ -401,3 +402,8 @@ def flip_ab(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
     (flip 1, the mirrored kernel)."""
     return {"corr": submconv_forward(feats, weight, bias, rb, flip=False),
             "conv": submconv_forward(feats, weight, bias, rb, flip=True)}
+
+
+def release_cache(device: int = -1) -> None:
+    """Return the device blocks the library keeps for reuse (all devices when -1)."""
+    _check(load_library().submconv_release_cache(int(device)), "submconv_release_cache")

@@ -5,6 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
 #include "common.h"
 
 namespace sc {
@@ -50,22 +54,112 @@ int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
     return SUBMCONV_OK;
 }
 
+// Device memory of the library (rulebooks and scratch) comes from a block cache.
+// The driver's stream-ordered allocator costs tens to hundreds of microseconds of
+// host time per call for large blocks, and a map build allocates and frees its
+// scratch every time; so freed blocks are kept, per device and per stream, and handed
+// out again for requests of up to their size and at least half of it.  A block is
+// reused only on the stream it was freed on, which orders its new use after every
+// pending use.  The cache holds at most CACHE_CAP bytes per device beyond that, blocks
+// are returned to the driver; submconv_release_cache empties it.
+namespace {
+struct Cached {
+    void *p;
+    size_t bytes;
+    int device;
+    hipStream_t stream;
+};
+constexpr size_t CACHE_CAP = size_t(16) << 30;
+std::mutex g_cache_mu;
+std::unordered_map<void *, std::pair<size_t, int>> g_live;  // block -> (bytes, device)
+std::vector<Cached> g_free;
+size_t g_cached[64];
+
+size_t size_class(size_t bytes)  // 8 classes per power of two: at most 12.5% slack
+{
+    bytes = (bytes + 255) & ~size_t(255);
+    size_t top = 256;
+    while (top < bytes) top <<= 1;
+    const size_t step = top >= 2048 ? top / 16 : 128;
+    return (bytes + step - 1) / step * step;
+}
+
+void release_cached(int device)  // caller holds g_cache_mu
+{
+    for (size_t i = 0; i < g_free.size();) {
+        if (device < 0 || g_free[i].device == device) {
+            (void)hipFreeAsync(g_free[i].p, g_free[i].stream);
+            if (g_free[i].device >= 0 && g_free[i].device < 64) g_cached[g_free[i].device] -= g_free[i].bytes;
+            g_free[i] = g_free.back();
+            g_free.pop_back();
+        } else {
+            ++i;
+        }
+    }
+}
+}  // namespace
+
 int dev_alloc(void **p, size_t bytes, hipStream_t stream)
 {
     *p = nullptr;
-    if (bytes == 0) bytes = 256;
+    bytes = size_class(bytes == 0 ? 256 : bytes);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SUBMCONV_E_HIP, "hipGetDevice failed");
+    {
+        std::lock_guard<std::mutex> lock(g_cache_mu);
+        size_t best = SIZE_MAX;
+        for (size_t i = 0; i < g_free.size(); ++i) {
+            const Cached &b = g_free[i];
+            if (b.device == dev && b.stream == stream && b.bytes >= bytes && b.bytes / 2 <= bytes &&
+                (best == SIZE_MAX || b.bytes < g_free[best].bytes))
+                best = i;
+        }
+        if (best != SIZE_MAX) {
+            *p = g_free[best].p;
+            g_live[*p] = {g_free[best].bytes, dev};
+            if (dev < 64) g_cached[dev] -= g_free[best].bytes;
+            g_free[best] = g_free.back();
+            g_free.pop_back();
+            return SUBMCONV_OK;
+        }
+    }
     hipError_t e = hipMallocAsync(p, bytes, stream);
+    if (e == hipErrorOutOfMemory) {  // give the cached blocks back and try once more
+        {
+            std::lock_guard<std::mutex> lock(g_cache_mu);
+            release_cached(dev);
+        }
+        (void)hipDeviceSynchronize();
+        e = hipMallocAsync(p, bytes, stream);
+    }
     if (e != hipSuccess) {
         *p = nullptr;
         return fail(e == hipErrorOutOfMemory ? SUBMCONV_E_OOM : SUBMCONV_E_HIP,
                     "device allocation of %zu bytes: %s", bytes, hipGetErrorString(e));
     }
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    g_live[*p] = {bytes, dev};
     return SUBMCONV_OK;
 }
 
 void dev_free(void *p, hipStream_t stream)
 {
-    if (p) (void)hipFreeAsync(p, stream);
+    if (!p) return;
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    auto it = g_live.find(p);
+    if (it == g_live.end()) {  // not from dev_alloc: hand it to the driver
+        (void)hipFreeAsync(p, stream);
+        return;
+    }
+    const size_t bytes = it->second.first;
+    const int dev = it->second.second;
+    g_live.erase(it);
+    if (dev >= 0 && dev < 64 && g_cached[dev] + bytes <= CACHE_CAP) {
+        g_free.push_back({p, bytes, dev, stream});
+        g_cached[dev] += bytes;
+    } else {
+        (void)hipFreeAsync(p, stream);
+    }
 }
 
 // Keep freed pool memory cached (once per device), so repeated builds do not
@@ -380,6 +474,13 @@ int submconv_weight_convert(const void *src, int32_t layout, int32_t cout, int32
     const size_t bytes = (size_t)cout * 27 * cin * elem_size(dtype);
     if (overlaps(dst, bytes, src, bytes)) return fail(SUBMCONV_E_ALIAS, "dst overlaps src");
     return weight_convert(src, layout, cout, cin, dtype, flip, dst, (hipStream_t)stream);
+}
+
+int submconv_release_cache(int32_t device)
+{
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    release_cached(device);
+    return SUBMCONV_OK;
 }
 
 }  // extern "C"

@@ -217,6 +217,38 @@ WORKLOADS = {
 _COORD_CACHE: dict = {}
 
 
+# A decoder-like chain (the pages' V-VAE decoder has 18 sparse conv kernels and grows
+# its set by subdivision): at each level some SubMConv3d layers share one map, then
+# the set is subdivided.  Levels: (grid, channels, convolutions); the first layer of a
+# level maps the previous level's channels to this level's.
+CHAIN_LEVELS = ((64, 128, 4), (128, 64, 4), (256, 32, 4), (512, 32, 6))
+CHAIN_SMALL = ((16, 16, 2), (32, 32, 2), (64, 32, 2))   # the same shape of chain, oracle-sized
+
+
+def chain_start(res: int = 64) -> np.ndarray:
+    """Start set of the chain: a noisy-sphere shell, one voxel thick (6,182 voxels at
+    64^3, 3.17M after three subdivisions, the size of the 512^3 workload); the 16^3
+    thin sphere for the small chain."""
+    if res == 16:
+        return _mask_coords([thin_sphere(16, (8, 8, 8), 6.0)])
+    return _mask_coords([noisy_sphere_shell(res, seed=5, r0=res * 0.27, amp=0.10, fmax=3, r_max=res / 2 - 1,
+                                            t=1)])
+
+
+def chain_values(levels, n0: int, seed: int = 90):
+    """Start features [n0, C0] and per layer (weight KRSC, bias), LeCun-normal weights
+    (std 1/sqrt(27 Cin)) so the scale of the activations stays bounded along the chain."""
+    feats, _, _ = make_values(n0, levels[0][1], 1, seed)
+    layers = []
+    cin = levels[0][1]
+    for li, (_, ch, convs) in enumerate(levels):
+        for j in range(convs):
+            _, w, b = make_values(1, cin, ch, seed + 1 + 16 * li + j, 1.0 / np.sqrt(27 * cin))
+            layers.append((li, w, b))
+            cin = ch
+    return feats, layers
+
+
 def workload(idx: int) -> tuple:
     """(Workload, coords int32 [M,4]); cached per process."""
     w = WORKLOADS[idx]

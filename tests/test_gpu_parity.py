@@ -517,6 +517,66 @@ def test_flip_ab_orientations():
     assert_close(to_f64(mirrored), to_f64(ab["conv"]), "f32", "mirror vs flip")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chain_small(dtype):
+    """The decoder-like chain at oracle size (16^3 -> 64^3, three levels, six layers):
+    per level a map, its layers on that map, then subdivide.  The oracle chain keeps
+    fp64 sums and, for bf16, rounds each layer's output to bf16 as the GPU stores it."""
+    levels = synth.CHAIN_SMALL
+    c0 = synth.chain_start(16)
+    feats, layers = synth.chain_values(levels, len(c0))
+    note("chain %s n0=%d" % (dtype, len(c0)))
+    zero_w = np.zeros((1, 3, 3, 3, feats.shape[1]), np.float32)
+    x, _, _, x64, _ = device_values(feats, zero_w, None, dtype)
+    dev_layers = []
+    for li, w, b in layers:
+        _, tw, tb, _, w64 = device_values(feats[:1, :w.shape[4]], w, b, dtype)
+        dev_layers.append((li, tw, tb, w64, b.astype(np.float64)))
+    coords, cc = coords_dev(c0), c0
+    for li, (res, ch, convs) in enumerate(levels):
+        rb = build(cc, res, 1)
+        nbr = dense.neighbor_table(cc, res, 1)
+        for lj, tw, tb, w64, b64 in dev_layers:
+            if lj != li:
+                continue
+            x = sc.submconv_forward(x, tw, tb, rb)
+            x64 = dense.forward(x64, w64, b64, nbr)
+            if dtype == "bf16":
+                x64 = synth.bf16_to_f32(synth.bf16_bits(x64.astype(np.float32))).astype(np.float64)
+        rb.free()
+        if li + 1 < len(levels):
+            coords, x = sc.submconv_subdivide(coords, x)
+            cc, x64 = ref.subdivide(cc, x64)
+            np.testing.assert_array_equal(coords.cpu().numpy(), cc)
+    assert_close(to_f64(x), x64, dtype, "chain output")
+
+
+def test_block_cache_reuse_across_sizes_and_streams():
+    """Builds that reuse the library's cached blocks (large and small sets in turn, a
+    second stream, after an explicit release) give the same tables as fresh ones."""
+    w2, c2 = synth.workload(2)
+    w1, c1 = synth.workload(1)
+    e2 = dense.neighbor_table(c2, w2.res, 1)
+    e1 = dense.neighbor_table(c1, w1.res, 1)
+    note("block cache")
+    for it in range(3):
+        for c, w, e in ((c2, w2, e2), (c1, w1, e1)):
+            rb = build(c, w.res, 1)
+            np.testing.assert_array_equal(rb.neighbors().cpu().numpy(), e)
+            rb.free()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        rb = sc.submconv_build_map(coords_dev(c2), w2.res, 1)
+        got = rb.neighbors().cpu().numpy()
+        rb.free()
+    side.synchronize()
+    np.testing.assert_array_equal(got, e2)
+    sc.release_cache()
+    rb = build(c1, w1.res, 1)
+    np.testing.assert_array_equal(rb.neighbors().cpu().numpy(), e1)
+    rb.free()
+
+
 def test_rulebook_neighbors_pointer_matches_copy():
     """submconv_rulebook_neighbors builds the input-order table once and hands out
     a device pointer; its bytes equal the copy API's and the oracle's."""
