@@ -246,10 +246,11 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     const size_t kbytes = (((size_t)n * r->key_bytes) + 255) & ~size_t(255);
     const size_t pbytes = (((size_t)n * 4) + 255) & ~size_t(255);
     // +1 KB: kernels copy table rows in 16-byte chunks that may run past the last row
-    const size_t nbytes = ((((size_t)n * 27 * 4) + 255) & ~size_t(255)) + 1024;
+    const size_t nbytes = ((((size_t)n * NBR_INTS * 4) + 255) & ~size_t(255)) + 1024;
     const size_t mbytes = (((size_t)r->ngroups * GWIN_INTS * 4) + 255) & ~size_t(255);
     const size_t lbytes = (size_t)win_plan_ints(n) * 4 + 256;
-    st = dev_alloc(&r->block, kbytes + pbytes + nbytes + mbytes + lbytes, s);
+    r->block_bytes = kbytes + pbytes + nbytes + mbytes + lbytes;
+    st = dev_alloc(&r->block, r->block_bytes, s);
     if (st != SUBMCONV_OK) { delete r; return st; }
     r->keys = r->block;
     r->perm = (int32_t *)((char *)r->block + kbytes);
@@ -289,7 +290,7 @@ int submconv_rulebook_copy_neighbors(const submconv_rulebook *rb, int32_t *dst, 
     if (rb->n == 0) return SUBMCONV_OK;
     if (!dst) return fail(SUBMCONV_E_INVALID_ARG, "dst is NULL");
     const size_t bytes = (size_t)rb->n * 27 * 4;
-    if (overlaps(dst, bytes, rb->block, (size_t)rb->n * 40)) return fail(SUBMCONV_E_ALIAS, "dst overlaps the rulebook");
+    if (overlaps(dst, bytes, rb->block, rb->block_bytes)) return fail(SUBMCONV_E_ALIAS, "dst overlaps the rulebook");
     return input_order_table(rb, dst, (hipStream_t)stream);
 }
 

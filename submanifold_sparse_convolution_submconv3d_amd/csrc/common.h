@@ -171,6 +171,48 @@ __device__ __forceinline__ uint32_t block_incl_scan256(uint32_t v, uint32_t *lds
 constexpr int GWIN_INTS = 18;
 constexpr int32_t GWIN_NONE = 0x7fffffff;
 
+// Neighbour rows of the rulebook, NBR_INTS int32 per sorted voxel.  For a (dz, dy)
+// row d = 3 (dz + 1) + (dy + 1), the voxel's neighbours at x - 1, x, x + 1 are keys
+// adjacent in sorted order, so their sorted positions are consecutive: ints 0-8
+// hold the position of each row's first present cell, int 9 the presence bits
+// (bit 3 d + j: cell x - 1 + j of row d exists).  The neighbour of tap k = 3 d + j
+// sits at first[d] + (present cells of the row before j).  40 bytes per voxel
+// instead of 108 for the 27 positions spelled out.
+constexpr int NBR_INTS = 10;
+
+// Sorted position of tap k's neighbour, or -1.
+__device__ __forceinline__ int32_t nbr_at(const int32_t *row, int k)
+{
+    const int d = k / 3, j = k - 3 * d;
+    const uint32_t m = ((uint32_t)row[9] >> (3 * d)) & 7u;
+    return ((m >> j) & 1u) ? row[d] + (int32_t)__popc(m & ((1u << j) - 1u)) : -1;
+}
+
+// The same from registers: first positions of rows d0 .. d0 + 4 and the presence bits
+// (k compile-time: ALU only).
+template <int D0>
+__device__ __forceinline__ int32_t nbr_at_reg(const int32_t (&first)[5], uint32_t mask, int k)
+{
+    const int d = k / 3, j = k - 3 * d;
+    const uint32_t m = (mask >> (3 * d)) & 7u;
+    return ((m >> j) & 1u) ? first[d - D0] + (int32_t)__popc(m & ((1u << j) - 1u)) : -1;
+}
+
+// The row form of 27 sorted positions (-1 = absent).
+__device__ __forceinline__ void nbr_pack(const int32_t (&p)[27], int32_t (&r)[NBR_INTS])
+{
+    uint32_t mask = 0;
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+        const int32_t a = p[3 * d], b = p[3 * d + 1], c = p[3 * d + 2];
+        r[d] = a >= 0 ? a : (b >= 0 ? b : (c >= 0 ? c : 0));
+        mask |= (a >= 0 ? 1u : 0u) << (3 * d);
+        mask |= (b >= 0 ? 2u : 0u) << (3 * d);
+        mask |= (c >= 0 ? 4u : 0u) << (3 * d);
+    }
+    r[9] = (int32_t)mask;
+}
+
 }  // namespace sc
 
 // Rulebook: library-owned device memory for one coordinate set.  Everything is
@@ -186,9 +228,10 @@ struct submconv_rulebook {
     int64_t taps;       // P: present entries of the table
     int64_t ngroups;    // groups of 32 sorted voxels
     void *block;        // single allocation holding the arrays below
+    size_t block_bytes; // its size
     void *keys;         // sorted keys [n]
     int32_t *perm;      // sorted position -> input row [n]
-    int32_t *nbr_sp;    // [n,27]: sorted position of each neighbour, or -1 (padded allocation)
+    int32_t *nbr_sp;    // [n,NBR_INTS]: neighbour rows by sorted position (see NBR_INTS; padded allocation)
     int32_t *gwin;      // [ngroups,18]: group row windows (see mapbuild.hip)
     int32_t *nbr_in;    // [n,27] input-order table of input rows, built on first request (or null)
     int32_t *plan;      // staging plan of the windowed forward kernel (see conv_win.hip)

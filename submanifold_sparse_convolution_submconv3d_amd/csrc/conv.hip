@@ -6,7 +6,8 @@
 // mirrored kernel), W in KRSC layout [Cout, 27, Cin] (lato.2_mrp_mlx working
 // notes, "Key facts" for the layout, commit summary for the mirror flag).
 // Voxels are visited in sorted order s (the rulebook's order): the output row is
-// perm[s] and the row of neighbour tap k is perm[nbr_sp[s][k]].  For inputs that
+// perm[s] and the row of neighbour tap k is perm[p], p its sorted position from the
+// rulebook's neighbour rows (nbr_at).  For inputs that
 // arrive in grid order perm is the identity; otherwise sorted order still keeps
 // a block's neighbourhoods spatially compact.
 // All kernels are output-stationary: a voxel's output row is accumulated in
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256) void k_conv_generic(const T *__restrict__ feat
     if ((uint64_t)i >= (uint64_t)n) return;
     float acc = 0.f;
     for (int k = 0; k < 27; ++k) {
-        const int32_t p = nbr[s * 27 + k];
+        const int32_t p = nbr_at(nbr + s * NBR_INTS, k);
         if ((uint32_t)p >= (uint64_t)n) continue;
         const int32_t j = perm[p];
         if ((uint32_t)j >= (uint64_t)n) continue;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
         const bool live = (uint64_t)i < (uint64_t)n;
         float acc = 0.f;
         for (int k = 0; k < 27; ++k) {
-            int32_t j = live ? nbr[s * 27 + k] : -1;
+            int32_t j = live ? nbr_at(nbr + s * NBR_INTS, k) : -1;
             j = (uint32_t)j < (uint64_t)n ? perm[j] : -1;
             if ((uint32_t)j >= (uint64_t)n) j = -1;
             float f[PER];
@@ -159,9 +160,9 @@ template <int NVOX>
 __device__ __forceinline__ void stage_nbr(const int32_t *nbr, int64_t n, int64_t v0, char *dst,
                                           int wave, int lane)
 {
-    constexpr int NI = (NVOX * 27 * 4 + 1023) / 1024;
-    const char *base = (const char *)(nbr + v0 * 27);
-    const int64_t left = (n - v0) * 27 * 4;  // valid bytes from base
+    constexpr int NI = (NVOX * NBR_INTS * 4 + 1023) / 1024;
+    const char *base = (const char *)(nbr + v0 * NBR_INTS);
+    const int64_t left = (n - v0) * NBR_INTS * 4;  // valid bytes from base
     for (int i = wave; i < NI; i += 4) {
         const int64_t off = (int64_t)i * 1024 + lane * 16;
         const void *src = off < left ? (const void *)(base + off) : (const void *)g_zero_row;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     using S = MfmaShape<T, CIN, COUT, VT>;
     constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
     __shared__ uint4 sW[S::WBUF][NFRAG * 64];
-    __shared__ __attribute__((aligned(16))) int32_t sN[S::VOX_PER_BLOCK * 27 + 256];
+    __shared__ __attribute__((aligned(16))) int32_t sN[S::VOX_PER_BLOCK * NBR_INTS + 256];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
 #pragma unroll
         for (int t = 0; t < VT; ++t) {
             const int64_t v = vbase + 32 * t + l32;
-            int32_t r = v < n ? sN[(wave * VT * 32 + 32 * t + l32) * 27 + k] : -1;
+            int32_t r = v < n ? nbr_at(sN + (wave * VT * 32 + 32 * t + l32) * NBR_INTS, k) : -1;
             r = (uint32_t)r < (uint64_t)n ? perm[r] : -1;
             if ((uint32_t)r >= (uint64_t)n) r = -1;
             j[t] = r;
@@ -384,7 +385,7 @@ struct RowShape {
     static constexpr bool RESIDENT = 27 * W_TAP <= 65536;
     static constexpr int WBUF = RESIDENT ? 27 : 2;
     static constexpr int VOX_PER_BLOCK = 4 * ROWS;
-    static constexpr int NBR_BYTES = VOX_PER_BLOCK * 27 * 4;
+    static constexpr int NBR_BYTES = VOX_PER_BLOCK * NBR_INTS * 4;
     static constexpr int LDS = WBUF * W_TAP + 4 * ROWS * RB + NBR_BYTES;
     static_assert(RB >= 64 && RB <= 1024 && (RB & (RB - 1)) == 0, "row size");
 };
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     char *sW = lds;                                             // [WBUF][COUT rows][RB]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     char *sF = lds + S::WBUF * S::W_TAP + wave * ROWS * RB;     // this wave's [ROWS][RB]
-    const int32_t *sN = (const int32_t *)(lds + S::WBUF * S::W_TAP + 4 * ROWS * RB);  // [block voxels][27]
+    const int32_t *sN = (const int32_t *)(lds + S::WBUF * S::W_TAP + 4 * ROWS * RB);  // [block voxels][NBR_INTS]
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t blk = xcd_block();
     const int64_t vbase = (blk * 4 + wave) * ROWS;
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     auto gather = [&](int k) -> bool {
         int32_t j = -1;
         if (lane < ROWS && vbase + lane < n) {
-            j = sN[(wave * ROWS + lane) * 27 + k];
+            j = nbr_at(sN + (wave * ROWS + lane) * NBR_INTS, k);
             j = (uint32_t)j < (uint64_t)n ? perm[j] : -1;
             if ((uint32_t)j >= (uint64_t)n) j = -1;
         }

@@ -65,7 +65,7 @@ struct BigShape {
     static constexpr int WCOPY = (WCH + 64 * WAVES - 1) / (64 * WAVES);
     static constexpr int WBUF = WCOPY * 64 * WAVES;  // chunks per buffer (copies past WCH land in padding)
     static constexpr int AHEAD = BIG_AHEAD;        // weight fragments read ahead of their MFMAs
-    static constexpr int TCH = ROUND * 16 * 27 / 4;  // table chunks of a full round
+    static constexpr int TCH = ROUND * 16 * NBR_INTS / 4;  // table chunks of a full round
     static constexpr int TCOPY = (TCH + 64 * WAVES - 1) / (64 * WAVES);
     static_assert(CIN % 32 == 0 && COUT % 16 == 0 && 16 % RT == 0, "tile shape");
     static_assert(CWF * RT <= 16 && CWF * G <= 8, "register budget: 64 accumulators, 32 B-operand VGPRs");
@@ -139,7 +139,7 @@ struct BigCtx {
     // table rows of columns [col, col + ROUND) -> sT
     __device__ __forceinline__ void stage_t(int64_t col) const
     {
-        const int64_t base = col * 16 * 27 / 4;
+        const int64_t base = col * 16 * NBR_INTS / 4;
 #pragma unroll
         for (int c = 0; c < S::TCOPY; ++c) {
             int64_t q = base + (wave + S::WAVES * c) * 64 + lane;
@@ -174,8 +174,13 @@ struct BigCtx {
             ovok[c] = colr < ncols && ov < n;
             ovrow[c] = ovok[c] ? ov : 0;
         }
+        uint32_t gmask[CW];  // presence bits of each column's voxel, read once per round
+#pragma unroll
+        for (int c = 0; c < CW; ++c) gmask[c] = 0;
         auto entry = [&](int k, int c) -> int32_t {
-            const int32_t e = tbl[gvloc[c] * 27 + k];
+            const int d = k / 3, j = k - 3 * d;
+            const uint32_t m = (gmask[c] >> (3 * d)) & 7u;
+            const int32_t e = ((m >> j) & 1u) ? tbl[gvloc[c] * NBR_INTS + d] + (int32_t)__popc(m & ((1u << j) - 1u)) : -1;
             return gvok[c] ? e : -1;
         };
         // perm entry of a sorted position (the buffer load returns 0 for e = -1), and the
@@ -209,6 +214,8 @@ struct BigCtx {
         // prologue: the table block has landed (copied before this round)
         wait_vmcnt<0>();
         big_lds_barrier();
+#pragma unroll
+        for (int c = 0; c < CW; ++c) gmask[c] = (uint32_t)tbl[gvloc[c] * NBR_INTS + 9];
         uint4 wr[S::WCOPY];
         load_w(0, wr);
         int32_t orow[CW], p1[CW], e1[CW], e2[CW];  // perm and entry of tap k+1, entry of tap k+2
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_conv_big(const uint16_t *__restr
 #pragma unroll
         for (int g = 0; g < S::G; ++g) x.aoff[g] = x.s16 * S::ROWCH + ((4 * g) ^ xr);
     }
-    x.tlast = (n * 27 + 3) / 4 - 1;
+    x.tlast = (n * NBR_INTS + 3) / 4 - 1;
     x.rf = __builtin_amdgcn_make_buffer_rsrc((void *)feats, (short)0, (int)(n * CIN * 2), 0x00020000);
     x.rp = __builtin_amdgcn_make_buffer_rsrc((void *)perm, (short)0, (int)(n * 4), 0x00020000);
     x.rw = __builtin_amdgcn_make_buffer_rsrc((void *)w, (short)0, 27 * CIN * COUT * 2, 0x00020000);

@@ -151,13 +151,13 @@ __global__ __launch_bounds__(64) void k_win_plan(const int32_t *__restrict__ gwi
 // ---------------------------------------------------------------------------
 
 constexpr int W32_ROW = 64;                                   // bytes per staged row
-constexpr int W32_TBL = 14 * 1024 + 512;                      // table block (13824 B in whole 1-KB copies)
+constexpr int W32_TBL = 5 * 1024 + 512;                       // neighbour rows of the tile (5120 B)
                                                               // then the tile's 128 sort-order row numbers
-constexpr int W32_PERM = WIN_SLOTS * 64 + 14 * 1024;          // offset of those row numbers
+constexpr int W32_PERM = WIN_SLOTS * 64 + 5 * 1024;           // offset of those row numbers
 constexpr int W32_BUF = WIN_SLOTS * W32_ROW + W32_TBL;        // one buffer
 constexpr int W32_LDS = 2 * W32_BUF;                          // 159744 B, two buffers
 static_assert(W32_LDS <= 160 * 1024, "LDS budget");
-static_assert(WIN_TILE * 27 * 4 <= W32_TBL, "table block");
+static_assert(WIN_TILE * NBR_INTS * 4 + 512 <= W32_TBL, "table block");
 
 __device__ __forceinline__ int w32_chunk_addr(int slot, int chunk)  // byte offset of a row chunk
 {
@@ -232,8 +232,8 @@ __device__ __forceinline__ void w32_copy_table(char *buf, const int32_t *__restr
 {
     const int64_t s0 = tile * WIN_TILE;
     const int64_t cnt = (n - s0) < WIN_TILE ? (n - s0) : WIN_TILE;
-    const int nt = (int)((cnt * 27 * 4 + 1023) >> 10);
-    const char *tb = (const char *)(nbr_sp + s0 * 27);
+    const int nt = (int)((cnt * NBR_INTS * 4 + 1023) >> 10);
+    const char *tb = (const char *)(nbr_sp + s0 * NBR_INTS);
     for (int i = wave; i < nt; i += W32_WAVES)
         __builtin_amdgcn_global_load_lds((gbl_void *)(tb + i * 1024 + lane * 16),
                                          (lds_void *)(buf + WIN_SLOTS * W32_ROW + i * 1024), 16, 0, 0);
@@ -280,20 +280,26 @@ __device__ __forceinline__ void w32_unroll(F &&f)
 
 // Taps K0 .. K0 + NK - 1 of this lane's voxel from the staged rows, with the
 // tile's side work (copies for the next tiles, stores of the previous one)
-// issued between the MFMAs.  e: the voxel's table entries for these taps
-// (sorted positions); delta from the plan; ok: the voxel exists.  Row reads run
+// issued between the MFMAs.  tbl: the voxel's neighbour row in LDS (decoded per
+// tap into a sorted position); delta from the plan; ok: the voxel exists.  Row reads run
 // PF taps ahead of their MFMAs.  Chunk 2 + kh sits at the chunk-kh address XOR
 // 32 (the swizzle flips bit 1 of the position, and 2 + kh = kh ^ 2).
 template <int K0, int NK, typename Side>
-__device__ __forceinline__ void w32_taps_lds(floatx16 &acc, const char *cur, const int (&e)[14], const int (&delta)[9],
+__device__ __forceinline__ void w32_taps_lds(floatx16 &acc, const char *cur, const int32_t *tbl, const int (&delta)[9],
                                              bool ok, int kh, const uint4 (&wf)[14][2], Side &&side)
 {
     constexpr int PF = 1;
+    constexpr int D0 = K0 / 3;  // this tap half's rows are D0 .. D0 + 4
+    int32_t first[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) first[i] = tbl[D0 + i];
+    const uint32_t mask = (uint32_t)tbl[9];
     int addr[NK];
     uint4 b[PF + 1][2];
     auto prep = [&](int j) {
-        int slot = e[j] + delta[(K0 + j) / 3];
-        slot = (ok && e[j] >= 0 && (unsigned)slot < (unsigned)WIN_CAP) ? slot : WIN_CAP;
+        const int32_t e = nbr_at_reg<D0>(first, mask, K0 + j);
+        int slot = e + delta[(K0 + j) / 3];
+        slot = (ok && e >= 0 && (unsigned)slot < (unsigned)WIN_CAP) ? slot : WIN_CAP;
         addr[j] = w32_chunk_addr(slot, kh);
         b[j % (PF + 1)][0] = *(const uint4 *)(cur + addr[j]);
         b[j % (PF + 1)][1] = *(const uint4 *)(cur + (addr[j] ^ 32));
@@ -317,13 +323,14 @@ __device__ __forceinline__ void w32_taps_lds(floatx16 &acc, const char *cur, con
 // the side work goes first.
 template <int K0, int NK, typename Side>
 __device__ __forceinline__ void w32_taps_global(floatx16 &acc, const uint16_t *__restrict__ feats,
-                                                const int32_t *__restrict__ perm, int64_t n, const int (&e)[14],
+                                                const int32_t *__restrict__ perm, int64_t n, const int32_t *tbl,
                                                 bool ok, int kh, const uint4 (&wf)[14][2], Side &&side)
 {
     w32_unroll<0, W32_ITEMS>(side);
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-        const int32_t r = (ok && e[j] >= 0 && e[j] < n) ? perm[e[j]] : -1;
+        const int32_t e = nbr_at(tbl, K0 + j);
+        const int32_t r = (ok && e >= 0 && e < n) ? perm[e] : -1;
         uint4 b0 = make_uint4(0, 0, 0, 0), b1 = b0;
         if ((uint32_t)r < (uint64_t)n) {
             b0 = *(const uint4 *)(feats + (int64_t)r * 32 + 8 * kh);
@@ -443,18 +450,15 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
         // this wave's taps for its 32 voxels
         const int64_t s = tile * WIN_TILE + cb * 32 + col;
         const bool valid = s < n;
-        const int32_t *tbl = (const int32_t *)(cur + WIN_SLOTS * W32_ROW) + (cb * 32 + col) * 27 + 14 * th;
-        int e[14];
-#pragma unroll
-        for (int j = 0; j < 14; ++j) e[j] = (th == 1 && j == 13) ? -1 : tbl[j];
+        const int32_t *tbl = (const int32_t *)(cur + WIN_SLOTS * W32_ROW) + (cb * 32 + col) * NBR_INTS;
         floatx16 acc = {};
         if (R0 >= 0) {
-            if (th == 0) w32_taps_lds<0, 14>(acc, cur, e, delta, valid, kh, wf, side);
-            else w32_taps_lds<14, 13>(acc, cur, e, delta, valid, kh, wf, side);
+            if (th == 0) w32_taps_lds<0, 14>(acc, cur, tbl, delta, valid, kh, wf, side);
+            else w32_taps_lds<14, 13>(acc, cur, tbl, delta, valid, kh, wf, side);
         } else {
             // neighbourhood too wide for the buffer: gather the rows from global memory
-            if (th == 0) w32_taps_global<0, 14>(acc, feats, perm, n, e, valid, kh, wf, side);
-            else w32_taps_global<14, 13>(acc, feats, perm, n, e, valid, kh, wf, side);
+            if (th == 0) w32_taps_global<0, 14>(acc, feats, perm, n, tbl, valid, kh, wf, side);
+            else w32_taps_global<14, 13>(acc, feats, perm, n, tbl, valid, kh, wf, side);
         }
         // combine the two tap halves through LDS (the current rows are no longer read)
         lds_barrier();

@@ -9,7 +9,9 @@
 // What the rulebook keeps, all indexed by sorted position s (C order of
 // (b, z, y, x)):
 //   keys[s], perm[s] (the input row of sorted voxel s),
-//   nbr_sp[s][k]  the SORTED POSITION of the voxel at key[s] + offset(k), or -1,
+//   nbr_sp[s]     the SORTED POSITIONS of the voxels at key[s] + offset(k), in the
+//                 row form of NBR_INTS ints (common.h): per (dz, dy) row the first
+//                 present position and presence bits, 40 bytes instead of 108,
 //   gwin[g]        per group of 32 consecutive sorted voxels and per (dz, dy)
 //                  row: the first and last sorted position the group's
 //                  neighbours in that row occupy.  A kernel merges the windows
@@ -125,7 +127,7 @@ __device__ __forceinline__ void block_finish(const int32_t *s_rows, int count, i
 {
     __syncthreads();
     if (threadIdx.x == 0) blk_taps[blockIdx.x] = *s_taps;
-    for (int e = threadIdx.x; e < count * 27; e += 256) dst[e] = s_rows[e];
+    for (int e = threadIdx.x; e < count * NBR_INTS; e += 256) dst[e] = s_rows[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
                                                     int32_t *__restrict__ gwin,
                                                     uint32_t *__restrict__ blk_taps)
 {
-    __shared__ int32_t s_rows[256 * 27];
+    __shared__ int32_t s_rows[256 * NBR_INTS];
     __shared__ uint32_t s_taps;
     const int tid = threadIdx.x;
     const int64_t s0 = (int64_t)blockIdx.x * 256;
@@ -277,17 +279,20 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
             if (bits & 4u) p[3 * d + 2] = (int32_t)q;
         }
     }
-    if (tid < count) {
-        int32_t *row = s_rows + tid * 27;
 #pragma unroll
-        for (int k = 0; k < 27; ++k) {
-            row[k] = p[k] < n ? p[k] : -1;
-            present += p[k] >= 0 && p[k] < n;
-        }
+    for (int k = 0; k < 27; ++k) {
+        p[k] = p[k] < n ? p[k] : -1;
+        present += p[k] >= 0;
+    }
+    if (tid < count) {
+        int32_t r[NBR_INTS];
+        nbr_pack(p, r);
+#pragma unroll
+        for (int q = 0; q < NBR_INTS; ++q) s_rows[tid * NBR_INTS + q] = r[q];
     }
     if (present) atomicAdd(&s_taps, present);
     group_windows_write(p, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
-    block_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, blk_taps);
+    block_finish(s_rows, count, nbr_sp + s0 * NBR_INTS, &s_taps, blk_taps);
 }
 
 // ---------------------------------------------------------------------------
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
                                                      uint32_t *__restrict__ blk_taps, DevStatus *st)
 {
     __shared__ K s_win[WIN_MAX];
-    __shared__ int32_t s_rows[256 * 27];
+    __shared__ int32_t s_rows[256 * NBR_INTS];
     __shared__ int64_t s_wlo[8], s_whi[8];
     __shared__ uint32_t s_taps;
 
@@ -390,17 +395,17 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
     }
     uint32_t present = 0;
     if (valid) {
-        int32_t *row = s_rows + tid * 27;
+        int32_t r[NBR_INTS];
+        nbr_pack(p, r);
 #pragma unroll
-        for (int k = 0; k < 27; ++k) {
-            row[k] = p[k];
-            present += p[k] >= 0;
-        }
+        for (int q = 0; q < NBR_INTS; ++q) s_rows[tid * NBR_INTS + q] = r[q];
+#pragma unroll
+        for (int k = 0; k < 27; ++k) present += p[k] >= 0;
     }
     if (dup) atomicOr(&st->flags, FLAG_DUPLICATE);
     if (present) atomicAdd(&s_taps, present);
     group_windows_write(p, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
-    block_finish(s_rows, count, nbr_sp + s0 * 27, &s_taps, blk_taps);
+    block_finish(s_rows, count, nbr_sp + s0 * NBR_INTS, &s_taps, blk_taps);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,7 +484,8 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
         perm_out[s] = i;
         const int x = (int)(key[q] & m), y = (int)((key[q] >> rb) & m), z = (int)((key[q] >> (2 * rb)) & m);
         const K bpart = (key[q] >> (3 * rb)) << (3 * rb);
-        int32_t *out = nbr_sp + (int64_t)s * 27;
+        int32_t p[27];
+#pragma unroll
         for (int k = 0; k < 27; ++k) {
             const int nz = z + k / 9 - 1, ny = y + (k / 3) % 3 - 1, nx = x + k % 3 - 1;
             int32_t r = -1;
@@ -489,8 +495,12 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
                 if ((word >> b) & 1u) r = (int32_t)(s_pre[t >> 5] + __popc(word & ((1u << b) - 1u)));
             }
             present += r >= 0;
-            out[k] = r;
+            p[k] = r;
         }
+        int32_t rr[NBR_INTS];
+        nbr_pack(p, rr);
+#pragma unroll
+        for (int q = 0; q < NBR_INTS; ++q) nbr_sp[(int64_t)s * NBR_INTS + q] = rr[q];
     }
     if (present) atomicAdd(&s_taps, present);
     __syncthreads();
@@ -560,7 +570,8 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
         if (s + 1 < n && s_key[s + 1] == key) atomicOr(&st->flags, FLAG_DUPLICATE);
         const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
         const K bpart = (key >> (3 * rb)) << (3 * rb);
-        int32_t *out = nbr_sp + (int64_t)s * 27;
+        int32_t p[27];
+#pragma unroll
         for (int k = 0; k < 27; ++k) {
             const int nz = z + k / 9 - 1, ny = y + (k / 3) % 3 - 1, nx = x + k % 3 - 1;
             int32_t r = -1;
@@ -570,8 +581,12 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
                 if (q < n && s_key[q] == t) r = (int32_t)q;
             }
             present += r >= 0;
-            out[k] = r;
+            p[k] = r;
         }
+        int32_t rr[NBR_INTS];
+        nbr_pack(p, rr);
+#pragma unroll
+        for (int q = 0; q < NBR_INTS; ++q) nbr_sp[(int64_t)s * NBR_INTS + q] = rr[q];
     }
     if (present) atomicAdd(&s_red[0], present);
     __syncthreads();
@@ -586,7 +601,7 @@ __global__ __launch_bounds__(256) void k_group_windows(const int32_t *__restrict
     int32_t p[27];
     const bool valid = s < n;
 #pragma unroll
-    for (int k = 0; k < 27; ++k) p[k] = valid ? nbr_sp[s * 27 + k] : -1;
+    for (int k = 0; k < 27; ++k) p[k] = valid ? nbr_at(nbr_sp + s * NBR_INTS, k) : -1;
     group_windows_write(p, valid, s >> 5, (n + 31) >> 5, gwin);
 }
 
@@ -602,7 +617,7 @@ __global__ __launch_bounds__(256) void k_input_order_table(const int32_t *__rest
     if (e >= n * 27) return;
     const int64_t s = e / 27;
     const int k = (int)(e - s * 27);
-    const int32_t p = nbr_sp[e];
+    const int32_t p = nbr_at(nbr_sp + s * NBR_INTS, k);
     const uint32_t row = (uint32_t)perm[s];
     if (row < (uint64_t)n) out[(int64_t)row * 27 + k] = (p >= 0 && p < n) ? perm[p] : -1;
 }
