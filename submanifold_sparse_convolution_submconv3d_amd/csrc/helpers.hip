@@ -235,8 +235,222 @@ __global__ __launch_bounds__(256) void k_down_reduce(const int32_t *__restrict__
     out_feats[m * c + ci] = Elem<T>::from_f32(MEAN ? acc / (float)cnt : acc);
 }
 
-// Operations of the coarse-grouping pipeline below.
+// Operations of the coarse-grouping pipelines below.
 enum { COARSE_S2D = 0, COARSE_MAX = 1, COARSE_MEAN = 2 };
+
+// ---------------------------------------------------------------------------
+// coarse grouping through an occupancy bitmap (dense coarse key spaces)
+// ---------------------------------------------------------------------------
+// The coarse cells that hold a fine voxel are the set bits of a bitmap over the
+// coarse key space; a cell's rank among them (prefix of the words' popcounts plus
+// the bits below it in its word) is its output row, in ascending key order.  Each
+// fine voxel then writes its row number into its cell's slot of an 8-entry child
+// list, and the output kernels read the children in slot order.  No sort.
+
+constexpr int CG_SLOTS = 2048;  // LDS hash slots per block in the mark (2 x the block's rows)
+
+// Validate, pack the coarse key (all ones for an invalid row) and set its bit; a
+// block first ORs its rows' bits into an LDS hash keyed by bitmap word, so that a
+// word costs one device-scope atomic per block (children of one cell are usually
+// neighbours in the input).
+__global__ __launch_bounds__(256) void k_cg_mark(const int4 *__restrict__ coords, int64_t n, int res, int batch,
+                                                 int rbc, uint32_t *__restrict__ ckey,
+                                                 unsigned long long *__restrict__ bm, DevStatus *st)
+{
+    __shared__ unsigned long long s_word[CG_SLOTS];
+    __shared__ unsigned long long s_bits[CG_SLOTS];
+    for (int i = threadIdx.x; i < CG_SLOTS; i += 256) {
+        s_word[i] = ~0ull;
+        s_bits[i] = 0ull;
+    }
+    __syncthreads();
+    bool bad_any = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t i = (int64_t)blockIdx.x * 1024 + q * 256 + threadIdx.x;
+        if (i >= n) continue;
+        const int4 c = coords[i];
+        const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
+                         (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
+        bad_any |= bad;
+        uint32_t key = ~0u;
+        if (!bad) {
+            key = ((((uint32_t)c.x << rbc | (uint32_t)(c.y >> 1)) << rbc | (uint32_t)(c.z >> 1)) << rbc) |
+                  (uint32_t)(c.w >> 1);
+            const unsigned long long w = key >> 6;
+            uint32_t h = ((uint32_t)w * 0x9E3779B1u) >> (32 - 11);
+            for (;;) {  // linear probing; twice as many slots as rows, so it never fills
+                const unsigned long long prev = atomicCAS(&s_word[h], ~0ull, w);
+                if (prev == ~0ull || prev == w) break;
+                h = (h + 1) & (CG_SLOTS - 1);
+            }
+            atomicOr(&s_bits[h], 1ull << (key & 63));
+        }
+        ckey[i] = key;
+    }
+    if (bad_any) atomicOr(&st->flags, FLAG_RANGE);
+    __syncthreads();
+    for (int i = threadIdx.x; i < CG_SLOTS; i += 256)
+        if (s_word[i] != ~0ull) atomicOr(&bm[s_word[i]], s_bits[i]);
+}
+
+// Child lists of the M coarse rows to -1 (M known on the device only); one row per thread.
+__global__ __launch_bounds__(256) void k_cg_init(int4 *__restrict__ child, const uint32_t *__restrict__ total)
+{
+    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over the capacity, n rows
+    if (m < (int64_t)*total) {
+        child[2 * m] = make_int4(-1, -1, -1, -1);
+        child[2 * m + 1] = make_int4(-1, -1, -1, -1);
+    }
+}
+
+// Row of each fine voxel's cell, its slot in the cell's child list (a second voxel
+// in one slot is a duplicate), and the cell's coordinates (every child writes the
+// same values).
+__global__ __launch_bounds__(256) void k_cg_rank(const uint32_t *__restrict__ ckey, const int4 *__restrict__ coords,
+                                                 int64_t n, int rbc, const unsigned long long *__restrict__ bm,
+                                                 const uint32_t *__restrict__ prefix, int32_t *__restrict__ child,
+                                                 int4 *__restrict__ out_coords, DevStatus *st)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t key = ckey[i];
+    if (key == ~0u) return;
+    const uint32_t w = key >> 6;
+    const int64_t m = (int64_t)prefix[w] + __popcll(bm[w] & ((1ull << (key & 63)) - 1ull));
+    if (m >= n) return;
+    const int4 c = coords[i];
+    const int slot = (c.y & 1) | ((c.z & 1) << 1) | ((c.w & 1) << 2);
+    if (atomicCAS(&child[m * 8 + slot], -1, (int32_t)i) != -1) atomicOr(&st->flags, FLAG_DUPLICATE);
+    const uint32_t msk = (1u << rbc) - 1u;
+    out_coords[m] = make_int4((int)(key >> (3 * rbc)), (int)((key >> (2 * rbc)) & msk), (int)((key >> rbc) & msk),
+                              (int)(key & msk));
+}
+
+// Downsample output: one thread per (coarse row, group of V channels), V = 16 bytes of
+// channels when rows are whole 16-byte vectors, else 1; children in slot order.
+template <typename T, int V, bool MEAN>
+__global__ __launch_bounds__(256) void k_cg_pool(const int32_t *__restrict__ child, const uint32_t *__restrict__ total,
+                                                 int c, const T *__restrict__ feats, T *__restrict__ out_feats)
+{
+    const int groups = c / V;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t m = e / groups;
+    if (m >= (int64_t)*total) return;
+    const int c0 = (int)(e - m * groups) * V;
+    float acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = MEAN ? 0.f : -__builtin_huge_valf();
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int32_t r = child[m * 8 + q];
+        if (r < 0) continue;
+        T x[V];
+        if constexpr (V * sizeof(T) == 16) *(uint4 *)x = *(const uint4 *)(feats + (int64_t)r * c + c0);
+        else x[0] = feats[(int64_t)r * c + c0];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const float f = Elem<T>::to_f32(x[v]);
+            acc[v] = MEAN ? acc[v] + f : fmaxf(acc[v], f);
+        }
+        ++cnt;
+    }
+    T y[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) y[v] = Elem<T>::from_f32(MEAN ? acc[v] / (float)cnt : acc[v]);
+    if constexpr (V * sizeof(T) == 16) *(uint4 *)(out_feats + m * c + c0) = *(const uint4 *)y;
+    else out_feats[m * c + c0] = y[0];
+}
+
+// Space-to-depth output: one thread per (coarse row, slot, unit of a row), units U of
+// 16 bytes when rows are whole vectors, else elements; empty slots zero.
+template <typename U>
+__global__ __launch_bounds__(256) void k_cg_s2d(const int32_t *__restrict__ child, const uint32_t *__restrict__ total,
+                                                int upr, const U *__restrict__ feats, U *__restrict__ out_feats,
+                                                uint8_t *__restrict__ out_mask)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over rows x 8 slots x units per row
+    const int64_t ms = e / upr;
+    const int64_t m = ms >> 3;
+    if (m >= (int64_t)*total) return;
+    const int ui = (int)(e - ms * upr);
+    const int32_t r = child[ms];
+    out_feats[e] = r >= 0 ? feats[(int64_t)r * upr + ui] : U{};
+    if (ui == 0 && out_mask) out_mask[ms] = r >= 0;
+}
+
+template <typename T>
+static int coarse_group_bitmap(const int32_t *coords, const void *feats, int64_t n, int c, int res, int batch,
+                               int rbc, int nbits, int32_t *out_coords, void *out_feats, uint8_t *out_mask,
+                               int64_t *out_m, hipStream_t s, int op)
+{
+    auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+    const int64_t words = nbits > 6 ? (int64_t(1) << (nbits - 6)) : 1;
+    size_t off = 0;
+    const size_t o_bm = off; off += up((size_t)(words + 1) * 8);
+    const size_t o_pre = off; off += up((size_t)words * 4);
+    const size_t o_key = off; off += up((size_t)n * 4);
+    const size_t o_child = off; off += up((size_t)n * 32);
+    const size_t o_scan = off; off += up(scan_scratch_bytes(words));
+    const size_t o_st = off; off += sizeof(DevStatus);
+    char *sc = nullptr;
+    SC_CHECK(dev_alloc((void **)&sc, off, s));
+    unsigned long long *bm = (unsigned long long *)(sc + o_bm);
+    uint32_t *pre = (uint32_t *)(sc + o_pre), *ckey = (uint32_t *)(sc + o_key);
+    int32_t *child = (int32_t *)(sc + o_child);
+    DevStatus *st = (DevStatus *)(sc + o_st);
+    uint32_t *total = (uint32_t *)&st->count;
+    int status = SUBMCONV_OK;
+    do {
+        if (hipMemsetAsync(bm, 0, (size_t)(words + 1) * 8, s) != hipSuccess ||
+            hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) {
+            status = fail(SUBMCONV_E_HIP, "clear failed");
+            break;
+        }
+        hipLaunchKernelGGL(k_cg_mark, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s, (const int4 *)coords, n, res,
+                           batch, rbc, ckey, bm, st);
+        if ((status = exclusive_scan_u32((const uint32_t *)bm, pre, words, total, sc + o_scan, s, SCAN_POPC64, true)) !=
+            SUBMCONV_OK)
+            break;
+        hipLaunchKernelGGL(k_cg_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (int4 *)child, total);
+        hipLaunchKernelGGL(k_cg_rank, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ckey, (const int4 *)coords, n,
+                           rbc, bm, pre, child, (int4 *)out_coords, st);
+        constexpr int V = 16 / sizeof(T);  // elements of a 16-byte vector
+        const bool vec = (c * sizeof(T)) % 16 == 0 && ((uintptr_t)feats & 15) == 0 && ((uintptr_t)out_feats & 15) == 0;
+        if (op == COARSE_S2D) {
+            if (vec)
+                hipLaunchKernelGGL(k_cg_s2d<uint4>, dim3((unsigned)((n * 8 * (c / V) + 255) / 256)), dim3(256), 0, s,
+                                   child, total, c / V, (const uint4 *)feats, (uint4 *)out_feats, out_mask);
+            else
+                hipLaunchKernelGGL(k_cg_s2d<T>, dim3((unsigned)((n * 8 * c + 255) / 256)), dim3(256), 0, s, child, total,
+                                   c, (const T *)feats, (T *)out_feats, out_mask);
+        } else {
+            const int gv = vec ? V : 1;
+            const unsigned grid = (unsigned)((n * (c / gv) + 255) / 256);
+            if (vec && op == COARSE_MEAN)
+                hipLaunchKernelGGL((k_cg_pool<T, V, true>), dim3(grid), dim3(256), 0, s, child, total, c, (const T *)feats,
+                                   (T *)out_feats);
+            else if (vec)
+                hipLaunchKernelGGL((k_cg_pool<T, V, false>), dim3(grid), dim3(256), 0, s, child, total, c,
+                                   (const T *)feats, (T *)out_feats);
+            else if (op == COARSE_MEAN)
+                hipLaunchKernelGGL((k_cg_pool<T, 1, true>), dim3(grid), dim3(256), 0, s, child, total, c, (const T *)feats,
+                                   (T *)out_feats);
+            else
+                hipLaunchKernelGGL((k_cg_pool<T, 1, false>), dim3(grid), dim3(256), 0, s, child, total, c,
+                                   (const T *)feats, (T *)out_feats);
+        }
+        if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in a coarse grouping failed"); break; }
+        DevStatus h;
+        if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
+        if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
+        else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
+        else *out_m = (int64_t)h.count;
+    } while (0);
+    dev_free(sc, s);
+    return status;
+}
 
 template <typename K, typename T>
 static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, int res, int batch,
@@ -316,6 +530,15 @@ static int coarse_group(const int32_t *coords, const void *feats, int64_t n, int
     const int nbits = 3 * rbc + bits_for(batch) + 3;
     if (nbits > 64) return fail(SUBMCONV_E_UNSUPPORTED, "grid and batch need %d key bits (max 64)", nbits);
     const bool k32 = nbits <= 32;
+    // dense coarse key space (the bitmap within a small multiple of the per-voxel data): no sort
+    const int cbits = nbits - 3;
+    if (cbits <= 31 && (int64_t(1) << cbits) / 8 <= 64 * n + (int64_t(4) << 20)) {
+        if (dtype == SUBMCONV_F32)
+            return coarse_group_bitmap<float>(coords, feats, n, c, res, batch, rbc, cbits, out_coords, out_feats,
+                                              out_mask, out_m, s, op);
+        return coarse_group_bitmap<uint16_t>(coords, feats, n, c, res, batch, rbc, cbits, out_coords, out_feats,
+                                             out_mask, out_m, s, op);
+    }
     if (dtype == SUBMCONV_F32)
         return k32 ? s2d_impl<uint32_t, float>(coords, feats, n, c, res, batch, out_coords, out_feats, out_mask, out_m, s, op)
                    : s2d_impl<uint64_t, float>(coords, feats, n, c, res, batch, out_coords, out_feats, out_mask, out_m, s, op);

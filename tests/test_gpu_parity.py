@@ -391,8 +391,9 @@ def test_subdivide(dtype, ch):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n,res,batch", [(1, 2, 1), (900, 12, 2), (5000, 33, 1)])
+@pytest.mark.parametrize("n,res,batch", [(1, 2, 1), (900, 12, 2), (5000, 33, 1), (3000, 2048, 2)])
 def test_space_to_depth_and_back(dtype, n, res, batch):
+    """Dense coarse key spaces group through a bitmap, sparse ones (2048^3) through a sort."""
     c = synth.random_coords(n, res, batch, 8)
     feats, _, _ = synth.make_values(n, 5, 1, 8)
     tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, 5), np.float32), None, dtype)
@@ -449,7 +450,8 @@ def test_upsample_masked(dtype, n, c):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["max", "mean"])
-@pytest.mark.parametrize("n,res,batch,c", [(1, 2, 1, 4), (900, 12, 2, 5), (5000, 33, 1, 32), (60000, 64, 2, 64)])
+@pytest.mark.parametrize("n,res,batch,c", [(1, 2, 1, 4), (900, 12, 2, 5), (5000, 33, 1, 32), (60000, 64, 2, 64),
+                                           (3000, 2048, 2, 8)])
 def test_downsample(dtype, mode, n, res, batch, c):
     """Pooling by 2: coarse coords exact and ascending; max exact; mean within the
     feature tolerance (fp32 sum in slot order vs the oracle's fp64 mean)."""
