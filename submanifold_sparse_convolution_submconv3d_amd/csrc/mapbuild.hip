@@ -119,6 +119,25 @@ __device__ __forceinline__ void group_windows_write(const int32_t (&p)[27], bool
     }
 }
 
+// The same from a packed neighbour row (first positions and presence bits).
+__device__ __forceinline__ void group_windows_write_row(const int32_t (&r)[NBR_INTS], bool valid, int64_t group,
+                                                        int64_t ngroups, int32_t *__restrict__ gwin)
+{
+    const int lane = (int)(threadIdx.x & 63), half = lane >> 5;
+    const bool owner = group < ngroups;
+    int32_t *w = gwin + group * GWIN_INTS;
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+        const uint32_t bits = ((uint32_t)r[9] >> (3 * d)) & 7u;
+        const uint64_t mask = __ballot(valid && bits != 0u);
+        const uint32_t m = (uint32_t)(mask >> (32 * half));
+        const int first = m ? __ffs((int)m) - 1 : 0;
+        const int last = m ? 31 - __clz((int)m) : 0;
+        if (owner && (lane & 31) == first) w[d] = m ? r[d] : GWIN_NONE;
+        if (owner && (lane & 31) == last) w[9 + d] = m ? r[d] + (int32_t)__popc(bits) - 1 : -1;
+    }
+}
+
 // Table rows of one block from LDS to global (a contiguous run) and the block's
 // present count.  Called by every thread after its row of s_rows is written and
 // its count is added to *s_taps.
@@ -224,9 +243,11 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
     const int count = (int)((n - s0) < 256 ? (n - s0) : 256);
     if (tid == 0) s_taps = 0;
     __syncthreads();
-    int32_t p[27];
+    // the packed row (first position per (dz, dy) row, presence bits), built
+    // straight from each row's three occupancy bits and the rank of its first cell
+    int32_t r[NBR_INTS];
 #pragma unroll
-    for (int k = 0; k < 27; ++k) p[k] = -1;
+    for (int q = 0; q < NBR_INTS; ++q) r[q] = 0;
     uint32_t present = 0;
     K key = K(0);
     if (tid < count) key = sk[s0 + tid];
@@ -234,7 +255,7 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
     // a duplicate or an invalid row (the build then reports an error): skip them
     const bool valid = tid < count && key_valid(key, rb, res, batch);
     if (valid) {
-        const int64_t s = s0 + tid;
+        const uint32_t s = (uint32_t)(s0 + tid), un = (uint32_t)n;  // positions fit in 31 bits
         const K m = (K(1) << rb) - 1;
         const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
         const K bpart = (key >> (3 * rb)) << (3 * rb);
@@ -242,56 +263,65 @@ __global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, in
         const uint32_t valid3 = (x > 0 ? 1u : 0u) | 2u | (x + 1 < res ? 4u : 0u);  // cells x-1, x, x+1 on the grid
         const uint32_t shift = x > 0 ? 0u : 1u;                // window bit j <-> cell x-1+j
         // Each row (dz, dy): the occupancy of cells x-1 .. x+1 (3 bits, from one or
-        // two words) and the rank of the row's first cell; the positions of the
-        // present cells follow by adding bits.  All 27 loads are issued without
-        // branching (rows off the grid read word 0 and are masked), so the whole
-        // neighbourhood costs one memory round trip.
-        uint64_t wd[9];
+        // two words) and the rank of the row's first cell; the present cells take
+        // consecutive positions from there.  All loads are issued without branching
+        // (rows off the grid read word 0 and are masked), so the whole neighbourhood
+        // costs one memory round trip.
+        K wd[9];
         uint32_t bsh[9];
         bool rok[9];
 #pragma unroll
         for (int d = 0; d < 9; ++d) {
             const int nz = z + d / 3 - 1, ny = y + d % 3 - 1;
             rok[d] = nz >= 0 && nz < res && ny >= 0 && ny < res;
-            const uint64_t c0 = rok[d] ? (uint64_t)(bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)xs) : 0;
+            const K c0 = rok[d] ? (K)(bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)xs) : K(0);
             wd[d] = c0 >> 6;
             bsh[d] = (uint32_t)(c0 & 63);
         }
-        unsigned long long lo_w[9], hi_w[9];
-        uint32_t pre[9];
+        // Of the next word only the low two bits can fall in the window: load its low
+        // half only (the bitmap has one word of padding).  A 64-bit load whose upper
+        // half is dead lets the compiler reuse that register at once, which makes it
+        // wait for the load there and serialises the round trips.
+        unsigned long long lo_w[9];
+        uint32_t hi_w[9], pre[9];
+        const uint32_t *bm32 = (const uint32_t *)bm;
 #pragma unroll
         for (int d = 0; d < 9; ++d) {
             lo_w[d] = bm[wd[d]];
-            hi_w[d] = bm[wd[d] + 1];  // the bitmap has one word of padding
+            hi_w[d] = bm32[2 * wd[d] + 2];
             pre[d] = prefix[wd[d]] + tsum[wd[d] / SCAN_TILE_ITEMS];
         }
+        uint32_t mask = 0;
 #pragma unroll
         for (int d = 0; d < 9; ++d) {
             const uint32_t b = bsh[d];
             unsigned long long v = lo_w[d] >> b;
-            if (b > 61) v |= hi_w[d] << (64 - b);
-            const uint32_t bits = rok[d] ? (((uint32_t)(v & 7ull) << shift) & valid3) : 0u;
+            if (b > 61) v |= (unsigned long long)hi_w[d] << (64 - b);
+            uint32_t bits = rok[d] ? (((uint32_t)(v & 7ull) << shift) & valid3) : 0u;
             // keys below the row window's first cell (the centre row: the voxel is at s)
-            int64_t q = (d == 4) ? s - (int64_t)(bits & 1u)
-                                 : (int64_t)pre[d] + __popcll(lo_w[d] & ((1ull << b) - 1ull));
-            if (bits & 1u) { p[3 * d] = (int32_t)q; ++q; }
-            if (bits & 2u) { p[3 * d + 1] = (int32_t)q; ++q; }
-            if (bits & 4u) p[3 * d + 2] = (int32_t)q;
-        }
-    }
+            const uint32_t q = (d == 4) ? s - (bits & 1u)
+                                        : pre[d] + (uint32_t)__popcll(lo_w[d] & ((1ull << b) - 1ull));
+            // a cell whose position would be n or more (a set with duplicates or
+            // invalid rows, which the build reports) is dropped
+            if (q + (uint32_t)__popc(bits) > un) {
+                uint32_t keep = q < un ? un - q : 0u, kept = 0;
 #pragma unroll
-    for (int k = 0; k < 27; ++k) {
-        p[k] = p[k] < n ? p[k] : -1;
-        present += p[k] >= 0;
+                for (int j = 0; j < 3; ++j)
+                    if (((bits >> j) & 1u) && keep) { kept |= 1u << j; --keep; }
+                bits = kept;
+            }
+            r[d] = bits ? (int32_t)q : 0;
+            mask |= bits << (3 * d);
+        }
+        r[9] = (int32_t)mask;
+        present = (uint32_t)__popc(mask);
     }
     if (tid < count) {
-        int32_t r[NBR_INTS];
-        nbr_pack(p, r);
 #pragma unroll
         for (int q = 0; q < NBR_INTS; ++q) s_rows[tid * NBR_INTS + q] = r[q];
     }
     if (present) atomicAdd(&s_taps, present);
-    group_windows_write(p, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
+    group_windows_write_row(r, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
     block_finish(s_rows, count, nbr_sp + s0 * NBR_INTS, &s_taps, blk_taps);
 }
 
