@@ -86,7 +86,7 @@ int radix_sort_pairs(K *keys_a, int32_t *vals_a, K *keys_b, int32_t *vals_b, int
 
 // Exclusive scan of n uint32 values (in place allowed), or of the set-bit counts of
 // n 32-bit / 64-bit words; writes the total to *total_dev if non-null.  `scratch`
-// must hold scan_scratch_bytes(n) bytes.
+// must hold scan_scratch_bytes(n) bytes; `in` and `out` must be 16-byte aligned.
 // With add_back false the last pass is skipped: out[i] is then the prefix within
 // i's tile of SCAN_TILE_ITEMS, and the caller adds the tile's offset, which the
 // scan leaves in ((uint32_t *)scratch)[i / SCAN_TILE_ITEMS].

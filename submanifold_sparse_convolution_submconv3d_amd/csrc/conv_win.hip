@@ -59,91 +59,123 @@ constexpr int WIN_SLOTS = 1024;  // row slots per buffer; the last one always ho
 constexpr int WIN_CAP = WIN_SLOTS - 1;
 
 // One thread per tile: union of its groups' row windows, sorted and merged.
-// Straight-line code with compile-time indices (registers only).  When blk_taps
-// is given, the kernel also sums those per-block present counts into st->taps
-// (one device-scope atomic per block of this kernel).
-__global__ __launch_bounds__(64) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
-                                                 int64_t ntiles, int gpt, int cap,
-                                                 int32_t *__restrict__ plan,
-                                                 const uint32_t *__restrict__ blk_taps, int64_t nblk,
-                                                 DevStatus *st)
+// Straight-line code with compile-time indices (registers only).  A block's
+// group windows are read into LDS and its plan records written back from LDS as
+// contiguous runs, so both sides are coalesced.  When blk_taps is given, the
+// kernel also sums those per-block present counts into st->taps (one
+// device-scope atomic per block of this kernel).
+constexpr int PLAN_GPT = WIN_TILE / 32;            // groups per tile
+constexpr int PLAN_BLOCK = 64;                     // tiles per block
+constexpr int PLAN_ROW = PLAN_INTS + 1;            // padded LDS record (no bank conflicts)
+__global__ __launch_bounds__(PLAN_BLOCK) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
+                                                         int64_t ntiles, int cap, int32_t *__restrict__ plan,
+                                                         const uint32_t *__restrict__ blk_taps, int64_t nblk,
+                                                         DevStatus *st)
 {
-    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    __shared__ int32_t s_win[PLAN_BLOCK * PLAN_GPT * GWIN_INTS];  // 18 KB
+    __shared__ int32_t s_plan[PLAN_BLOCK * PLAN_ROW];              // 8.4 KB
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * PLAN_BLOCK, t = t0 + tid;
     if (blk_taps) {
         unsigned long long taps = 0;
-        for (int64_t b = t; b < nblk; b += (int64_t)gridDim.x * 64) taps += blk_taps[b];
+        for (int64_t b = t; b < nblk; b += (int64_t)gridDim.x * PLAN_BLOCK) taps += blk_taps[b];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) taps += __shfl_xor(taps, off, 64);
-        if (threadIdx.x == 0 && taps) atomicAdd(&st->taps, taps);
+        if (tid == 0 && taps) atomicAdd(&st->taps, taps);
     }
-    if (t >= ntiles) return;
-    int32_t lo[9], hi[9], row[9];
+    // the block's groups are a contiguous run of gwin (8-byte aligned records)
+    {
+        const int64_t g0 = t0 * PLAN_GPT;
+        const int64_t ng = min((int64_t)PLAN_BLOCK * PLAN_GPT, ngroups - g0);
+        const int pairs = ng > 0 ? (int)(ng * GWIN_INTS / 2) : 0;
+        const int2 *src = (const int2 *)(gwin + (ng > 0 ? g0 : 0) * GWIN_INTS);
+        constexpr int PER = PLAN_BLOCK * PLAN_GPT * GWIN_INTS / 2 / PLAN_BLOCK;  // 36 pairs per thread
+        int2 v[PER];
 #pragma unroll
-    for (int d = 0; d < 9; ++d) {
-        lo[d] = GWIN_NONE;
-        hi[d] = -1;
-        row[d] = d;
+        for (int e = 0; e < PER; ++e) {
+            const int idx = e * PLAN_BLOCK + tid;
+            v[e] = src[idx < pairs ? idx : 0];
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = e * PLAN_BLOCK + tid;
+            if (idx < pairs) ((int2 *)s_win)[idx] = v[e];
+        }
     }
-    for (int g = 0; g < gpt; ++g) {
-        const int64_t gi = t * gpt + g;
-        if (gi >= ngroups) break;
-        const int32_t *w = gwin + gi * GWIN_INTS;
+    __syncthreads();
+    int32_t *p = s_plan + tid * PLAN_ROW;
+    if (t < ntiles) {
+        int32_t lo[9], hi[9], row[9];
 #pragma unroll
         for (int d = 0; d < 9; ++d) {
-            const int32_t h = w[9 + d];
-            if (h >= 0) {
-                lo[d] = min(lo[d], w[d]);
-                hi[d] = max(hi[d], h);
+            lo[d] = GWIN_NONE;
+            hi[d] = -1;
+            row[d] = d;
+        }
+#pragma unroll
+        for (int g = 0; g < PLAN_GPT; ++g) {
+            if (t * PLAN_GPT + g >= ngroups) break;
+            const int32_t *w = s_win + (tid * PLAN_GPT + g) * GWIN_INTS;
+#pragma unroll
+            for (int d = 0; d < 9; ++d) {
+                const int32_t h = w[9 + d];
+                if (h >= 0) {
+                    lo[d] = min(lo[d], w[d]);
+                    hi[d] = max(hi[d], h);
+                }
             }
         }
-    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8 - i; ++j) {
-            const bool sw = lo[j] > lo[j + 1];
-            const int32_t a = lo[j], b = hi[j], c = row[j];
-            lo[j] = sw ? lo[j + 1] : a;
-            hi[j] = sw ? hi[j + 1] : b;
-            row[j] = sw ? row[j + 1] : c;
-            lo[j + 1] = sw ? a : lo[j + 1];
-            hi[j + 1] = sw ? b : hi[j + 1];
-            row[j + 1] = sw ? c : row[j + 1];
+            for (int j = 0; j < 8 - i; ++j) {
+                const bool sw = lo[j] > lo[j + 1];
+                const int32_t a = lo[j], b = hi[j], c = row[j];
+                lo[j] = sw ? lo[j + 1] : a;
+                hi[j] = sw ? hi[j + 1] : b;
+                row[j] = sw ? row[j + 1] : c;
+                lo[j + 1] = sw ? a : lo[j + 1];
+                hi[j + 1] = sw ? b : hi[j + 1];
+                row[j + 1] = sw ? c : row[j + 1];
+            }
+        int nr = 0, total = 0;
+        int32_t cur_lo = 0, cur_hi = -2;
+        int32_t delta[9];
+#pragma unroll
+        for (int d = 0; d < 9; ++d) delta[d] = 0;
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            if (lo[i] == GWIN_NONE) continue;  // empty rows sort last
+            if (nr == 0 || lo[i] > cur_hi + 1) {
+                if (nr > 0) total += cur_hi - cur_lo + 1;
+                p[2 + nr] = lo[i];
+                p[11 + nr] = total;
+                cur_lo = lo[i];
+                cur_hi = hi[i];
+                ++nr;
+            } else if (hi[i] > cur_hi) {
+                cur_hi = hi[i];
+            }
+            const int32_t dl = total - cur_lo;  // slot of sorted position q in this range: q + dl
+#pragma unroll
+            for (int d = 0; d < 9; ++d)
+                if (row[i] == d) delta[d] = dl;
         }
-    int32_t *p = plan + t * PLAN_INTS;
-    int nr = 0, total = 0;
-    int32_t cur_lo = 0, cur_hi = -2;
-    int32_t delta[9];
-#pragma unroll
-    for (int d = 0; d < 9; ++d) delta[d] = 0;
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-        if (lo[i] == GWIN_NONE) continue;  // empty rows sort last
-        if (nr == 0 || lo[i] > cur_hi + 1) {
-            if (nr > 0) total += cur_hi - cur_lo + 1;
-            p[2 + nr] = lo[i];
-            p[11 + nr] = total;
-            cur_lo = lo[i];
-            cur_hi = hi[i];
-            ++nr;
-        } else if (hi[i] > cur_hi) {
-            cur_hi = hi[i];
+        if (nr > 0) total += cur_hi - cur_lo + 1;
+        for (int r = nr; r < 9; ++r) {
+            p[2 + r] = 0;
+            p[11 + r] = total;
         }
-        const int32_t dl = total - cur_lo;  // slot of sorted position q in this range: q + dl
 #pragma unroll
-        for (int d = 0; d < 9; ++d)
-            if (row[i] == d) delta[d] = dl;
+        for (int d = 0; d < 9; ++d) p[20 + d] = delta[d];
+        p[0] = total <= cap ? total : -1;
+        p[1] = nr;
+        p[29] = p[30] = p[31] = 0;
     }
-    if (nr > 0) total += cur_hi - cur_lo + 1;
-    for (int r = nr; r < 9; ++r) {
-        p[2 + r] = 0;
-        p[11 + r] = total;
-    }
-#pragma unroll
-    for (int d = 0; d < 9; ++d) p[20 + d] = delta[d];
-    p[0] = total <= cap ? total : -1;
-    p[1] = nr;
-    p[29] = p[30] = p[31] = 0;
+    __syncthreads();
+    const int rows = (int)min((int64_t)PLAN_BLOCK, ntiles - t0);
+    int32_t *dst = plan + t0 * PLAN_INTS;
+    for (int e = tid; e < rows * PLAN_INTS; e += PLAN_BLOCK) dst[e] = s_plan[(e / PLAN_INTS) * PLAN_ROW + e % PLAN_INTS];
 }
 
 // ---------------------------------------------------------------------------
@@ -514,8 +546,8 @@ int win_plan_build(submconv_rulebook *rb, const uint32_t *blk_taps, int64_t nblk
     if (ntiles == 0) return SUBMCONV_OK;
     // one thread per tile, small blocks: the work is a short serial merge per tile,
     // so spreading the tiles over every CU is what matters
-    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + 63) / 64)), dim3(64), 0, s, rb->gwin,
-                       rb->ngroups, ntiles, WIN_TILE / 32, WIN_CAP, rb->plan, blk_taps, nblk, st);
+    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + PLAN_BLOCK - 1) / PLAN_BLOCK)), dim3(PLAN_BLOCK), 0, s,
+                       rb->gwin, rb->ngroups, ntiles, WIN_CAP, rb->plan, blk_taps, nblk, st);
     SC_LAUNCHED("win_plan");
     return SUBMCONV_OK;
 }

@@ -175,11 +175,18 @@ __global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, i
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * (256 * MARK_ROWS) + threadIdx.x;
     bool bad_any = false;
+    // all rows' loads first (clamped index, no branch), so they share one round trip
+    int4 cq[MARK_ROWS];
 #pragma unroll
     for (int q = 0; q < MARK_ROWS; ++q) {
         const int64_t i = base + q * 256;  // consecutive threads read consecutive rows
+        cq[q] = coords[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int q = 0; q < MARK_ROWS; ++q) {
+        const int64_t i = base + q * 256;
         if (i >= n) continue;
-        const int4 c = coords[i];
+        const int4 c = cq[q];
         const bool bad = (unsigned)c.x >= (unsigned)batch || (unsigned)c.y >= (unsigned)res ||
                          (unsigned)c.z >= (unsigned)res || (unsigned)c.w >= (unsigned)res;
         bad_any |= bad;
@@ -675,7 +682,11 @@ int win_plan_build(submconv_rulebook *rb, const uint32_t *blk_taps, int64_t nblk
 __global__ __launch_bounds__(256) void k_clear(DevStatus *st, unsigned long long *__restrict__ w, int64_t words)
 {
     if (blockIdx.x == 0 && threadIdx.x == 0) *st = DevStatus{};
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) w[i] = 0ull;
+    // pairs of words as 16-byte stores (w is 16-byte aligned), then an odd last word
+    const int64_t pairs = words >> 1;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pairs; i += (int64_t)gridDim.x * 256)
+        ((ulonglong2 *)w)[i] = make_ulonglong2(0ull, 0ull);
+    if ((words & 1) && blockIdx.x == 0 && threadIdx.x == 0) w[words - 1] = 0ull;
 }
 
 static bool use_bitmap(int64_t n, int nbits)
@@ -718,7 +729,7 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     do {
         // one launch clears the status block and (dense path) the bitmap
         const int64_t clear_words = path == 2 ? words + 1 : 0;
-        hipLaunchKernelGGL(k_clear, dim3((unsigned)(clear_words > 0 ? (clear_words + 2047) / 2048 : 1)), dim3(256), 0,
+        hipLaunchKernelGGL(k_clear, dim3((unsigned)(clear_words > 0 ? (clear_words + 4095) / 4096 : 1)), dim3(256), 0,
                            stream, st, (unsigned long long *)(scratch + o_bm), clear_words);
         if (path == 0 || path == 1) {
             if (path == 0)

@@ -221,26 +221,60 @@ __global__ __launch_bounds__(256) void k_scan_tiles(const uint32_t *__restrict__
 {
     __shared__ uint32_t lds[4];
     const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + (int64_t)threadIdx.x * SCAN_ITEMS;
+    // A thread's items are contiguous: a full run moves as 16-byte loads and stores
+    // (a thread's first item is 32- or 64-byte aligned: base is a multiple of 8).
+    const bool full = base + SCAN_ITEMS <= n;
     uint32_t v[SCAN_ITEMS];
     uint32_t local = 0;
+    if (MODE == 2 && full) {
+        const ulonglong2 *src = (const ulonglong2 *)((const uint64_t *)in + base);
 #pragma unroll
-    for (int e = 0; e < SCAN_ITEMS; ++e) {
-        if (MODE == 2) {
-            const uint64_t x = (base + e < n) ? ((const uint64_t *)in)[base + e] : 0ull;
-            v[e] = (uint32_t)__popcll(x);
-        } else {
-            const uint32_t x = (base + e < n) ? in[base + e] : 0u;
-            v[e] = MODE == 1 ? (uint32_t)__popc(x) : x;
+        for (int h = 0; h < SCAN_ITEMS / 2; ++h) {
+            const ulonglong2 x = src[h];
+            v[2 * h] = (uint32_t)__popcll(x.x);
+            v[2 * h + 1] = (uint32_t)__popcll(x.y);
         }
-        local += v[e];
+    } else if (MODE != 2 && full) {
+        const uint4 *src = (const uint4 *)(in + base);
+#pragma unroll
+        for (int h = 0; h < SCAN_ITEMS / 4; ++h) {
+            const uint4 x = src[h];
+            v[4 * h] = MODE == 1 ? (uint32_t)__popc(x.x) : x.x;
+            v[4 * h + 1] = MODE == 1 ? (uint32_t)__popc(x.y) : x.y;
+            v[4 * h + 2] = MODE == 1 ? (uint32_t)__popc(x.z) : x.z;
+            v[4 * h + 3] = MODE == 1 ? (uint32_t)__popc(x.w) : x.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < SCAN_ITEMS; ++e) {
+            if (MODE == 2) {
+                const uint64_t x = (base + e < n) ? ((const uint64_t *)in)[base + e] : 0ull;
+                v[e] = (uint32_t)__popcll(x);
+            } else {
+                const uint32_t x = (base + e < n) ? in[base + e] : 0u;
+                v[e] = MODE == 1 ? (uint32_t)__popc(x) : x;
+            }
+        }
     }
+#pragma unroll
+    for (int e = 0; e < SCAN_ITEMS; ++e) local += v[e];
     uint32_t total;
     const uint32_t incl = block_incl_scan256(local, lds, &total);
     uint32_t run = incl - local;
+    uint32_t o[SCAN_ITEMS];
 #pragma unroll
     for (int e = 0; e < SCAN_ITEMS; ++e) {
-        if (base + e < n) out[base + e] = run;
+        o[e] = run;
         run += v[e];
+    }
+    if (full) {
+        uint4 *dst = (uint4 *)(out + base);
+#pragma unroll
+        for (int h = 0; h < SCAN_ITEMS / 4; ++h) dst[h] = make_uint4(o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < SCAN_ITEMS; ++e)
+            if (base + e < n) out[base + e] = o[e];
     }
     if (threadIdx.x == 0) sums[blockIdx.x] = total;
 }
