@@ -371,7 +371,13 @@ __device__ __forceinline__ int swz(int row)
     else return (row / (16 / CH)) & (CH - 1);
 }
 
-template <typename T, int CIN, int COUT, int VT>
+constexpr int align1k(int b) { return (b + 1023) & ~1023; }
+
+// OS output groups: the OS waves of a column share its gathered rows and split
+// Cout, so a block covers 4/OS columns (more blocks on small sets, less MFMA work
+// per wave).  A shared column region is double-buffered: one wave may gather tap
+// k+1 while the other still reads tap k.
+template <typename T, int CIN, int COUT, int VT, int OS = 1>
 struct RowShape {
     static constexpr int ES = (int)sizeof(T);
     static constexpr int RB = CIN * ES;                // bytes per feature / weight row
@@ -379,18 +385,27 @@ struct RowShape {
     static constexpr int RPI = 1024 / RB;              // rows per 1 KB load instruction
     static constexpr int EPC = 16 / ES;
     static constexpr int G = CH / 2;
-    static constexpr int RT = COUT / 32;
-    static constexpr int ROWS = VT * 32;               // gathered rows per wave
+    static constexpr int RT = COUT / 32 / OS;          // 32-output tiles per wave
+    static constexpr int ROWS = VT * 32;               // gathered rows per column
+    static constexpr int COLS = 4 / OS;                // columns per block
+    static constexpr int FB = OS == 1 ? 1 : 2;         // row buffers per column
     static constexpr int W_TAP = COUT * RB;            // bytes of one weight tap
     static constexpr bool RESIDENT = 27 * W_TAP <= 65536;
     static constexpr int WBUF = RESIDENT ? 27 : 2;
-    static constexpr int VOX_PER_BLOCK = 4 * ROWS;
+    static constexpr int VOX_PER_BLOCK = COLS * ROWS;
     static constexpr int NBR_BYTES = VOX_PER_BLOCK * NBR_INTS * 4;
-    static constexpr int LDS = WBUF * W_TAP + 4 * ROWS * RB + NBR_BYTES;
+    // the kernel's objects: weights (one object of 27 taps, or two of one tap), one
+    // or two row buffers, the table block; 1-KB alignment of each
+    static constexpr int LDS = (RESIDENT ? align1k(27 * W_TAP) + 1024 : 2 * align1k(W_TAP)) +
+                               (FB == 2 ? 2 : 1) * align1k(COLS * ROWS * RB) + (FB == 2 ? 0 : 1024) +
+                               align1k(NBR_BYTES);
     static_assert(RB >= 64 && RB <= 1024 && (RB & (RB - 1)) == 0, "row size");
+    static_assert(OS == 1 || OS == 2, "output groups");
+    static_assert(RT >= 1 && RT * 32 * OS == COUT, "Cout split");
+    static_assert((ROWS / RPI) % OS == 0, "gather instructions split evenly");
 };
 
-template <typename T, int CIN, int COUT, int VT>
+template <typename T, int CIN, int COUT, int VT, int OS>
 __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ feats,
                                                         const T *__restrict__ w,
                                                         const float *__restrict__ bias,
@@ -398,47 +413,64 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
                                                         const int32_t *__restrict__ perm,
                                                         T *__restrict__ out, int64_t n, int flip)
 {
-    using S = RowShape<T, CIN, COUT, VT>;
+    using S = RowShape<T, CIN, COUT, VT, OS>;
     constexpr int RB = S::RB, CH = S::CH, RPI = S::RPI, EPC = S::EPC, G = S::G, RT = S::RT;
-    constexpr int ROWS = S::ROWS;
-    __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
-    char *sW = lds;                                             // [WBUF][COUT rows][RB]
+    constexpr int ROWS = S::ROWS, COLS = S::COLS, FB = S::FB;
+    // One object per region and buffer: the compiler tracks direct global-to-LDS
+    // copies per object, so reading one buffer does not wait for copies into another
+    // (within one object every LDS read waited for every copy in flight).
+    __shared__ __attribute__((aligned(1024))) char sW0[S::RESIDENT ? 27 * S::W_TAP : S::W_TAP];
+    __shared__ __attribute__((aligned(1024))) char sW1[S::RESIDENT ? 16 : S::W_TAP];
+    __shared__ __attribute__((aligned(1024))) char sF0[COLS * ROWS * RB];
+    __shared__ __attribute__((aligned(1024))) char sF1[FB == 2 ? COLS * ROWS * RB : 16];
+    __shared__ __attribute__((aligned(1024))) char sNb[S::NBR_BYTES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    char *sF = lds + S::WBUF * S::W_TAP + wave * ROWS * RB;     // this wave's [ROWS][RB]
-    const int32_t *sN = (const int32_t *)(lds + S::WBUF * S::W_TAP + 4 * ROWS * RB);  // [block voxels][NBR_INTS]
+    const int colw = wave / OS, og = wave % OS;                 // column, output group
+    const int32_t *sN = (const int32_t *)sNb;                   // [block voxels][NBR_INTS]
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t blk = xcd_block();
-    const int64_t vbase = (blk * 4 + wave) * ROWS;
+    const int64_t vbase = (blk * COLS + colw) * ROWS;
 
-    // weight tap k -> LDS buffer buf, whole rows, swizzled
-    auto stage_w = [&](int k, int buf) {
+    // weight tap k -> `dst` (one tap: [COUT rows][RB]), whole rows, swizzled
+    auto stage_w = [&](int k, char *dst) {
         const int kw = flip ? 26 - k : k;
         constexpr int NI = COUT / RPI;                          // 1 KB instructions per tap
         for (int i = wave; i < NI; i += 4) {
             const int o = i * RPI + lane / CH;
             const int c = (lane % CH) ^ swz<RB>(o);
             const T *src = w + ((int64_t)o * 27 + kw) * CIN + c * EPC;
-            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(sW + buf * S::W_TAP + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
         }
     };
-    // this wave's neighbour rows for tap k -> its LDS region; returns whether any exists
-    auto gather = [&](int k) -> bool {
-        int32_t j = -1;
-        if (lane < ROWS && vbase + lane < n) {
-            j = nbr_at(sN + (wave * ROWS + lane) * NBR_INTS, k);
-            j = (uint32_t)j < (uint64_t)n ? perm[j] : -1;
-            if ((uint32_t)j >= (uint64_t)n) j = -1;
-        }
+    // input row of the tap-k neighbour of the column's voxel `lane` (lanes < ROWS):
+    // looked up one tap before its gather, so the load overlaps a tap of MFMAs.  The
+    // load is unconditional and its value is not inspected here (either would make
+    // the compiler wait for it at once); the gather applies the checks.
+    struct Look {
+        int32_t r;
+        bool ok;
+    };
+    auto lookup = [&](int k) -> Look {
+        int32_t e = -1;
+        if (lane < ROWS && vbase + lane < n) e = nbr_at(sN + (colw * ROWS + lane) * NBR_INTS, k);
+        const bool ok = (uint32_t)e < (uint64_t)n;
+        return Look{perm[ok ? e : 0], ok};
+    };
+    // the column's neighbour rows for tap k -> its region of `fbuf` (the OS waves of
+    // the column each issue every OS-th copy); returns whether any row exists
+    auto gather = [&](const Look &L, char *fbuf) -> bool {
+        const int32_t j = L.ok && (uint32_t)L.r < (uint64_t)n ? L.r : -1;
         const bool any = __any(j >= 0);
         if (any) {
+            char *dst = fbuf + colw * ROWS * RB;
 #pragma unroll
-            for (int i = 0; i < ROWS / RPI; ++i) {
+            for (int i = og; i < ROWS / RPI; i += OS) {
                 const int row = i * RPI + lane / CH;
                 const int jr = __shfl(j, row, 64);
                 const int c = (lane % CH) ^ swz<RB>(row);
                 const void *src = jr >= 0 ? (const void *)(feats + (int64_t)jr * CIN + c * EPC)
                                           : (const void *)((const char *)g_zero_row + c * 16);
-                __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(sF + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
             }
         }
         return any;
@@ -453,46 +485,62 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
             for (int q = 0; q < 16; ++q) acc[r][t][q] = 0.f;
 
     if constexpr (S::RESIDENT) {
-        for (int k = 0; k < 27; ++k) stage_w(k, k);
+        for (int k = 0; k < 27; ++k) stage_w(k, sW0 + k * S::W_TAP);
     } else {
-        stage_w(0, 0);
+        stage_w(0, sW0);
     }
-    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK,
-                                lds + S::WBUF * S::W_TAP + 4 * ROWS * RB, wave, lane);
+    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK, sNb, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bool any = gather(0);
-    for (int k = 0; k < 27; ++k) {
+    bool any = gather(lookup(0), sF0);
+    Look jn = lookup(1);                 // the next tap's rows
+
+    // tap k; ODD picks the buffers at compile time (the tap loop is unrolled by two):
+    // weights and rows of tap k are read from one buffer while tap k+1 fills the other
+    auto step = [&](auto odd, int k) {
+        constexpr bool O = decltype(odd)::value;
+        char *wnxt = O ? sW0 : sW1;
+        char *fcur = (FB == 2 && O) ? sF1 : sF0;
+        char *fnxt = (FB == 2 && !O) ? sF1 : sF0;
+        const char *wb = S::RESIDENT ? sW0 + k * S::W_TAP : (O ? sW1 : sW0);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into LDS have landed
-        __syncthreads();                 // ... and everyone's; buffer (k+1)&1 is free
+        __syncthreads();                 // ... and everyone's; the other buffers are free
         if constexpr (!S::RESIDENT) {
-            if (k + 1 < 27) stage_w(k + 1, (k + 1) & 1);
+            if (k + 1 < 27) stage_w(k + 1, wnxt);
         }
         uint4 F[VT][G];
         if (any) {
+            const char *src = fcur + colw * ROWS * RB;
 #pragma unroll
             for (int t = 0; t < VT; ++t)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int row = 32 * t + l32;
-                    F[t][g] = *(const uint4 *)(sF + row * RB + (((2 * g + half) ^ swz<RB>(row)) << 4));
+                    F[t][g] = *(const uint4 *)(src + row * RB + (((2 * g + half) ^ swz<RB>(row)) << 4));
                 }
         }
-        SC_WAIT_LGKM0();                 // fragments are in registers: the region may be refilled
+        // With one row buffer the fragments must be in registers before this wave
+        // refills its region; with two, the next gather goes to the other buffer, which
+        // every wave of the column finished reading before the barrier above.
+        if constexpr (FB == 1) SC_WAIT_LGKM0();
         const bool any_now = any;
-        any = (k + 1 < 27) ? gather(k + 1) : false;
+        any = (k + 1 < 27) ? gather(jn, fnxt) : false;
+        if (k + 2 < 27) jn = lookup(k + 2);
         if (any_now) {
-            const char *wb = sW + (S::RESIDENT ? k : (k & 1)) * S::W_TAP;
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {
-                    const int o = 32 * r + l32;
+                    const int o = 32 * (og * RT + r) + l32;
                     const uint4 a = *(const uint4 *)(wb + o * RB + (((2 * g + half) ^ swz<RB>(o)) << 4));
 #pragma unroll
                     for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], a, F[t][g]);
                 }
         }
+    };
+    for (int k = 0; k < 27; k += 2) {
+        step(std::false_type{}, k);
+        if (k + 1 < 27) step(std::true_type{}, k + 1);
     }
 
 #pragma unroll
@@ -505,7 +553,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
         for (int r = 0; r < RT; ++r)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int o = 32 * r + 8 * q + 4 * half;
+                const int o = 32 * (og * RT + r) + 8 * q + 4 * half;
                 float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (bias) b = *(const float4 *)(bias + o);
                 Store4<T>::put(out + orow * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
@@ -582,9 +630,22 @@ static void launch_mfma_vt(const void *f, const void *w, const float *b, const i
                            void *o, int64_t n, int flip, hipStream_t s)
 {
     if constexpr (RowShape<T, CIN, COUT, VT>::LDS <= 160 * 1024) {
+        // Split Cout over two waves per column when one-wave columns would leave
+        // fewer than two blocks per CU (256 CUs).
         constexpr int per_block = RowShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
+        if constexpr (VT == 1 && COUT >= 64) {
+            if constexpr (RowShape<T, CIN, COUT, 1, 2>::LDS <= 160 * 1024) {
+                if ((n + per_block - 1) / per_block < 2 * 256) {
+                    constexpr int pb2 = RowShape<T, CIN, COUT, 1, 2>::VOX_PER_BLOCK;
+                    const unsigned grid = (unsigned)((n + pb2 - 1) / pb2);
+                    hipLaunchKernelGGL((k_conv_mfma_rows<T, CIN, COUT, 1, 2>), dim3(grid), dim3(256), 0, s,
+                                       (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
+                    return;
+                }
+            }
+        }
         const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
-        hipLaunchKernelGGL((k_conv_mfma_rows<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_conv_mfma_rows<T, CIN, COUT, VT, 1>), dim3(grid), dim3(256), 0, s,
                            (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     } else {
         constexpr int per_block = MfmaShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;

@@ -332,6 +332,27 @@ def sampled_check(c, res, batch, cin, cout, dtype, seed, bias, std, rows=3000, s
     assert torch.equal(out, out2)
 
 
+# the rows MFMA kernel's three block layouts: on small sets two waves share a
+# 32-voxel column and split Cout (the random-set tests above); from 512 blocks of
+# 128 voxels on, one wave per column; from 2 * 256 * 256 voxels on, two columns per
+# wave.  Checked on sampled output rows against the oracle.
+@pytest.mark.parametrize("n,cin,cout,dtype", [(70001, 64, 64, "f32"), (70001, 32, 128, "bf16"),
+                                              (140001, 64, 64, "bf16"), (140001, 128, 64, "f32")])
+def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
+    c = synth.random_coords(n, 64, 1, 21)
+    feats, weight, b = synth.make_values(len(c), cin, cout, 5)
+    tf, tw, tb, f64, w64 = device_values(feats, weight, b, dtype)
+    rb = build(c, 64, 1)
+    note("mfma rows layout n=%d %d->%d %s" % (n, cin, cout, dtype))
+    out = sc.submconv_forward(tf, tw, tb, rb, variant=sc.KERNEL_MFMA)
+    table = dense.neighbor_table(c, 64, 1)
+    pick = np.sort(np.random.default_rng(n).choice(len(c), size=3000, replace=False))
+    pick = np.unique(np.concatenate([pick, [0, len(c) - 1]]))
+    expect = ref.forward(f64, w64, b, table[pick])
+    got = to_f64(out[torch.from_numpy(pick).to(DEV)])
+    assert_close(got, expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
+
+
 def test_forward_workload4_sampled():
     w, c = synth.workload(4)
     sampled_check(c, w.res, w.batch, w.cin, w.cout, "bf16", w.value_seed, w.bias, w.weight_std)
