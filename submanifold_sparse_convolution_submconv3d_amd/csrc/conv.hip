@@ -237,7 +237,11 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
 {
     using S = MfmaShape<T, CIN, COUT, VT>;
     constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
-    __shared__ uint4 sW[S::WBUF][NFRAG * 64];
+    // two weight objects when taps rotate through two buffers: the compiler tracks
+    // direct global-to-LDS copies per object, so reading tap k's buffer does not wait
+    // for the copy of tap k+1 into the other (and, through it, for every load in flight)
+    __shared__ uint4 sW0[S::RESIDENT ? 27 : 1][NFRAG * 64];
+    __shared__ uint4 sW1[S::RESIDENT ? 1 : 1][S::RESIDENT ? 4 : NFRAG * 64];
     __shared__ __attribute__((aligned(16))) int32_t sN[S::VOX_PER_BLOCK * NBR_INTS + 256];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -245,26 +249,41 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     const int64_t blk = xcd_block();
     const int64_t vbase = (blk * 4 + wave) * (VT * 32);
 
-    // copy weight tap k (kernel tap k' = flip ? 26-k : k) into LDS buffer `buf`
-    auto stage_w = [&](int k, int buf) {
+    // copy weight tap k (kernel tap k' = flip ? 26-k : k) into the LDS buffer `dst`
+    auto stage_w = [&](int k, uint4 *dst) {
         const int kw = flip ? 26 - k : k;
         for (int f = wave; f < NFRAG; f += 4) {
             const int r = f / G, g = f - r * G;
             const T *src = w + ((int64_t)(32 * r + l32) * 27 + kw) * CIN + (2 * g + half) * EPC;
-            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)&sW[buf][f * 64], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)&dst[f * 64], 16, 0, 0);
         }
     };
-    // neighbour rows of this wave's voxels for tap k, and their feature fragments
-    auto load_tap = [&](int k, int32_t (&j)[VT], uint4 (&F)[VT][G]) -> bool {
-        bool any = false;
+    // input rows of this wave's voxels' tap-k neighbours, looked up a tap before
+    // their fragments are fetched: the perm loads are unconditional and not
+    // inspected here, so they overlap a tap of MFMAs instead of being waited on
+    struct Look {
+        int32_t r[VT];
+        bool ok[VT];
+    };
+    auto lookup = [&](int k) -> Look {
+        Look L;
 #pragma unroll
         for (int t = 0; t < VT; ++t) {
             const int64_t v = vbase + 32 * t + l32;
-            int32_t r = v < n ? nbr_at(sN + (wave * VT * 32 + 32 * t + l32) * NBR_INTS, k) : -1;
-            r = (uint32_t)r < (uint64_t)n ? perm[r] : -1;
-            if ((uint32_t)r >= (uint64_t)n) r = -1;
-            j[t] = r;
-            any |= r >= 0;
+            const int32_t e = v < n ? nbr_at(sN + (wave * VT * 32 + 32 * t + l32) * NBR_INTS, k) : -1;
+            L.ok[t] = (uint32_t)e < (uint64_t)n;
+            L.r[t] = perm[L.ok[t] ? e : 0];
+        }
+        return L;
+    };
+    // feature fragments of the looked-up rows (zeros for missing neighbours)
+    auto fetch = [&](const Look &L, uint4 (&F)[VT][G]) -> bool {
+        bool any = false;
+        int32_t j[VT];
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+            j[t] = L.ok[t] && (uint32_t)L.r[t] < (uint64_t)n ? L.r[t] : -1;
+            any |= j[t] >= 0;
         }
 #pragma unroll
         for (int t = 0; t < VT; ++t)
@@ -294,30 +313,33 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
             }
     };
 
-    int32_t j0[VT], j1[VT];
     uint4 F0[VT][G], F1[VT][G];
     if constexpr (S::RESIDENT) {
-        for (int k = 0; k < 27; ++k) stage_w(k, k);
+        for (int k = 0; k < 27; ++k) stage_w(k, sW0[k]);
     } else {
-        stage_w(0, 0);
+        stage_w(0, sW0[0]);
     }
     stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK, (char *)sN, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bool any0 = load_tap(0, j0, F0), any1 = false;
+    bool any0 = fetch(lookup(0), F0), any1 = false;
+    Look Ln = lookup(1);                 // the next tap's rows
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // one tap: prefetch tap k+1 (weights into LDS, features into the other
-    // register set), run tap k's MFMAs, then wait and (when the weights
-    // rotate through two buffers) meet at a barrier
-    auto tap = [&](int k, uint4 (&Fc)[VT][G], bool anyc, int32_t (&jn)[VT], uint4 (&Fn)[VT][G]) -> bool {
+    // register set) and look up tap k+2, run tap k's MFMAs, then wait and (when
+    // the weights rotate through two buffers) meet at a barrier.  ODD (the loop is
+    // unrolled by two) picks the weight buffers at compile time.
+    auto tap = [&](auto odd, int k, uint4 (&Fc)[VT][G], bool anyc, uint4 (&Fn)[VT][G]) -> bool {
+        constexpr bool O = decltype(odd)::value;
         bool anyn = false;
         if (k + 1 < 27) {
-            if constexpr (!S::RESIDENT) stage_w(k + 1, (k + 1) & 1);
-            anyn = load_tap(k + 1, jn, Fn);
+            if constexpr (!S::RESIDENT) stage_w(k + 1, O ? sW0[0] : sW1[0]);
+            anyn = fetch(Ln, Fn);
         }
-        if (__any(anyc)) compute(sW[S::RESIDENT ? k : (k & 1)], Fc);
+        if (k + 2 < 27) Ln = lookup(k + 2);
+        if (__any(anyc)) compute(S::RESIDENT ? sW0[k] : (O ? sW1[0] : sW0[0]), Fc);
         if constexpr (!S::RESIDENT) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -325,8 +347,8 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
         return anyn;
     };
     for (int k = 0; k < 27; k += 2) {
-        any1 = tap(k, F0, any0, j1, F1);
-        if (k + 1 < 27) any0 = tap(k + 1, F1, any1, j0, F0);
+        any1 = tap(std::false_type{}, k, F0, any0, F1);
+        if (k + 1 < 27) any0 = tap(std::true_type{}, k + 1, F1, any1, F0);
     }
 
 #pragma unroll
