@@ -58,124 +58,129 @@ constexpr int WIN_TILE = 128;    // voxels per tile (4 groups of 32)
 constexpr int WIN_SLOTS = 1024;  // row slots per buffer; the last one always holds zeros
 constexpr int WIN_CAP = WIN_SLOTS - 1;
 
-// One thread per tile: union of its groups' row windows, sorted and merged.
-// Straight-line code with compile-time indices (registers only).  A block's
-// group windows are read into LDS and its plan records written back from LDS as
-// contiguous runs, so both sides are coalesced.  When blk_taps is given, the
-// kernel also sums those per-block present counts into st->taps (one
-// device-scope atomic per block of this kernel).
-constexpr int PLAN_GPT = WIN_TILE / 32;            // groups per tile
-constexpr int PLAN_BLOCK = 64;                     // tiles per block
-constexpr int PLAN_ROW = PLAN_INTS + 1;            // padded LDS record (no bank conflicts)
-__global__ __launch_bounds__(PLAN_BLOCK) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
-                                                         int64_t ntiles, int cap, int32_t *__restrict__ plan,
-                                                         const uint32_t *__restrict__ blk_taps, int64_t nblk,
-                                                         DevStatus *st)
+// 16-lane inclusive scans (shuffles of width 16 stay inside a team)
+__device__ __forceinline__ int32_t team_scan_add(int32_t x, int q)
 {
-    __shared__ int32_t s_win[PLAN_BLOCK * PLAN_GPT * GWIN_INTS];  // 18 KB
-    __shared__ int32_t s_plan[PLAN_BLOCK * PLAN_ROW];              // 8.4 KB
-    const int tid = threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * PLAN_BLOCK, t = t0 + tid;
-    if (blk_taps) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 16);
+        x += q >= off ? y : 0;
+    }
+    return x;
+}
+__device__ __forceinline__ int32_t team_scan_max(int32_t x, int q)
+{
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 16);
+        x = q >= off && y > x ? y : x;
+    }
+    return x;
+}
+
+// A team of 16 lanes per tile: lane q < 9 takes (dz, dy) row q, the union of its
+// window over the tile's groups.  The rows are ranked by window start (ties by
+// row, empty rows last), each lane then takes the row of its rank, and the
+// merge into ranges is a set of team scans: sorted element i starts a range
+// when its start exceeds by more than one the largest end before it (which is
+// the end of the current range, since ranges end in increasing order).  The
+// block's records are assembled in LDS and written as one contiguous run.
+// The first PLAN_TAP_BLOCKS blocks also sum the per-block present counts of
+// the resolve (blk_taps, when given) into st->taps.
+constexpr int PLAN_GPT = WIN_TILE / 32;              // groups per tile
+constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_TILES = PLAN_THREADS / 16;        // tiles per block
+constexpr int PLAN_TAP_BLOCKS = 64;
+__global__ __launch_bounds__(PLAN_THREADS) void k_win_plan(const int32_t *__restrict__ gwin, int64_t ngroups,
+                                                           int64_t ntiles, int cap, int32_t *__restrict__ plan,
+                                                           const uint32_t *__restrict__ blk_taps, int64_t nblk,
+                                                           DevStatus *st)
+{
+    __shared__ __attribute__((aligned(16))) int32_t s_rec[PLAN_TILES * PLAN_INTS];
+    const int tid = threadIdx.x, q = tid & 15, team = tid >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * PLAN_TILES, t = t0 + team;
+    if (blk_taps && blockIdx.x < PLAN_TAP_BLOCKS) {
+        const int64_t stride = (int64_t)min((int64_t)gridDim.x, (int64_t)PLAN_TAP_BLOCKS) * PLAN_THREADS;
         unsigned long long taps = 0;
-        for (int64_t b = t; b < nblk; b += (int64_t)gridDim.x * PLAN_BLOCK) taps += blk_taps[b];
+        for (int64_t b = (int64_t)blockIdx.x * PLAN_THREADS + tid; b < nblk; b += stride) taps += blk_taps[b];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) taps += __shfl_xor(taps, off, 64);
-        if (tid == 0 && taps) atomicAdd(&st->taps, taps);
+        if ((tid & 63) == 0 && taps) atomicAdd(&st->taps, taps);
     }
-    // the block's groups are a contiguous run of gwin (8-byte aligned records)
-    {
-        const int64_t g0 = t0 * PLAN_GPT;
-        const int64_t ng = min((int64_t)PLAN_BLOCK * PLAN_GPT, ngroups - g0);
-        const int pairs = ng > 0 ? (int)(ng * GWIN_INTS / 2) : 0;
-        const int2 *src = (const int2 *)(gwin + (ng > 0 ? g0 : 0) * GWIN_INTS);
-        constexpr int PER = PLAN_BLOCK * PLAN_GPT * GWIN_INTS / 2 / PLAN_BLOCK;  // 36 pairs per thread
-        int2 v[PER];
+
+    // row q's window over the tile's groups (groups past ngroups are empty)
+    int32_t lo = GWIN_NONE, hi = -1;
+    if (t < ntiles && q < 9) {
+        int32_t wl[PLAN_GPT], wh[PLAN_GPT];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = e * PLAN_BLOCK + tid;
-            v[e] = src[idx < pairs ? idx : 0];
-        }
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = e * PLAN_BLOCK + tid;
-            if (idx < pairs) ((int2 *)s_win)[idx] = v[e];
-        }
-    }
-    __syncthreads();
-    int32_t *p = s_plan + tid * PLAN_ROW;
-    if (t < ntiles) {
-        int32_t lo[9], hi[9], row[9];
-#pragma unroll
-        for (int d = 0; d < 9; ++d) {
-            lo[d] = GWIN_NONE;
-            hi[d] = -1;
-            row[d] = d;
+        for (int g = 0; g < PLAN_GPT; ++g) {
+            const int64_t gi = min(t * PLAN_GPT + g, ngroups - 1);
+            wl[g] = gwin[gi * GWIN_INTS + q];
+            wh[g] = gwin[gi * GWIN_INTS + 9 + q];
         }
 #pragma unroll
         for (int g = 0; g < PLAN_GPT; ++g) {
-            if (t * PLAN_GPT + g >= ngroups) break;
-            const int32_t *w = s_win + (tid * PLAN_GPT + g) * GWIN_INTS;
-#pragma unroll
-            for (int d = 0; d < 9; ++d) {
-                const int32_t h = w[9 + d];
-                if (h >= 0) {
-                    lo[d] = min(lo[d], w[d]);
-                    hi[d] = max(hi[d], h);
-                }
+            if (t * PLAN_GPT + g < ngroups && wh[g] >= 0) {
+                lo = min(lo, wl[g]);
+                hi = max(hi, wh[g]);
             }
         }
+    }
+    // rank among the 9 rows, and the row of rank q (lanes 9-15 keep their own)
+    int rank = q;
+    if (q < 9) {
+        rank = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8 - i; ++j) {
-                const bool sw = lo[j] > lo[j + 1];
-                const int32_t a = lo[j], b = hi[j], c = row[j];
-                lo[j] = sw ? lo[j + 1] : a;
-                hi[j] = sw ? hi[j + 1] : b;
-                row[j] = sw ? row[j + 1] : c;
-                lo[j + 1] = sw ? a : lo[j + 1];
-                hi[j + 1] = sw ? b : hi[j + 1];
-                row[j + 1] = sw ? c : row[j + 1];
-            }
-        int nr = 0, total = 0;
-        int32_t cur_lo = 0, cur_hi = -2;
-        int32_t delta[9];
-#pragma unroll
-        for (int d = 0; d < 9; ++d) delta[d] = 0;
-#pragma unroll
-        for (int i = 0; i < 9; ++i) {
-            if (lo[i] == GWIN_NONE) continue;  // empty rows sort last
-            if (nr == 0 || lo[i] > cur_hi + 1) {
-                if (nr > 0) total += cur_hi - cur_lo + 1;
-                p[2 + nr] = lo[i];
-                p[11 + nr] = total;
-                cur_lo = lo[i];
-                cur_hi = hi[i];
-                ++nr;
-            } else if (hi[i] > cur_hi) {
-                cur_hi = hi[i];
-            }
-            const int32_t dl = total - cur_lo;  // slot of sorted position q in this range: q + dl
-#pragma unroll
-            for (int d = 0; d < 9; ++d)
-                if (row[i] == d) delta[d] = dl;
+        for (int e = 0; e < 9; ++e) {
+            const int32_t le = __shfl(lo, e, 16);
+            rank += (le < lo || (le == lo && e < q)) ? 1 : 0;
         }
-        if (nr > 0) total += cur_hi - cur_lo + 1;
-        for (int r = nr; r < 9; ++r) {
-            p[2 + r] = 0;
-            p[11 + r] = total;
-        }
+    }
+    int src = q;
 #pragma unroll
-        for (int d = 0; d < 9; ++d) p[20 + d] = delta[d];
-        p[0] = total <= cap ? total : -1;
-        p[1] = nr;
-        p[29] = p[30] = p[31] = 0;
+    for (int e = 0; e < 9; ++e) {
+        const int re = __shfl(rank, e, 16);
+        src = (q < 9 && re == q) ? e : src;
+    }
+    const int32_t slo = __shfl(lo, src, 16), shi = __shfl(hi, src, 16);
+    const bool ne = q < 9 && slo != GWIN_NONE;        // a non-empty row (they come first)
+
+    // ranges: starts, the start of each element's range, ends, lengths, slot bases
+    const int32_t incl_max = team_scan_max(ne ? shi : INT32_MIN, q);
+    const int32_t prev_max = __shfl_up(incl_max, 1, 16);
+    const bool start = ne && (q == 0 || slo > prev_max + 1);
+    const int32_t rlo = team_scan_max(start ? slo : INT32_MIN, q);   // the range's first position
+    const bool next_ne = q < 15 && __shfl_down(ne ? 1 : 0, 1, 16) != 0;
+    const bool next_start = q < 15 && __shfl_down(start ? 1 : 0, 1, 16) != 0;
+    const bool end = ne && (!next_ne || next_start);
+    const int32_t len = end ? incl_max - rlo + 1 : 0;
+    const int32_t incl_len = team_scan_add(len, q);
+    const int32_t base = incl_len - len;                            // slot of the range's first row
+    const int32_t total = __shfl(incl_len, 15, 16);
+    const int32_t rid = team_scan_add(start ? 1 : 0, q) - 1;        // range index (at a start)
+    const int32_t nr = __shfl(rid, 15, 16) + 1;
+
+    int32_t *rec = s_rec + team * PLAN_INTS;
+    if (q < 9) {
+        if (start) {
+            rec[2 + rid] = slo;
+            rec[11 + rid] = base;
+        }
+        if (q >= nr) {
+            rec[2 + q] = 0;
+            rec[11 + q] = total;
+        }
+        rec[20 + src] = ne ? base - rlo : 0;  // slot = sorted position + delta
+    } else if (q == 9) {
+        rec[0] = total <= cap ? total : -1;
+        rec[1] = nr;
+    } else if (q < 13) {
+        rec[29 + (q - 10)] = 0;
     }
     __syncthreads();
-    const int rows = (int)min((int64_t)PLAN_BLOCK, ntiles - t0);
-    int32_t *dst = plan + t0 * PLAN_INTS;
-    for (int e = tid; e < rows * PLAN_INTS; e += PLAN_BLOCK) dst[e] = s_plan[(e / PLAN_INTS) * PLAN_ROW + e % PLAN_INTS];
+    const int rows = (int)min((int64_t)PLAN_TILES, ntiles - t0);
+    if (tid < rows * (PLAN_INTS / 4))
+        ((int4 *)(plan + t0 * PLAN_INTS))[tid] = ((const int4 *)s_rec)[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -544,9 +549,8 @@ int win_plan_build(submconv_rulebook *rb, const uint32_t *blk_taps, int64_t nblk
 {
     const int64_t ntiles = (rb->n + WIN_TILE - 1) / WIN_TILE;
     if (ntiles == 0) return SUBMCONV_OK;
-    // one thread per tile, small blocks: the work is a short serial merge per tile,
-    // so spreading the tiles over every CU is what matters
-    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + PLAN_BLOCK - 1) / PLAN_BLOCK)), dim3(PLAN_BLOCK), 0, s,
+    // 16 lanes per tile, 16 tiles per block
+    hipLaunchKernelGGL(k_win_plan, dim3((unsigned)((ntiles + PLAN_TILES - 1) / PLAN_TILES)), dim3(PLAN_THREADS), 0, s,
                        rb->gwin, rb->ngroups, ntiles, WIN_CAP, rb->plan, blk_taps, nblk, st);
     SC_LAUNCHED("win_plan");
     return SUBMCONV_OK;
