@@ -68,7 +68,8 @@ extern "C" {
 #define SUBMCONV_KERNEL_LOWC 2    /* narrow channels (<= 32), wave shuffles, no matrix cores */
 #define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128} */
 #define SUBMCONV_KERNEL_WINDOW 4  /* matrix cores fed from a tile's neighbourhood staged in LDS
-                                     (bf16, Cin = Cout = 32) */
+                                     (bf16, Cin = Cout = 32, N * 64 <= 2^31 - 1; otherwise
+                                     SUBMCONV_E_UNSUPPORTED) */
 #define SUBMCONV_KERNEL_PERSISTENT 5 /* persistent matrix-core kernel, weights streamed through LDS,
                                         operands gathered into registers (bf16, 64->64 or 128->128,
                                         N * Cin * 2 <= 2^31 - 1; otherwise SUBMCONV_E_UNSUPPORTED) */

@@ -724,7 +724,7 @@ static int launch_mfma(const void *f, const void *w, const float *b, const int32
     return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: Cin must be 32, 64 or 128");
 }
 
-bool window_supported(int cin, int cout, int dtype);
+bool window_supported(int cin, int cout, int dtype, int64_t n);
 bool big_supported(int cin, int cout, int dtype, int64_t n);
 int launch_big(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb, void *out,
                int cin, int cout, int dtype, int flip, hipStream_t s);
@@ -733,7 +733,7 @@ int launch_window(const void *feats, const void *w, const float *bias, const sub
 
 int choose_forward_kernel(int cin, int cout, int dtype, int64_t n)
 {
-    if (window_supported(cin, cout, dtype)) return SUBMCONV_KERNEL_WINDOW;
+    if (window_supported(cin, cout, dtype, n)) return SUBMCONV_KERNEL_WINDOW;
     if (big_supported(cin, cout, dtype, n)) return SUBMCONV_KERNEL_PERSISTENT;
     if (mfma_size(cin) && mfma_size(cout)) return SUBMCONV_KERNEL_MFMA;
     if (pow2_le32(cin) && pow2_le32(cout)) return SUBMCONV_KERNEL_LOWC;

@@ -246,17 +246,19 @@ __device__ __forceinline__ int32_t w32_row_of(const int32_t *__restrict__ perm, 
 }
 
 // Row copy `item` = 4c + q of this wave: slots 64k + 16q .. +15 of chunk k = wave + 8c.
-// rid[item] holds, in lane l, the input row of slot 64k + 16q + l/4.
-__device__ __forceinline__ void w32_copy_rows(char *buf, const uint16_t *__restrict__ feats, int64_t n, int R,
+// rid[item] holds, in lane l, the input row of slot 64k + 16q + l/4.  The rows come
+// through a buffer resource over the features (n * 64 bytes): a row is a 32-bit
+// byte offset, and a missing row an offset past the end, which reads zeros.
+__device__ __forceinline__ void w32_copy_rows(char *buf, __amdgpu_buffer_rsrc_t frs, int64_t n, int R,
                                               int32_t rid, int item, int wave, int lane, int lchunk)
 {
     const int k = wave + W32_WAVES * (item >> 2);
     const int slot0 = 64 * k + 16 * (item & 3);
     if (slot0 >= R) return;
     const int slot = slot0 + (lane >> 2);
-    const void *src = slot < R && (uint32_t)rid < (uint64_t)n ? (const void *)(feats + (int64_t)rid * 32 + lchunk * 8)
-                                                              : (const void *)g_win_zero;
-    __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(buf + slot0 * W32_ROW), 16, 0, 0);
+    const uint32_t voff = slot < R && (uint32_t)rid < (uint32_t)n ? (uint32_t)rid * W32_ROW + (uint32_t)lchunk * 16u
+                                                                  : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(frs, (lds_void *)(buf + slot0 * W32_ROW), 16, voff, 0, 0, 0);
 }
 
 // Copies of a tile's neighbour-table block (whole 1-KB copies; the table
@@ -327,19 +329,30 @@ __device__ __forceinline__ void w32_taps_lds(floatx16 &acc, const char *cur, con
 {
     constexpr int PF = 1;
     constexpr int D0 = K0 / 3;  // this tap half's rows are D0 .. D0 + 4
-    int32_t first[5];
+    // Per (dz,dy) row, once per tile: the LDS slot of its first present cell (its
+    // sorted position plus the plan's offset) and its presence bits (none when the
+    // voxel is not valid).  A tap is then a bit test, at most a popcount, a clamp
+    // and the swizzled address: the tap loop is bound by VALU issue, not by MFMA.
+    int32_t rslot[5];
+    uint32_t rbits[5];
+    const uint32_t mask = ok ? (uint32_t)tbl[9] : 0u;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) first[i] = tbl[D0 + i];
-    const uint32_t mask = (uint32_t)tbl[9];
-    int addr[NK];
+    for (int i = 0; i < 5; ++i) {
+        rslot[i] = D0 + i < 9 ? tbl[D0 + i] + delta[D0 + i] : 0;
+        rbits[i] = D0 + i < 9 ? (mask >> (3 * (D0 + i))) & 7u : 0u;
+    }
+    const int kh16 = kh << 4;
     uint4 b[PF + 1][2];
     auto prep = [&](int j) {
-        const int32_t e = nbr_at_reg<D0>(first, mask, K0 + j);
-        int slot = e + delta[(K0 + j) / 3];
-        slot = (ok && e >= 0 && (unsigned)slot < (unsigned)WIN_CAP) ? slot : WIN_CAP;
-        addr[j] = w32_chunk_addr(slot, kh);
-        b[j % (PF + 1)][0] = *(const uint4 *)(cur + addr[j]);
-        b[j % (PF + 1)][1] = *(const uint4 *)(cur + (addr[j] ^ 32));
+        const int d = (K0 + j) / 3 - D0, jj = (K0 + j) % 3;
+        const uint32_t m = rbits[d];
+        const int32_t off = jj == 0 ? 0 : (jj == 1 ? (int32_t)(m & 1u) : (int32_t)__popc(m & 3u));
+        // a missing neighbour reads the zero slot; an out-of-range slot (not produced
+        // by a consistent table and plan) is clamped to it
+        const uint32_t slot = ((m >> jj) & 1u) ? min((uint32_t)(rslot[d] + off), (uint32_t)WIN_CAP) : (uint32_t)WIN_CAP;
+        const int addr = (int)(slot * W32_ROW) | ((((int)slot << 3) & 0x30) ^ kh16);  // w32_chunk_addr(slot, kh)
+        b[j % (PF + 1)][0] = *(const uint4 *)(cur + addr);
+        b[j % (PF + 1)][1] = *(const uint4 *)(cur + (addr ^ 32));
     };
 #pragma unroll
     for (int j = 0; j < PF; ++j) prep(j);
@@ -396,6 +409,7 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
     const int col = lane & 31, kh = lane >> 5;
     const int cb = wave & 3, th = wave >> 2;  // column block, tap half (taps 0-13 or 14-26)
     const int lchunk = w32_lane_chunk(lane);
+    const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc((void *)feats, 0, (int)(n * W32_ROW), 0x00020000);
 
     // tiles of this block: the XCD's contiguous run, dealt round-robin to its blocks
     const int xcd = blockIdx.x & 7, bpx = gridDim.x >> 3, jb = blockIdx.x >> 3;
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
         for (int c = 0; c < W32_CHUNKS; ++c) rows[c] = w32_row_of(perm, n, g0, 64 * (wave + W32_WAVES * c) + lane);
         w32_expand(rows, rid, lane);
 #pragma unroll
-        for (int it = 0; it < 4 * W32_CHUNKS; ++it) w32_copy_rows(buf0, feats, n, g0.R, rid[it], it, wave, lane, lchunk);
+        for (int it = 0; it < 4 * W32_CHUNKS; ++it) w32_copy_rows(buf0, frs, n, g0.R, rid[it], it, wave, lane, lchunk);
         w32_copy_table(buf0, nbr_sp, perm, n, tile_at(0), wave, lane);
         if (count > 1) {
             const W32Ranges g1 = w32_ranges(pv1);
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
             if constexpr (j == 0) {
                 if (more1) w32_copy_table(nxt, nbr_sp, perm, n, tile_at(i + 1), wave, lane);
             } else if constexpr (j <= 8) {
-                if (more1) w32_copy_rows(nxt, feats, n, R1, rid[j - 1], j - 1, wave, lane, lchunk);
+                if (more1) w32_copy_rows(nxt, frs, n, R1, rid[j - 1], j - 1, wave, lane, lchunk);
             } else if constexpr (j == 9) {
                 if (pend_out) {
 #pragma unroll
@@ -566,16 +580,17 @@ static int device_cus(int dev)
     return cus;
 }
 
-bool window_supported(int cin, int cout, int dtype)
+bool window_supported(int cin, int cout, int dtype, int64_t n)
 {
-    return dtype == SUBMCONV_BF16 && cin == 32 && cout == 32;
+    // feature rows are addressed by 32-bit byte offsets (a buffer resource)
+    return dtype == SUBMCONV_BF16 && cin == 32 && cout == 32 && n * W32_ROW <= INT32_MAX;
 }
 
 int launch_window(const void *feats, const void *w, const float *bias, const submconv_rulebook *rb,
                   void *out, int cin, int cout, int dtype, int flip, hipStream_t s)
 {
-    if (!window_supported(cin, cout, dtype))
-        return fail(SUBMCONV_E_UNSUPPORTED, "window kernel: bf16 with Cin = Cout = 32 only");
+    if (!window_supported(cin, cout, dtype, rb->n))
+        return fail(SUBMCONV_E_UNSUPPORTED, "window kernel: bf16 with Cin = Cout = 32 and N * 64 <= 2^31 - 1 only");
     const int64_t ntiles = (rb->n + WIN_TILE - 1) / WIN_TILE;
     int blocks = device_cus(rb->device) & ~7;
     if (blocks < 8) blocks = 8;
