@@ -257,6 +257,15 @@ def workload(idx: int) -> tuple:
     return w, _COORD_CACHE[idx]
 
 
+def device_normal(n: int, c: int, seed: int, device):
+    """Standard-normal float32 [n, c] drawn on `device` by torch's seeded generator, for
+    sets too large to draw on the host (the oracle then reads back only the rows it needs)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((n, c), generator=g, device=device, dtype=torch.float32)
+
+
 def make_values(n: int, cin: int, cout: int, seed: int, weight_std: Optional[float] = None,
                 bias: str = "uniform") -> tuple:
     """fp32 feats [n,cin], KRSC weight [cout,3,3,3,cin], bias [cout].

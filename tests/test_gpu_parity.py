@@ -353,6 +353,47 @@ def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
     assert_close(got, expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
 
 
+# The windowed kernel addresses bf16 feature rows by 32-bit byte offsets, so it takes
+# N * 64 <= 2^31 - 1; just past that, forcing it is refused and the automatic choice
+# runs another kernel.  A dense slab (128 x 512 x 512 voxels, C order, plus 1001 of the
+# next plane), so the neighbours of the sampled rows follow from their index.
+def test_forward_window_size_cap():
+    plane, nslab = 512 * 512, 128 * 512 * 512
+    n = nslab + 1001
+    assert n * 64 > 2 ** 31 - 1 >= (n - 1002) * 64
+    i = np.arange(n, dtype=np.int64)
+    c = np.zeros((n, 4), np.int32)
+    c[:, 1], c[:, 2], c[:, 3] = i // plane, (i // 512) % 512, i % 512
+    _, weight, b = synth.make_values(1, 32, 32, 9)
+    _, tw, tb, _, w64 = device_values(np.zeros((1, 32), np.float32), weight, b, "bf16")
+    tf = synth.device_normal(n, 32, 9, DEV).to(torch.bfloat16)
+    rb = build(c, 512, 1)
+    note("window cap: forced window refused, n=%d" % n)
+    with pytest.raises(sc.SubmconvError) as e:
+        sc.submconv_forward(tf, tw, tb, rb, variant=sc.KERNEL_WINDOW)
+    assert e.value.status == -4
+    note("window cap: automatic choice, n=%d" % n)
+    out = sc.submconv_forward(tf, tw, tb, rb)
+    pick = np.random.default_rng(5).choice(n, size=2000, replace=False)
+    pick = np.unique(np.concatenate([pick, [0, n - 1, nslab - plane, nslab - 1, nslab, nslab + 511]]))
+    z, y, x = pick // plane, (pick // 512) % 512, pick % 512
+    table = np.full((len(pick), 27), -1, np.int64)
+    for k in range(27):
+        dz, dy, dx = ref.tap_offset(k)
+        nz, ny, nx = z + dz, y + dy, x + dx
+        j = nz * plane + ny * 512 + nx
+        ok = (nz >= 0) & (ny >= 0) & (ny < 512) & (nx >= 0) & (nx < 512) & (j < n)
+        table[ok, k] = j[ok]
+    rows, inv = np.unique(table[table >= 0], return_inverse=True)
+    compact = np.full(table.shape, -1, np.int64)
+    compact[table >= 0] = inv
+    f64 = to_f64(tf[torch.from_numpy(rows).to(DEV)])
+    expect = ref.forward(f64, w64, b, compact)
+    got = to_f64(out[torch.from_numpy(pick).to(DEV)])
+    assert_close(got, expect, "bf16", "window cap, automatic kernel")
+    rb.free()
+
+
 def test_forward_workload4_sampled():
     w, c = synth.workload(4)
     sampled_check(c, w.res, w.batch, w.cin, w.cout, "bf16", w.value_seed, w.bias, w.weight_std)
