@@ -353,26 +353,28 @@ def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
     assert_close(got, expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
 
 
-# The windowed kernel addresses bf16 feature rows by 32-bit byte offsets, so it takes
-# N * 64 <= 2^31 - 1; just past that, forcing it is refused and the automatic choice
-# runs another kernel.  A dense slab (128 x 512 x 512 voxels, C order, plus 1001 of the
-# next plane), so the neighbours of the sampled rows follow from their index.
-def test_forward_window_size_cap():
-    plane, nslab = 512 * 512, 128 * 512 * 512
+# Kernels that address bf16 feature rows by 32-bit byte offsets take N * Cin * 2 <=
+# 2^31 - 1 (windowed: 32 channels; persistent: 64 and 128).  Just past the cap,
+# forcing the kernel is refused and the automatic choice runs another one.  A dense
+# slab (depth x 512 x 512 voxels, C order, plus 1001 of the next plane), so the
+# neighbours of the sampled rows follow from their index.
+@pytest.mark.parametrize("ch,kernel,depth", [(32, "window", 128), (64, "persistent", 64), (128, "persistent", 32)])
+def test_forward_size_caps(ch, kernel, depth):
+    plane, nslab = 512 * 512, depth * 512 * 512
     n = nslab + 1001
-    assert n * 64 > 2 ** 31 - 1 >= (n - 1002) * 64
+    assert n * ch * 2 > 2 ** 31 - 1 >= (n - 1002) * ch * 2
     i = np.arange(n, dtype=np.int64)
     c = np.zeros((n, 4), np.int32)
     c[:, 1], c[:, 2], c[:, 3] = i // plane, (i // 512) % 512, i % 512
-    _, weight, b = synth.make_values(1, 32, 32, 9)
-    _, tw, tb, _, w64 = device_values(np.zeros((1, 32), np.float32), weight, b, "bf16")
-    tf = synth.device_normal(n, 32, 9, DEV).to(torch.bfloat16)
+    _, weight, b = synth.make_values(1, ch, ch, 9)
+    _, tw, tb, _, w64 = device_values(np.zeros((1, ch), np.float32), weight, b, "bf16")
+    tf = synth.device_normal(n, ch, 9, DEV).to(torch.bfloat16)
     rb = build(c, 512, 1)
-    note("window cap: forced window refused, n=%d" % n)
+    note("size cap: forced %s refused, n=%d, %d ch" % (kernel, n, ch))
     with pytest.raises(sc.SubmconvError) as e:
-        sc.submconv_forward(tf, tw, tb, rb, variant=sc.KERNEL_WINDOW)
+        sc.submconv_forward(tf, tw, tb, rb, variant=KERNELS[kernel])
     assert e.value.status == -4
-    note("window cap: automatic choice, n=%d" % n)
+    note("size cap: automatic choice, n=%d, %d ch" % (n, ch))
     out = sc.submconv_forward(tf, tw, tb, rb)
     pick = np.random.default_rng(5).choice(n, size=2000, replace=False)
     pick = np.unique(np.concatenate([pick, [0, n - 1, nslab - plane, nslab - 1, nslab, nslab + 511]]))
@@ -390,7 +392,7 @@ def test_forward_window_size_cap():
     f64 = to_f64(tf[torch.from_numpy(rows).to(DEV)])
     expect = ref.forward(f64, w64, b, compact)
     got = to_f64(out[torch.from_numpy(pick).to(DEV)])
-    assert_close(got, expect, "bf16", "window cap, automatic kernel")
+    assert_close(got, expect, "bf16", "size cap %d ch, automatic kernel" % ch)
     rb.free()
 
 
