@@ -575,38 +575,62 @@ __global__ __launch_bounds__(256) void k_d2s_count(const uint8_t *__restrict__ m
     cnt[i] = c;
 }
 
-// Children of the two expansions: one thread per (voxel, slot, vector of a child row),
-// V = uint4 when rows are whole 16-byte vectors, else the element type.  REPL: the
-// child copies the parent's whole row (masked upsample); otherwise it takes the
-// slot's channels of an 8-times-wider row (depth_to_space).  mask == nullptr: every
-// slot, child 8 cell + slot; else the masked slots at base[cell] + (masked slots before).
-template <typename V, bool REPL>
+// Children of the two expansions: one thread per (voxel, vector of a child row), over
+// the 8 slots in order; V = uint4 when rows are whole 16-byte vectors, else the element
+// type.  REPL: the child copies the parent's whole row (masked upsample, read once);
+// otherwise it takes the slot's channels of an 8-times-wider row (depth_to_space).
+// mask == nullptr: every slot, child 8 cell + slot; else the masked slots, in slot
+// order, from base[cell].  MASK8: mask rows are 8-byte aligned and read as one word.
+template <typename V, bool REPL, bool MASK8>
 __global__ __launch_bounds__(256) void k_expand(const int4 *__restrict__ cc, const V *__restrict__ cf,
                                                 const uint8_t *__restrict__ mask, const uint32_t *__restrict__ base,
                                                 int64_t m, int vpr, int4 *__restrict__ out_coords,
                                                 V *__restrict__ out_feats)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m x 8 x vpr
-    if (e >= m * 8 * vpr) return;
-    const int64_t cell = e / (8 * vpr);
-    const int rest = (int)(e - cell * 8 * vpr);
-    const int slot = rest / vpr, vi = rest - slot * vpr;
-    int64_t dst;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m x vpr
+    if (e >= m * vpr) return;
+    const int64_t cell = e / vpr;
+    const int vi = (int)(e - cell * vpr);
+    uint32_t bits = 0xFFu;
+    int64_t dst = cell * 8;
     if (mask) {
-        const uint8_t *mr = mask + cell * 8;
-        if (!mr[slot]) return;
-        int before = 0;
-        for (int q = 0; q < slot; ++q) before += mr[q] != 0;
-        dst = (int64_t)base[cell] + before;
-        if (dst >= 8 * m) return;
-    } else {
-        dst = cell * 8 + slot;
+        bits = 0;
+        if (MASK8) {
+            const unsigned long long w = *(const unsigned long long *)(mask + cell * 8);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bits |= ((w >> (8 * q)) & 0xFFull) ? 1u << q : 0u;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bits |= mask[cell * 8 + q] ? 1u << q : 0u;
+        }
+        dst = base[cell];
     }
-    out_feats[dst * vpr + vi] = REPL ? cf[cell * vpr + vi] : cf[e];
-    if (vi == 0) {
-        const int4 p = cc[cell];
-        out_coords[dst] = make_int4(p.x, 2 * p.y + (slot & 1), 2 * p.z + ((slot >> 1) & 1), 2 * p.w + (slot >> 2));
+    V v{};
+    if (REPL) v = cf[cell * vpr + vi];
+    int4 p = make_int4(0, 0, 0, 0);
+    if (vi == 0) p = cc[cell];
+#pragma unroll
+    for (int slot = 0; slot < 8; ++slot) {
+        if (!((bits >> slot) & 1u)) continue;
+        if (dst >= 8 * m) break;
+        out_feats[dst * vpr + vi] = REPL ? v : cf[(cell * 8 + slot) * vpr + vi];
+        if (vi == 0)
+            out_coords[dst] = make_int4(p.x, 2 * p.y + (slot & 1), 2 * p.z + ((slot >> 1) & 1), 2 * p.w + (slot >> 2));
+        ++dst;
     }
+}
+
+template <typename V, bool REPL>
+static void launch_expand_v(const int32_t *cc, const V *cf, const uint8_t *mask, const uint32_t *base, int64_t m,
+                            int vpr, int32_t *out_coords, V *out_feats, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((m * vpr + 255) / 256);
+    if (mask && ((uintptr_t)mask & 7) == 0)
+        hipLaunchKernelGGL((k_expand<V, REPL, true>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, cf, mask, base, m,
+                           vpr, (int4 *)out_coords, out_feats);
+    else
+        hipLaunchKernelGGL((k_expand<V, REPL, false>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, cf, mask, base,
+                           m, vpr, (int4 *)out_coords, out_feats);
 }
 
 template <bool REPL>
@@ -616,17 +640,14 @@ static int launch_expand(const int32_t *cc, const void *cf, const uint8_t *mask,
     const int es = dtype == SUBMCONV_F32 ? 4 : 2;
     const int64_t row = (int64_t)c * es;  // bytes of a child row
     const bool vec = row % 16 == 0 && ((uintptr_t)cf & 15) == 0 && ((uintptr_t)out_feats & 15) == 0;
-    const int vpr = vec ? (int)(row / 16) : c;
-    const unsigned grid = (unsigned)((m * 8 * vpr + 255) / 256);
     if (vec)
-        hipLaunchKernelGGL((k_expand<uint4, REPL>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, (const uint4 *)cf,
-                           mask, base, m, vpr, (int4 *)out_coords, (uint4 *)out_feats);
+        launch_expand_v<uint4, REPL>(cc, (const uint4 *)cf, mask, base, m, (int)(row / 16), out_coords,
+                                     (uint4 *)out_feats, s);
     else if (dtype == SUBMCONV_F32)
-        hipLaunchKernelGGL((k_expand<float, REPL>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, (const float *)cf,
-                           mask, base, m, vpr, (int4 *)out_coords, (float *)out_feats);
+        launch_expand_v<float, REPL>(cc, (const float *)cf, mask, base, m, c, out_coords, (float *)out_feats, s);
     else
-        hipLaunchKernelGGL((k_expand<uint16_t, REPL>), dim3(grid), dim3(256), 0, s, (const int4 *)cc,
-                           (const uint16_t *)cf, mask, base, m, vpr, (int4 *)out_coords, (uint16_t *)out_feats);
+        launch_expand_v<uint16_t, REPL>(cc, (const uint16_t *)cf, mask, base, m, c, out_coords, (uint16_t *)out_feats,
+                                        s);
     SC_LAUNCHED("expand");
     return SUBMCONV_OK;
 }
