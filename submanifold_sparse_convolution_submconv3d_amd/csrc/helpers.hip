@@ -37,6 +37,26 @@ __global__ __launch_bounds__(256) void k_subdivide_coords(const int4 *__restrict
     out[e] = make_int4(c.x, 2 * c.y + (q >> 2), 2 * c.z + ((q >> 1) & 1), 2 * c.w + (q & 1));
 }
 
+// Row and unit of a flat thread index with `per` units per row (per > 0, a kernel
+// argument, so the test is uniform): a shift when per is a power of two, else a
+// division, 32-bit while the index fits.  A 64-bit division by a runtime value costs
+// more than the 16-byte move these streaming kernels do per thread.
+__device__ __forceinline__ int64_t split_index(int64_t e, int per, int &u)
+{
+    if ((per & (per - 1)) == 0) {
+        u = (int)(e & (per - 1));
+        return e >> __builtin_ctz((unsigned)per);
+    }
+    if ((uint64_t)e <= 0xFFFFFFFFull) {
+        const uint32_t q = (uint32_t)e / (uint32_t)per;
+        u = (int)((uint32_t)e - q * (uint32_t)per);
+        return (int64_t)q;
+    }
+    const int64_t q = e / per;
+    u = (int)(e - q * per);
+    return q;
+}
+
 // Copy each parent row to its 8 children in units V (16-byte vectors or 4-byte words;
 // rows are whole units).
 template <typename V>
@@ -45,8 +65,8 @@ __global__ __launch_bounds__(256) void k_subdivide_feats(const V *__restrict__ i
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over 8n rows x words
     if (e >= 8 * n * words) return;
-    const int64_t child = e / words;
-    const int wi = (int)(e - child * words);
+    int wi;
+    const int64_t child = split_index(e, words, wi);
     out[e] = in[(child >> 3) * words + wi];
 }
 
@@ -57,8 +77,8 @@ __global__ __launch_bounds__(256) void k_subdivide_feats16(const uint16_t *__res
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= 8 * n * c) return;
-    const int64_t child = e / c;
-    const int ci = (int)(e - child * c);
+    int ci;
+    const int64_t child = split_index(e, c, ci);
     out[e] = in[(child >> 3) * c + ci];
 }
 
@@ -168,8 +188,8 @@ __global__ __launch_bounds__(256) void k_s2d_scatter(const K *__restrict__ sk,
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= n * c) return;
-    const int64_t s = e / c;
-    const int ci = (int)(e - s * c);
+    int ci;
+    const int64_t s = split_index(e, c, ci);
     const int slot = (int)(sk[s] & 7);
     const int64_t m = seg[s];
     const uint32_t src = (uint32_t)perm[s];
@@ -219,9 +239,9 @@ __global__ __launch_bounds__(256) void k_down_reduce(const int32_t *__restrict__
                                                      const T *__restrict__ feats, T *__restrict__ out_feats)
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over (at most n coarse voxels) x c
-    const int64_t m = e / c;
+    int ci;
+    const int64_t m = split_index(e, c, ci);
     if (m >= (int64_t)*total) return;
-    const int ci = (int)(e - m * c);
     const int64_t s0 = start[m];
     float acc = MEAN ? 0.f : -__builtin_huge_valf();
     int cnt = 0;
@@ -335,9 +355,10 @@ __global__ __launch_bounds__(256) void k_cg_pool(const int32_t *__restrict__ chi
 {
     const int groups = c / V;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t m = e / groups;
+    int gi;
+    const int64_t m = split_index(e, groups, gi);
     if (m >= (int64_t)*total) return;
-    const int c0 = (int)(e - m * groups) * V;
+    const int c0 = gi * V;
     float acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = MEAN ? 0.f : -__builtin_huge_valf();
@@ -371,10 +392,11 @@ __global__ __launch_bounds__(256) void k_cg_s2d(const int32_t *__restrict__ chil
                                                 uint8_t *__restrict__ out_mask)
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over rows x 8 slots x units per row
-    const int64_t ms = e / upr;
+    int ui;
+    const int64_t ms = split_index(e, upr, ui);
     const int64_t m = ms >> 3;
     if (m >= (int64_t)*total) return;
-    const int ui = (int)(e - ms * upr);
+
     const int32_t r = child[ms];
     out_feats[e] = r >= 0 ? feats[(int64_t)r * upr + ui] : U{};
     if (ui == 0 && out_mask) out_mask[ms] = r >= 0;
@@ -589,8 +611,8 @@ __global__ __launch_bounds__(256) void k_expand(const int4 *__restrict__ cc, con
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m x vpr
     if (e >= m * vpr) return;
-    const int64_t cell = e / vpr;
-    const int vi = (int)(e - cell * vpr);
+    int vi;
+    const int64_t cell = split_index(e, vpr, vi);
     uint32_t bits = 0xFFu;
     int64_t dst = cell * 8;
     if (mask) {
