@@ -230,11 +230,13 @@ __device__ __forceinline__ W32Ranges w32_ranges(int pv)
     return g;
 }
 
-// Input row of `slot` (-1 past R): one lane per slot.
+// Input row of `slot` (slots < R): one lane per slot.
+// The load is unconditional (a slot past R reads a clamped position whose value the
+// copy ignores) and its value is not inspected here, so it is not waited for until
+// the copies of its tile use it.
 __device__ __forceinline__ int32_t w32_row_of(const int32_t *__restrict__ perm, int64_t n, const W32Ranges &g,
                                               int slot)
 {
-    if (slot >= g.R) return -1;
     int32_t b = g.base[0];
 #pragma unroll
     for (int q = 1; q < 9; ++q) {
@@ -242,7 +244,7 @@ __device__ __forceinline__ int32_t w32_row_of(const int32_t *__restrict__ perm, 
         b = slot >= g.off[q] ? g.base[q] : b;
     }
     const int32_t pos = b + slot;
-    return (uint32_t)pos < (uint64_t)n ? perm[pos] : -1;
+    return perm[pos < 0 ? 0 : (pos >= (int32_t)n ? (int32_t)n - 1 : pos)];
 }
 
 // Row copy `item` = 4c + q of this wave: slots 64k + 16q .. +15 of chunk k = wave + 8c.
@@ -305,7 +307,7 @@ __device__ __forceinline__ void w32_mfma(floatx16 &acc, const uint4 &a, const ui
 }
 
 template <int J> using w32_item = std::integral_constant<int, J>;
-constexpr int W32_ITEMS = 13;  // side-work items per tile (see the kernel)
+constexpr int W32_ITEMS = 10;  // side-work items per tile (see the kernel)
 
 // f(w32_item<I>{}), ..., f(w32_item<N - 1>{}) with compile-time indices
 template <int I, int N, typename F>
@@ -404,6 +406,8 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
     // object, so reads of one buffer need not wait for copies into the other
     __shared__ __attribute__((aligned(1024))) char buf0[W32_BUF];
     __shared__ __attribute__((aligned(1024))) char buf1[W32_BUF];
+    // the bias, read once: a global load in the reduction waits for every copy in flight
+    __shared__ __attribute__((aligned(16))) float s_bias[32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, kh = lane >> 5;
@@ -418,9 +422,10 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
     const int64_t count = first < t_end ? (t_end - first + bpx - 1) / bpx : 0;
     if (count == 0) return;
 
-    // the zero slot of both buffers
+    // the zero slot of both buffers, and the bias
     if (tid < 4) *(uint4 *)(buf0 + WIN_CAP * W32_ROW + tid * 16) = make_uint4(0, 0, 0, 0);
     else if (tid < 8) *(uint4 *)(buf1 + WIN_CAP * W32_ROW + (tid - 4) * 16) = make_uint4(0, 0, 0, 0);
+    if (tid >= 64 && tid < 96) s_bias[tid - 64] = bias ? bias[tid - 64] : 0.f;
 
     // weights of this wave's taps: lane holds output channel `col`, input
     // channels 16h + 8kh .. +7 (the last slot of the second half is unused)
@@ -470,14 +475,21 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
         int delta[9];
 #pragma unroll
         for (int d = 0; d < 9; ++d) delta[d] = plan_get(pv0, 20 + d);
-        W32Ranges g2;
         const bool more1 = i + 1 < count, more2 = i + 2 < count;
         w32_expand(rows, rid, lane);  // row numbers of tile i+1, for its copies
-        int pv3 = 0;
+        // The plan of tile i+3 and the row numbers of tile i+2, first used in the next
+        // tiles, issued here in code both tap halves share: issued inside the halves they
+        // were merged by register copies after them, and with copies into LDS in flight
+        // a copy waits for every load outstanding.
+        const int pv3 = plan_load(i + 3);
+        if (more2) {
+            const W32Ranges g2 = w32_ranges(pv2);
+#pragma unroll
+            for (int c = 0; c < W32_CHUNKS; ++c) rows[c] = w32_row_of(perm, n, g2, 64 * (wave + W32_WAVES * c) + lane);
+        }
 
         // side work, one item per tap: 0 the table block of tile i+1 (first: it comes
-        // from HBM, read once), 1-8 its row copies, 9 the stores of tile i-1, 10 the
-        // plan of tile i+3, 11-12 row numbers of tile i+2
+        // from HBM, read once), 1-8 its row copies, 9 the stores of tile i-1
         auto side = [&](auto jc) {
             constexpr int j = decltype(jc)::value;
             if constexpr (j == 0) {
@@ -489,12 +501,6 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
 #pragma unroll
                     for (int g = 0; g < 4; ++g) *(uint2 *)(pend_out + 8 * g) = make_uint2(pend[2 * g], pend[2 * g + 1]);
                 }
-            } else if constexpr (j == 10) {
-                pv3 = plan_load(i + 3);
-            } else if constexpr (j == 11 || j == 12) {
-                constexpr int c = j - 11;
-                if constexpr (c == 0) g2 = w32_ranges(pv2);
-                if (more2) rows[c] = w32_row_of(perm, n, g2, 64 * (wave + W32_WAVES * c) + lane);
             }
         };
 
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
         if (th == 1) {  // the second tap half also adds the bias (once per output)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 bv = bias ? *(const float4 *)(bias + 8 * g + 4 * kh) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 bv = *(const float4 *)(s_bias + 8 * g + 4 * kh);
                 red[64 * g] = make_float4(acc[4 * g] + bv.x, acc[4 * g + 1] + bv.y, acc[4 * g + 2] + bv.z,
                                           acc[4 * g + 3] + bv.w);
             }
