@@ -192,8 +192,9 @@ constexpr int W32_TBL = 5 * 1024 + 512;                       // neighbour rows 
                                                               // then the tile's 128 sort-order row numbers
 constexpr int W32_PERM = WIN_SLOTS * 64 + 5 * 1024;           // offset of those row numbers
 constexpr int W32_BUF = WIN_SLOTS * W32_ROW + W32_TBL;        // one buffer
-constexpr int W32_LDS = 2 * W32_BUF;                          // 159744 B, two buffers
-static_assert(W32_LDS <= 160 * 1024, "LDS budget");
+constexpr int W32_LDS = 2 * W32_BUF;                          // 142336 B, two buffers
+constexpr int W32_RED = 4 * 4 * 64 * 16;                       // partial sums of the second tap half
+static_assert(W32_LDS + W32_RED + 32 * 4 <= 160 * 1024, "LDS budget (buffers, partial sums, bias)");
 static_assert(WIN_TILE * NBR_INTS * 4 + 512 <= W32_TBL, "table block");
 
 __device__ __forceinline__ int w32_chunk_addr(int slot, int chunk)  // byte offset of a row chunk
@@ -408,6 +409,9 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
     __shared__ __attribute__((aligned(1024))) char buf1[W32_BUF];
     // the bias, read once: a global load in the reduction waits for every copy in flight
     __shared__ __attribute__((aligned(16))) float s_bias[32];
+    // the second tap half's partial sums (its own buffer: writing them needs no wait for
+    // the other waves to finish reading the current rows)
+    __shared__ __attribute__((aligned(16))) float4 s_red[W32_RED / 16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, kh = lane >> 5;
@@ -517,9 +521,8 @@ __global__ __launch_bounds__(512, 2) void k_conv_win32(const uint16_t *__restric
             if (th == 0) w32_taps_global<0, 14>(acc, feats, perm, n, tbl, valid, kh, wf, side);
             else w32_taps_global<14, 13>(acc, feats, perm, n, tbl, valid, kh, wf, side);
         }
-        // combine the two tap halves through LDS (the current rows are no longer read)
-        lds_barrier();
-        float4 *red = (float4 *)(cur + cb * 4096) + lane;
+        // combine the two tap halves through LDS
+        float4 *red = s_red + cb * 256 + lane;
         if (th == 1) {  // the second tap half also adds the bias (once per output)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
