@@ -281,6 +281,47 @@ def bench_chain(args):
     return 0
 
 
+def bench_peaks(args):
+    """What the box reaches on plain work, beside the vendor peaks the roofline fractions use: a device
+    copy (torch's copy kernel, 1 GiB each way) and dense GEMMs (torch.matmul, 8192^3, bf16 and fp32 with
+    TF32 off; the vendor's library GEMMs, not this package's code)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.backends.cuda.matmul.allow_tf32 = False
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    copy_ms = timed(lambda: b.copy_(a), max(args.steps, 10))
+    copy_tbps = 2.0 * a.numel() * 4 / (copy_ms * 1e-3) / 1e12
+    del a, b
+    out = {"metric": "measured device copy and dense GEMM rates (context for the roofline peaks)",
+           "copy_TBps": copy_tbps, "copy_frac_of_8TBps": copy_tbps / 8.0}
+    m = 8192
+    for name, dt, peak in (("bf16", torch.bfloat16, 2500.0), ("f32", torch.float32, 157.3)):
+        x = torch.randn(m, m, device=dev).to(dt)
+        y = torch.randn(m, m, device=dev).to(dt)
+        ms = timed(lambda: torch.matmul(x, y), 5 if dt == torch.float32 else 10)
+        tf = 2.0 * m ** 3 / (ms * 1e-3) / 1e12
+        out["gemm_%s_TFLOPs" % name] = tf
+        out["gemm_%s_frac_of_peak" % name] = tf / peak
+        del x, y
+    out["n_gpus"] = 1
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +336,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the second dtype and the cold-cache pass")
     ap.add_argument("--chain", action="store_true",
                     help="time the decoder-like chain 64^3 -> 512^3 (18 convolutions) instead (own JSON line)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure a device copy and dense library GEMMs instead (context; own JSON line)")
     ap.add_argument("--helpers", action="store_true",
                     help="time the coordinate-set helpers on the 512^3 subdivided shell instead (own JSON line)")
     args = ap.parse_args()
@@ -302,6 +345,8 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         return 2
+    if args.peaks:
+        return bench_peaks(args)
     if args.helpers:
         return bench_helpers(args)
     if args.chain:
