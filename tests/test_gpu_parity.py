@@ -198,7 +198,8 @@ def run_forward(c, res, batch, cin, cout, dtype, kernel, flip, seed=0, bias="uni
 @pytest.mark.parametrize("kernel,cin,cout", [("generic", 16, 16), ("generic", 3, 5), ("generic", 24, 40),
                                              ("lowc", 16, 16), ("lowc", 8, 32), ("lowc", 32, 16), ("lowc", 32, 32),
                                              ("mfma", 32, 32), ("mfma", 64, 64), ("mfma", 128, 128),
-                                             ("mfma", 32, 128), ("mfma", 128, 64),
+                                             ("mfma", 32, 128), ("mfma", 128, 64), ("mfma", 32, 64),
+                                             ("mfma", 64, 128), ("mfma", 64, 32), ("mfma", 128, 32),
                                              ("persistent", 64, 64), ("persistent", 128, 128)])
 def test_forward_random_set(dtype, flip, kernel, cin, cout):
     if kernel == "persistent" and dtype == "f32":
