@@ -227,6 +227,12 @@ struct MfmaShape {
     static_assert(G >= 1 && RT >= 1, "channel counts too small for the matrix-core path");
 };
 
+// Persistent: one block per CU takes a balanced contiguous run of 32-voxel columns
+// and walks it in rounds.  In a full round each of the 4 waves owns one column and
+// all Cout; in the last, partial round the waves share the remaining columns and
+// split Cout (1 column: a quarter each, 2 columns: a half each, 3 columns: one wave
+// idles).  With one block per CU, a grid of 128-voxel blocks ran whole extra rounds
+// on some CUs while the rest idled (10-14% at 146k voxels).
 template <typename T, int CIN, int COUT, int VT>
 __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
                                                    const T *__restrict__ w,
@@ -237,6 +243,7 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
 {
     using S = MfmaShape<T, CIN, COUT, VT>;
     constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
+    static_assert(VT == 1 && RT % 4 == 0, "one column per wave, Cout split four ways in a partial round");
     // two weight objects when taps rotate through two buffers: the compiler tracks
     // direct global-to-LDS copies per object, so reading tap k's buffer does not wait
     // for the copy of tap k+1 into the other (and, through it, for every load in flight)
@@ -246,8 +253,11 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
+    const int64_t ncols = (n + 31) / 32;
     const int64_t blk = xcd_block();
-    const int64_t vbase = (blk * 4 + wave) * (VT * 32);
+    const int64_t c0 = ncols * blk / gridDim.x, c1 = ncols * (blk + 1) / gridDim.x;
+    const int m = (int)(c1 - c0);
+    if (m <= 0) return;
 
     // copy weight tap k (kernel tap k' = flip ? 26-k : k) into the LDS buffer `dst`
     auto stage_w = [&](int k, uint4 *dst) {
@@ -258,116 +268,120 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
             __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)&dst[f * 64], 16, 0, 0);
         }
     };
-    // input rows of this wave's voxels' tap-k neighbours, looked up a tap before
-    // their fragments are fetched: the perm loads are unconditional and not
-    // inspected here, so they overlap a tap of MFMAs instead of being waited on
-    struct Look {
-        int32_t r[VT];
-        bool ok[VT];
-    };
-    auto lookup = [&](int k) -> Look {
-        Look L;
-#pragma unroll
-        for (int t = 0; t < VT; ++t) {
-            const int64_t v = vbase + 32 * t + l32;
-            const int32_t e = v < n ? nbr_at(sN + (wave * VT * 32 + 32 * t + l32) * NBR_INTS, k) : -1;
-            L.ok[t] = (uint32_t)e < (uint64_t)n;
-            L.r[t] = perm[L.ok[t] ? e : 0];
-        }
-        return L;
-    };
-    // feature fragments of the looked-up rows (zeros for missing neighbours)
-    auto fetch = [&](const Look &L, uint4 (&F)[VT][G]) -> bool {
-        bool any = false;
-        int32_t j[VT];
-#pragma unroll
-        for (int t = 0; t < VT; ++t) {
-            j[t] = L.ok[t] && (uint32_t)L.r[t] < (uint64_t)n ? L.r[t] : -1;
-            any |= j[t] >= 0;
-        }
-#pragma unroll
-        for (int t = 0; t < VT; ++t)
+
+    // One round: tap loop of this wave's column `col` (its voxels at sN rows
+    // (col - col0) * 32 ..) for output tiles r0 .. r0 + RTW - 1; inactive waves take
+    // part in the copies and barriers only.
+    auto round = [&](auto rtw, int64_t col0, int64_t col, int r0, bool active) {
+        constexpr int RTW = decltype(rtw)::value;
+        const int64_t vbase = col * 32;
+        const int srow = (int)(col - col0) * 32;
+
+        // input rows of this wave's voxels' tap-k neighbours, looked up a tap before
+        // their fragments are fetched: the perm loads are unconditional and not
+        // inspected here, so they overlap a tap of MFMAs instead of being waited on
+        struct Look {
+            int32_t r;
+            bool ok;
+        };
+        auto lookup = [&](int k) -> Look {
+            const int64_t v = vbase + l32;
+            const int32_t e = active && v < n ? nbr_at(sN + (srow + l32) * NBR_INTS, k) : -1;
+            Look L;
+            L.ok = (uint32_t)e < (uint64_t)n;
+            L.r = perm[L.ok ? e : 0];
+            return L;
+        };
+        // feature fragments of the looked-up rows (zeros for missing neighbours)
+        auto fetch = [&](const Look &L, uint4 (&F)[G]) -> bool {
+            const int32_t j = L.ok && (uint32_t)L.r < (uint64_t)n ? L.r : -1;
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                F[t][g] = j[t] >= 0 ? *(const uint4 *)(feats + (int64_t)j[t] * CIN + (2 * g + half) * EPC)
-                                    : make_uint4(0, 0, 0, 0);
-        return any;
-    };
+                F[g] = j >= 0 ? *(const uint4 *)(feats + (int64_t)j * CIN + (2 * g + half) * EPC) : make_uint4(0, 0, 0, 0);
+            return j >= 0;
+        };
 
-    floatx16 acc[RT][VT];
+        floatx16 acc[RTW];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RTW; ++r)
 #pragma unroll
-        for (int t = 0; t < VT; ++t)
+            for (int q = 0; q < 16; ++q) acc[r][q] = 0.f;
+        auto compute = [&](const uint4 *wb, const uint4 (&F)[G]) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[r][t][q] = 0.f;
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int r = 0; r < RTW; ++r) {
+                    const uint4 a = wb[((r0 + r) * G + g) * 64 + lane];
+                    Mma<T>::step(acc[r], a, F[g]);
+                }
+        };
 
-    auto compute = [&](const uint4 *wb, const uint4 (&F)[VT][G]) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                const uint4 a = wb[(r * G + g) * 64 + lane];
-#pragma unroll
-                for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], a, F[t][g]);
+        // the previous round's readers of sN and of the weight buffers are done
+        __syncthreads();
+        if constexpr (S::RESIDENT) {
+            for (int k = 0; k < 27; ++k) stage_w(k, sW0[k]);
+        } else {
+            stage_w(0, sW0[0]);
+        }
+        stage_nbr<S::VOX_PER_BLOCK>(nbr, n, col0 * 32, (char *)sN, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        uint4 F0[G], F1[G];
+        bool any0 = fetch(lookup(0), F0), any1 = false;
+        Look Ln = lookup(1);  // the next tap's rows
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        // one tap: prefetch tap k+1 (weights into LDS, features into the other
+        // register set) and look up tap k+2, run tap k's MFMAs, then wait and (when
+        // the weights rotate through two buffers) meet at a barrier.  ODD (the loop is
+        // unrolled by two) picks the weight buffers at compile time.
+        auto tap = [&](auto odd, int k, uint4 (&Fc)[G], bool anyc, uint4 (&Fn)[G]) -> bool {
+            constexpr bool O = decltype(odd)::value;
+            bool anyn = false;
+            if (k + 1 < 27) {
+                if constexpr (!S::RESIDENT) stage_w(k + 1, O ? sW0[0] : sW1[0]);
+                anyn = fetch(Ln, Fn);
             }
-    };
-
-    uint4 F0[VT][G], F1[VT][G];
-    if constexpr (S::RESIDENT) {
-        for (int k = 0; k < 27; ++k) stage_w(k, sW0[k]);
-    } else {
-        stage_w(0, sW0[0]);
-    }
-    stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK, (char *)sN, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    bool any0 = fetch(lookup(0), F0), any1 = false;
-    Look Ln = lookup(1);                 // the next tap's rows
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // one tap: prefetch tap k+1 (weights into LDS, features into the other
-    // register set) and look up tap k+2, run tap k's MFMAs, then wait and (when
-    // the weights rotate through two buffers) meet at a barrier.  ODD (the loop is
-    // unrolled by two) picks the weight buffers at compile time.
-    auto tap = [&](auto odd, int k, uint4 (&Fc)[VT][G], bool anyc, uint4 (&Fn)[VT][G]) -> bool {
-        constexpr bool O = decltype(odd)::value;
-        bool anyn = false;
-        if (k + 1 < 27) {
-            if constexpr (!S::RESIDENT) stage_w(k + 1, O ? sW0[0] : sW1[0]);
-            anyn = fetch(Ln, Fn);
+            if (k + 2 < 27) Ln = lookup(k + 2);
+            if (__any(anyc)) compute(S::RESIDENT ? sW0[k] : (O ? sW1[0] : sW0[0]), Fc);
+            if constexpr (!S::RESIDENT) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+            return anyn;
+        };
+        for (int k = 0; k < 27; k += 2) {
+            any1 = tap(std::false_type{}, k, F0, any0, F1);
+            if (k + 1 < 27) any0 = tap(std::true_type{}, k + 1, F1, any1, F0);
         }
-        if (k + 2 < 27) Ln = lookup(k + 2);
-        if (__any(anyc)) compute(S::RESIDENT ? sW0[k] : (O ? sW1[0] : sW0[0]), Fc);
-        if constexpr (!S::RESIDENT) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-        return anyn;
-    };
-    for (int k = 0; k < 27; k += 2) {
-        any1 = tap(std::false_type{}, k, F0, any0, F1);
-        if (k + 1 < 27) any0 = tap(std::true_type{}, k + 1, F1, any1, F0);
-    }
 
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-        const int64_t v = vbase + 32 * t + l32;
-        if (v >= n) continue;
+        const int64_t v = vbase + l32;
+        if (!active || v >= n) return;
         const int64_t orow = perm[v];
-        if ((uint64_t)orow >= (uint64_t)n) continue;
+        if ((uint64_t)orow >= (uint64_t)n) return;
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RTW; ++r)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int o = 32 * r + 8 * q + 4 * half;
-                float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (bias) b = *(const float4 *)(bias + o);
-                Store4<T>::put(out + orow * COUT + o, acc[r][t][4 * q] + b.x, acc[r][t][4 * q + 1] + b.y,
-                               acc[r][t][4 * q + 2] + b.z, acc[r][t][4 * q + 3] + b.w);
+                const int o = 32 * (r0 + r) + 8 * q + 4 * half;
+                float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (bias) bv = *(const float4 *)(bias + o);
+                Store4<T>::put(out + orow * COUT + o, acc[r][4 * q] + bv.x, acc[r][4 * q + 1] + bv.y,
+                               acc[r][4 * q + 2] + bv.z, acc[r][4 * q + 3] + bv.w);
             }
-    }
+    };
+
+    const int full = m / 4, rem = m % 4;
+    for (int rd = 0; rd < full; ++rd)
+        round(std::integral_constant<int, RT>{}, c0 + 4 * rd, c0 + 4 * rd + wave, 0, true);
+    const int64_t ct = c0 + 4 * full;
+    if (rem == 1)
+        round(std::integral_constant<int, RT / 4>{}, ct, ct, wave * (RT / 4), true);
+    else if (rem == 2)
+        round(std::integral_constant<int, RT / 2>{}, ct, ct + (wave >> 1), (wave & 1) * (RT / 2), true);
+    else if (rem == 3)
+        round(std::integral_constant<int, RT>{}, ct, ct + (wave < 3 ? wave : 2), 0, wave < 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -647,6 +661,19 @@ static int launch_lowc(const void *f, const void *w, const float *b, const int32
     return fail(SUBMCONV_E_UNSUPPORTED, "lowc kernel: Cin must be a power of two <= 32");
 }
 
+// compute units of the current device (cached per device)
+static int current_device_cus()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev >= 0 && dev < 64) cached[dev] = cus;
+    return cus;
+}
+
 template <typename T, int CIN, int COUT, int VT>
 static void launch_mfma_vt(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm,
                            void *o, int64_t n, int flip, hipStream_t s)
@@ -670,8 +697,10 @@ static void launch_mfma_vt(const void *f, const void *w, const float *b, const i
         hipLaunchKernelGGL((k_conv_mfma_rows<T, CIN, COUT, VT, 1>), dim3(grid), dim3(256), 0, s,
                            (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     } else {
-        constexpr int per_block = MfmaShape<T, CIN, COUT, VT>::VOX_PER_BLOCK;
-        const unsigned grid = (unsigned)((n + per_block - 1) / per_block);
+        // persistent: one block per CU (fewer when there are fewer 32-voxel columns)
+        const int64_t ncols = (n + 31) / 32;
+        const int64_t cus = current_device_cus();
+        const unsigned grid = (unsigned)(ncols < cus ? ncols : cus);
         hipLaunchKernelGGL((k_conv_mfma<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
                            (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     }

@@ -354,6 +354,27 @@ def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
     assert_close(got, expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
 
 
+# The persistent fp32 128 -> 128 kernel: each block (one per CU) walks a balanced run of
+# 32-voxel columns in rounds, and its last round splits Cout among the waves when 1, 2
+# or 3 columns remain.  With 256 blocks, 24576 voxels leave 3 columns per block (one
+# wave idles) and 52000 leave 6 or 7 (a full round, then 2 or 3); the set of 3001 in
+# the random-set tests leaves 1.  Sampled rows against the oracle.
+@pytest.mark.parametrize("n", [24576, 52000, 146279])
+def test_forward_mfma_persistent_rounds(n):
+    c = synth.random_coords(n, 64, 1, 23)
+    feats, weight, b = synth.make_values(len(c), 128, 128, 7)
+    tf, tw, tb, f64, w64 = device_values(feats, weight, b, "f32")
+    rb = build(c, 64, 1)
+    note("mfma persistent rounds n=%d" % n)
+    out = sc.submconv_forward(tf, tw, tb, rb, variant=sc.KERNEL_MFMA)
+    table = dense.neighbor_table(c, 64, 1)
+    pick = np.sort(np.random.default_rng(n + 1).choice(len(c), size=3000, replace=False))
+    pick = np.unique(np.concatenate([pick, [0, len(c) - 1]]))
+    expect = ref.forward(f64, w64, b, table[pick])
+    got = to_f64(out[torch.from_numpy(pick).to(DEV)])
+    assert_close(got, expect, "f32", "mfma persistent n=%d" % n)
+
+
 # Kernels that address bf16 feature rows by 32-bit byte offsets take N * Cin * 2 <=
 # 2^31 - 1 (windowed: 32 channels; persistent: 64 and 128).  Just past the cap,
 # forcing the kernel is refused and the automatic choice runs another one.  A dense
