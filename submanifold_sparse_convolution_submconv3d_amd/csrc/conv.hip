@@ -156,14 +156,14 @@ __device__ uint4 g_zero_row[64] = {};  // 1 KB of zeros: the row of a missing ne
 // 1 KB per wave instruction).  The table allocation is padded, so a 16-byte chunk
 // that straddles its end stays inside it; chunks wholly past the end read zeros
 // (those voxels do not exist and their entries are never used).
-template <int NVOX>
+template <int NVOX, int NWAVES = 4>
 __device__ __forceinline__ void stage_nbr(const int32_t *nbr, int64_t n, int64_t v0, char *dst,
                                           int wave, int lane)
 {
     constexpr int NI = (NVOX * NBR_INTS * 4 + 1023) / 1024;
     const char *base = (const char *)(nbr + v0 * NBR_INTS);
     const int64_t left = (n - v0) * NBR_INTS * 4;  // valid bytes from base
-    for (int i = wave; i < NI; i += 4) {
+    for (int i = wave; i < NI; i += NWAVES) {
         const int64_t off = (int64_t)i * 1024 + lane * 16;
         const void *src = off < left ? (const void *)(base + off) : (const void *)g_zero_row;
         __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
@@ -227,29 +227,36 @@ struct MfmaShape {
     static_assert(G >= 1 && RT >= 1, "channel counts too small for the matrix-core path");
 };
 
-// Persistent: one block per CU takes a balanced contiguous run of 32-voxel columns
-// and walks it in rounds.  In a full round each of the 4 waves owns one column and
-// all Cout; in the last, partial round the waves share the remaining columns and
-// split Cout (1 column: a quarter each, 2 columns: a half each, 3 columns: one wave
-// idles).  With one block per CU, a grid of 128-voxel blocks ran whole extra rounds
-// on some CUs while the rest idled (10-14% at 146k voxels).
+// Persistent: one block of 8 waves per CU (two per SIMD, so that one wave's
+// copy-issue and LDS stalls hide behind the other's MFMAs) takes a balanced
+// contiguous run of 32-voxel columns and walks it in rounds.  In a full round each
+// wave owns one column and all Cout; in the last, partial round the waves share the
+// remaining columns and split Cout so that no SIMD carries more than it must.  With
+// one block per CU, a grid of fixed-size blocks ran whole extra rounds on some CUs
+// while the rest idled.
+constexpr int MFMA_P_WAVES = 8;
+
 template <typename T, int CIN, int COUT, int VT>
-__global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
-                                                   const T *__restrict__ w,
-                                                   const float *__restrict__ bias,
-                                                   const int32_t *__restrict__ nbr,
-                                                   const int32_t *__restrict__ perm,
-                                                   T *__restrict__ out, int64_t n, int flip)
+__global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__restrict__ feats,
+                                                                  const T *__restrict__ w,
+                                                                  const float *__restrict__ bias,
+                                                                  const int32_t *__restrict__ nbr,
+                                                                  const int32_t *__restrict__ perm,
+                                                                  T *__restrict__ out, int64_t n, int flip)
 {
     using S = MfmaShape<T, CIN, COUT, VT>;
+    constexpr int WV = MFMA_P_WAVES, VPB = 32 * WV;
     constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
-    static_assert(VT == 1 && RT % 4 == 0, "one column per wave, Cout split four ways in a partial round");
-    // two weight objects when taps rotate through two buffers: the compiler tracks
-    // direct global-to-LDS copies per object, so reading tap k's buffer does not wait
-    // for the copy of tap k+1 into the other (and, through it, for every load in flight)
-    __shared__ uint4 sW0[S::RESIDENT ? 27 : 1][NFRAG * 64];
-    __shared__ uint4 sW1[S::RESIDENT ? 1 : 1][S::RESIDENT ? 4 : NFRAG * 64];
-    __shared__ __attribute__((aligned(16))) int32_t sN[S::VOX_PER_BLOCK * NBR_INTS + 256];
+    constexpr int NW = NFRAG / WV;  // weight fragments each wave copies per tap
+    static_assert(VT == 1 && RT % 4 == 0, "one column per wave, Cout split in quarters in a partial round");
+    static_assert(!S::RESIDENT && CIN * (int)sizeof(T) <= 1024, "weights rotate through two tap buffers; a row fits the zero row");
+    static_assert(NFRAG % WV == 0 && NW <= G / 2 && G % 2 == 0, "the next tap's copies fit the first half of the MFMA groups");
+    // two weight objects: the compiler tracks direct global-to-LDS copies per object,
+    // so reading tap k's buffer does not wait for the copy of tap k+1 into the other
+    // (and, through it, for every load in flight)
+    __shared__ uint4 sW0[1][NFRAG * 64];
+    __shared__ uint4 sW1[1][NFRAG * 64];
+    __shared__ __attribute__((aligned(16))) int32_t sN[VPB * NBR_INTS + 256];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
@@ -259,23 +266,44 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
     const int m = (int)(c1 - c0);
     if (m <= 0) return;
 
-    // copy weight tap k (kernel tap k' = flip ? 26-k : k) into the LDS buffer `dst`
-    auto stage_w = [&](int k, uint4 *dst) {
+    // copy weight fragment f of tap k (kernel tap k' = flip ? 26-k : k) into `dst`
+    auto copy_w = [&](int k, uint4 *dst, int f) {
         const int kw = flip ? 26 - k : k;
-        for (int f = wave; f < NFRAG; f += 4) {
-            const int r = f / G, g = f - r * G;
-            const T *src = w + ((int64_t)(32 * r + l32) * 27 + kw) * CIN + (2 * g + half) * EPC;
-            __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)&dst[f * 64], 16, 0, 0);
-        }
+        const int r = f / G, g = f - r * G;
+        const T *src = w + ((int64_t)(32 * r + l32) * 27 + kw) * CIN + (2 * g + half) * EPC;
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)&dst[f * 64], 16, 0, 0);
+    };
+    auto stage_w = [&](int k, uint4 *dst) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) copy_w(k, dst, wave + WV * i);
     };
 
-    // One round: tap loop of this wave's column `col` (its voxels at sN rows
-    // (col - col0) * 32 ..) for output tiles r0 .. r0 + RTW - 1; inactive waves take
-    // part in the copies and barriers only.
+    // One round over the columns col0 .. (up to 8): this wave's column `col` (its
+    // voxels at sN rows (col - col0) * 32 ..), output tiles r0 .. r0 + RTW - 1.  An
+    // inactive wave only copies its share of the weights and meets the barriers.
     auto round = [&](auto rtw, int64_t col0, int64_t col, int r0, bool active) {
         constexpr int RTW = decltype(rtw)::value;
         const int64_t vbase = col * 32;
         const int srow = (int)(col - col0) * 32;
+
+        // the previous round's readers of sN and of the weight buffers are done
+        __syncthreads();
+        stage_w(0, sW0[0]);
+        stage_nbr<VPB, WV>(nbr, n, col0 * 32, (char *)sN, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        if (!active) {
+            for (int k = 0; k < 26; k += 2) {
+                stage_w(k + 1, sW1[0]);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                stage_w(k + 2, sW0[0]);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+            return;
+        }
 
         // input rows of this wave's voxels' tap-k neighbours, looked up a tap before
         // their fragments are fetched: the perm loads are unconditional and not
@@ -286,19 +314,18 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
         };
         auto lookup = [&](int k) -> Look {
             const int64_t v = vbase + l32;
-            const int32_t e = active && v < n ? nbr_at(sN + (srow + l32) * NBR_INTS, k) : -1;
+            const int32_t e = v < n ? nbr_at(sN + (srow + l32) * NBR_INTS, k) : -1;
             Look L;
             L.ok = (uint32_t)e < (uint64_t)n;
             L.r = perm[L.ok ? e : 0];
             return L;
         };
-        // feature fragments of the looked-up rows (zeros for missing neighbours)
-        auto fetch = [&](const Look &L, uint4 (&F)[G]) -> bool {
-            const int32_t j = L.ok && (uint32_t)L.r < (uint64_t)n ? L.r : -1;
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                F[g] = j >= 0 ? *(const uint4 *)(feats + (int64_t)j * CIN + (2 * g + half) * EPC) : make_uint4(0, 0, 0, 0);
-            return j >= 0;
+        // first chunk of this lane's feature fragments for a looked-up row: the row
+        // itself, or the zero row for a missing neighbour (an address choice, so every
+        // fragment is one unconditional load)
+        auto frag_src = [&](const Look &L) -> const T * {
+            const bool real = L.ok && (uint32_t)L.r < (uint64_t)n;
+            return (real ? feats + (int64_t)L.r * CIN : (const T *)g_zero_row) + half * EPC;
         };
 
         floatx16 acc[RTW];
@@ -306,58 +333,69 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
         for (int r = 0; r < RTW; ++r)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[r][q] = 0.f;
-        auto compute = [&](const uint4 *wb, const uint4 (&F)[G]) {
+
+        // tap k's MFMAs (weights in LDS buffer wb, features in F).  With PF the next
+        // tap's copies go out piece by piece between the MFMA groups of the first half
+        // of the tap: group g < G/2 brings feature fragments 2g, 2g+1 into Fn and
+        // weight fragment g of this wave's share into wn (issued all at once, a wave's
+        // copies stalled its issue for about a third of a tap; issued through the whole
+        // tap, the last gathers were still in flight at its end).  The groups are kept
+        // apart so that the copies stay spread and the registers of only one group's
+        // LDS reads are live.
+        auto compute = [&](auto pf, const uint4 *wb, const uint4 (&F)[G], int kn, uint4 *wn,
+                           const T *fsrc, uint4 (&Fn)[G]) {
+            constexpr bool PF = decltype(pf)::value;
 #pragma unroll
-            for (int g = 0; g < G; ++g)
+            for (int g = 0; g < G; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (PF) {
+                    if (g < G / 2) {
+                        Fn[2 * g] = *(const uint4 *)(fsrc + 4 * g * EPC);
+                        Fn[2 * g + 1] = *(const uint4 *)(fsrc + (4 * g + 2) * EPC);
+                    }
+                    if (g < NW) copy_w(kn, wn, wave + WV * g);
+                }
 #pragma unroll
                 for (int r = 0; r < RTW; ++r) {
                     const uint4 a = wb[((r0 + r) * G + g) * 64 + lane];
                     Mma<T>::step(acc[r], a, F[g]);
                 }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         };
 
-        // the previous round's readers of sN and of the weight buffers are done
-        __syncthreads();
-        if constexpr (S::RESIDENT) {
-            for (int k = 0; k < 27; ++k) stage_w(k, sW0[k]);
-        } else {
-            stage_w(0, sW0[0]);
-        }
-        stage_nbr<S::VOX_PER_BLOCK>(nbr, n, col0 * 32, (char *)sN, wave, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
         uint4 F0[G], F1[G];
-        bool any0 = fetch(lookup(0), F0), any1 = false;
+        {
+            const T *src = frag_src(lookup(0));
+#pragma unroll
+            for (int g = 0; g < G; ++g) F0[g] = *(const uint4 *)(src + 2 * g * EPC);
+        }
         Look Ln = lookup(1);  // the next tap's rows
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
 
-        // one tap: prefetch tap k+1 (weights into LDS, features into the other
-        // register set) and look up tap k+2, run tap k's MFMAs, then wait and (when
-        // the weights rotate through two buffers) meet at a barrier.  ODD (the loop is
-        // unrolled by two) picks the weight buffers at compile time.
-        auto tap = [&](auto odd, int k, uint4 (&Fc)[G], bool anyc, uint4 (&Fn)[G]) -> bool {
+        // taps 0..25: copy tap k+1 (weights into the other LDS buffer, features into
+        // the other register set) during tap k's MFMAs, look up tap k+2, then wait and
+        // meet at a barrier.  ODD (the loop is unrolled by two) picks the weight
+        // buffers at compile time.  Taps run even where no voxel of the column has the
+        // neighbour (well under 1% of column-taps on surface-like sets): a branch
+        // around the MFMAs made the compiler copy the accumulators on every tap.
+        auto tap = [&](auto odd, int k, uint4 (&Fc)[G], uint4 (&Fn)[G]) {
             constexpr bool O = decltype(odd)::value;
-            bool anyn = false;
-            if (k + 1 < 27) {
-                if constexpr (!S::RESIDENT) stage_w(k + 1, O ? sW0[0] : sW1[0]);
-                anyn = fetch(Ln, Fn);
-            }
+            const T *fsrc = frag_src(Ln);
             if (k + 2 < 27) Ln = lookup(k + 2);
-            if (__any(anyc)) compute(S::RESIDENT ? sW0[k] : (O ? sW1[0] : sW0[0]), Fc);
-            if constexpr (!S::RESIDENT) {
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-            }
-            return anyn;
+            compute(std::true_type{}, O ? sW1[0] : sW0[0], Fc, k + 1, O ? sW0[0] : sW1[0], fsrc, Fn);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         };
-        for (int k = 0; k < 27; k += 2) {
-            any1 = tap(std::false_type{}, k, F0, any0, F1);
-            if (k + 1 < 27) any0 = tap(std::true_type{}, k + 1, F1, any1, F0);
+        for (int k = 0; k < 26; k += 2) {
+            tap(std::false_type{}, k, F0, F1);
+            tap(std::true_type{}, k + 1, F1, F0);
         }
+        // tap 26 (even: buffer 0, register set 0), nothing left to copy
+        compute(std::false_type{}, sW0[0], F0, 26, sW1[0], (const T *)g_zero_row, F1);
 
         const int64_t v = vbase + l32;
-        if (!active || v >= n) return;
+        if (v >= n) return;
         const int64_t orow = perm[v];
         if ((uint64_t)orow >= (uint64_t)n) return;
 #pragma unroll
@@ -372,16 +410,25 @@ __global__ __launch_bounds__(256) void k_conv_mfma(const T *__restrict__ feats,
             }
     };
 
-    const int full = m / 4, rem = m % 4;
+    // waves w and w + 4 share a SIMD; each partial-round split below gives every SIMD
+    // at most the quarter-tile work the columns need (rem 5..7 cost a full round)
+    using Q = std::integral_constant<int, RT / 4>;
+    using H = std::integral_constant<int, RT / 2>;
+    using A = std::integral_constant<int, RT>;
+    const int full = m / WV, rem = m % WV;
     for (int rd = 0; rd < full; ++rd)
-        round(std::integral_constant<int, RT>{}, c0 + 4 * rd, c0 + 4 * rd + wave, 0, true);
-    const int64_t ct = c0 + 4 * full;
-    if (rem == 1)
-        round(std::integral_constant<int, RT / 4>{}, ct, ct, wave * (RT / 4), true);
-    else if (rem == 2)
-        round(std::integral_constant<int, RT / 2>{}, ct, ct + (wave >> 1), (wave & 1) * (RT / 2), true);
-    else if (rem == 3)
-        round(std::integral_constant<int, RT>{}, ct, ct + (wave < 3 ? wave : 2), 0, wave < 3);
+        round(A{}, c0 + WV * rd, c0 + WV * rd + wave, 0, true);
+    const int64_t ct = c0 + WV * full;
+    if (rem == 1)  // waves 0..3 (one per SIMD): a quarter of Cout each
+        round(Q{}, ct, ct, (wave & 3) * (RT / 4), wave < 4);
+    else if (rem == 2)  // 4 waves per column, a quarter each
+        round(Q{}, ct, ct + (wave >> 2), (wave & 3) * (RT / 4), true);
+    else if (rem == 3)  // 2 waves per column, a half each (waves 6, 7 idle)
+        round(H{}, ct, ct + (wave < 6 ? wave >> 1 : 0), (wave & 1) * (RT / 2), wave < 6);
+    else if (rem == 4)
+        round(H{}, ct, ct + (wave >> 1), (wave & 1) * (RT / 2), true);
+    else if (rem > 4)
+        round(A{}, ct, ct + (wave < rem ? wave : 0), 0, wave < rem);
 }
 
 // ---------------------------------------------------------------------------
@@ -701,7 +748,7 @@ static void launch_mfma_vt(const void *f, const void *w, const float *b, const i
         const int64_t ncols = (n + 31) / 32;
         const int64_t cus = current_device_cus();
         const unsigned grid = (unsigned)(ncols < cus ? ncols : cus);
-        hipLaunchKernelGGL((k_conv_mfma<T, CIN, COUT, VT>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_conv_mfma<T, CIN, COUT, VT>), dim3(grid), dim3(64 * MFMA_P_WAVES), 0, s,
                            (const T *)f, (const T *)w, b, nbr, perm, (T *)o, n, flip);
     }
 }

@@ -354,12 +354,13 @@ def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
     assert_close(got, expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
 
 
-# The persistent fp32 128 -> 128 kernel: each block (one per CU) walks a balanced run of
-# 32-voxel columns in rounds, and its last round splits Cout among the waves when 1, 2
-# or 3 columns remain.  With 256 blocks, 24576 voxels leave 3 columns per block (one
-# wave idles) and 52000 leave 6 or 7 (a full round, then 2 or 3); the set of 3001 in
-# the random-set tests leaves 1.  Sampled rows against the oracle.
-@pytest.mark.parametrize("n", [24576, 52000, 146279])
+# The persistent fp32 128 -> 128 kernel: each block of 8 waves (one per CU) walks a
+# balanced run of 32-voxel columns in rounds of 8, and its last round splits Cout among
+# the waves when 1 to 4 columns remain (5 to 7: idle waves).  With 256 blocks the
+# columns per block are: 24576 voxels 3; 40000 voxels 4 or 5; 52000 voxels 6 or 7;
+# 65536 voxels 8 (one full round, no partial one); 146279 voxels 17 or 18 (two full
+# rounds, then 1 or 2).  Sampled rows against the oracle.
+@pytest.mark.parametrize("n", [24576, 40000, 52000, 65536, 146279])
 def test_forward_mfma_persistent_rounds(n):
     c = synth.random_coords(n, 64, 1, 23)
     feats, weight, b = synth.make_values(len(c), 128, 128, 7)
