@@ -135,13 +135,14 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
 // (The contraction order may be permuted freely as long as A and B agree.)
 // D (32 x 32): lane l holds column l % 32, rows 8 (q/4) + 4 (l/32) + q % 4.
 //
-// Data movement per block (4 waves, each 32*VT voxels x all Cout):
+// Data movement of the persistent fp32 128 -> 128 kernel below (8 waves per
+// block, each a 32-voxel column x all Cout in a full round):
 //   * weight tap k' is copied once per block into LDS in fragment order by
 //     direct global->LDS loads (no register staging), double-buffered so the
-//     copy of the next tap overlaps this tap's MFMAs; when all 27 taps fit in
-//     64 KB they are copied once and stay resident (no per-tap barrier);
+//     copy of the next tap overlaps this tap's MFMAs;
 //   * the B operand (gathered feature rows) is loaded straight into registers,
-//     one tap ahead of the MFMAs that use it; a missing neighbour gives zeros.
+//     one tap ahead of the MFMAs that use it; a missing neighbour reads the
+//     zero row.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -221,9 +222,6 @@ struct MfmaShape {
     static constexpr int G = CIN * ES / 32;            // fragment groups along Cin
     static constexpr int RT = COUT / 32;               // row tiles (output channels)
     static constexpr int NFRAG = RT * G;               // weight fragments per tap (1 KB each)
-    static constexpr bool RESIDENT = 27 * NFRAG * 1024 <= 65536;
-    static constexpr int WBUF = RESIDENT ? 27 : 2;     // tap buffers in LDS
-    static constexpr int VOX_PER_BLOCK = 4 * 32 * VT;
     static_assert(G >= 1 && RT >= 1, "channel counts too small for the matrix-core path");
 };
 
@@ -249,7 +247,7 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
     constexpr int G = S::G, RT = S::RT, NFRAG = S::NFRAG, EPC = S::EPC;
     constexpr int NW = NFRAG / WV;  // weight fragments each wave copies per tap
     static_assert(VT == 1 && RT % 4 == 0, "one column per wave, Cout split in quarters in a partial round");
-    static_assert(!S::RESIDENT && CIN * (int)sizeof(T) <= 1024, "weights rotate through two tap buffers; a row fits the zero row");
+    static_assert(CIN * (int)sizeof(T) <= 1024, "a feature row fits the zero row");
     static_assert(NFRAG % WV == 0 && NW <= G / 2 && G % 2 == 0, "the next tap's copies fit the first half of the MFMA groups");
     // two weight objects: the compiler tracks direct global-to-LDS copies per object,
     // so reading tap k's buffer does not wait for the copy of tap k+1 into the other
