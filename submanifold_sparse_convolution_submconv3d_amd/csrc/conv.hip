@@ -537,24 +537,36 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
         const bool ok = (uint32_t)e < (uint64_t)n;
         return Look{perm[ok ? e : 0], ok};
     };
-    // the column's neighbour rows for tap k -> its region of `fbuf` (the OS waves of
-    // the column each issue every OS-th copy); returns whether any row exists
-    auto gather = [&](const Look &L, char *fbuf) -> bool {
-        const int32_t j = L.ok && (uint32_t)L.r < (uint64_t)n ? L.r : -1;
-        const bool any = __any(j >= 0);
-        if (any) {
-            char *dst = fbuf + colw * ROWS * RB;
+    // row to gather for a looked-up entry, or -1 (the zero row)
+    auto row_of = [&](const Look &L) -> int32_t { return L.ok && (uint32_t)L.r < (uint64_t)n ? L.r : -1; };
+    // copy q of the column's neighbour rows into its region of `fbuf`: the OS waves of
+    // the column each issue every OS-th 1 KB copy; a missing neighbour copies the zero
+    // row (an address choice, so the copy is unconditional)
+    constexpr int NGP = (ROWS / RPI) / OS;  // row copies per wave and tap
+    auto spread_rows = [&](int32_t j, int32_t (&jr)[NGP]) {  // row of each copy's lane
 #pragma unroll
-            for (int i = og; i < ROWS / RPI; i += OS) {
-                const int row = i * RPI + lane / CH;
-                const int jr = __shfl(j, row, 64);
-                const int c = (lane % CH) ^ swz<RB>(row);
-                const void *src = jr >= 0 ? (const void *)(feats + (int64_t)jr * CIN + c * EPC)
-                                          : (const void *)((const char *)g_zero_row + c * 16);
-                __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
-            }
-        }
-        return any;
+        for (int q = 0; q < NGP; ++q) jr[q] = __shfl(j, (og + OS * q) * RPI + lane / CH, 64);
+    };
+    auto gather_piece = [&](const int32_t (&jrs)[NGP], char *fbuf, int q) {
+        const int i = og + OS * q;
+        const int row = i * RPI + lane / CH;
+        const int jr = jrs[q];
+        const int c = (lane % CH) ^ swz<RB>(row);
+        const void *src = jr >= 0 ? (const void *)(feats + (int64_t)jr * CIN + c * EPC)
+                                  : (const void *)((const char *)g_zero_row + c * 16);
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(fbuf + colw * ROWS * RB + i * 1024), 16, 0, 0);
+    };
+    // weight copy p of this wave for tap k (instruction wave + 4p of the tap; a wave
+    // with fewer repeats its last one, which writes the same bytes again)
+    constexpr int NI_W = COUT / RPI;
+    constexpr int NWP = S::RESIDENT ? 0 : (NI_W + 3) / 4;
+    auto copy_w_piece = [&](int k, char *dst, int p) {
+        const int kw = flip ? 26 - k : k;
+        const int i = wave + 4 * p < NI_W ? wave + 4 * p : NI_W - 1;
+        const int o = i * RPI + lane / CH;
+        const int c = (lane % CH) ^ swz<RB>(o);
+        const T *src = w + ((int64_t)o * 27 + kw) * CIN + c * EPC;
+        __builtin_amdgcn_global_load_lds((gbl_void *)src, (lds_void *)(dst + i * 1024), 16, 0, 0);
     };
 
     floatx16 acc[RT][VT];
@@ -573,24 +585,30 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     stage_nbr<S::VOX_PER_BLOCK>(nbr, n, blk * S::VOX_PER_BLOCK, sNb, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bool any = gather(lookup(0), sF0);
-    Look jn = lookup(1);                 // the next tap's rows
+    {
+        int32_t jr0[NGP];
+        spread_rows(row_of(lookup(0)), jr0);
+#pragma unroll
+        for (int q = 0; q < NGP; ++q) gather_piece(jr0, sF0, q);
+    }
+    Look jn = lookup(1);  // the next tap's rows
 
-    // tap k; ODD picks the buffers at compile time (the tap loop is unrolled by two):
-    // weights and rows of tap k are read from one buffer while tap k+1 fills the other
-    auto step = [&](auto odd, int k) {
-        constexpr bool O = decltype(odd)::value;
+    // Tap k; ODD picks the buffers at compile time (the tap loop is unrolled by two):
+    // weights and rows of tap k are read from one buffer while tap k+1 fills the
+    // other.  With PF (taps 0..25) the next tap's copies are issued a few at a time
+    // between the MFMA groups of the first half of the tap: issued together at its
+    // start they held the wave's issue for a large part of it.  Every tap runs its MFMAs (a branch around
+    // them made the compiler copy the accumulators each tap).
+    auto step = [&](auto odd, auto pf, int k) {
+        constexpr bool O = decltype(odd)::value, PF = decltype(pf)::value;
         char *wnxt = O ? sW0 : sW1;
         char *fcur = (FB == 2 && O) ? sF1 : sF0;
         char *fnxt = (FB == 2 && !O) ? sF1 : sF0;
         const char *wb = S::RESIDENT ? sW0 + k * S::W_TAP : (O ? sW1 : sW0);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into LDS have landed
         __syncthreads();                 // ... and everyone's; the other buffers are free
-        if constexpr (!S::RESIDENT) {
-            if (k + 1 < 27) stage_w(k + 1, wnxt);
-        }
         uint4 F[VT][G];
-        if (any) {
+        {
             const char *src = fcur + colw * ROWS * RB;
 #pragma unroll
             for (int t = 0; t < VT; ++t)
@@ -604,25 +622,46 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
         // refills its region; with two, the next gather goes to the other buffer, which
         // every wave of the column finished reading before the barrier above.
         if constexpr (FB == 1) SC_WAIT_LGKM0();
-        const bool any_now = any;
-        any = (k + 1 < 27) ? gather(jn, fnxt) : false;
-        if (k + 2 < 27) jn = lookup(k + 2);
-        if (any_now) {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int r = 0; r < RT; ++r) {
-                    const int o = 32 * (og * RT + r) + l32;
-                    const uint4 a = *(const uint4 *)(wb + o * RB + (((2 * g + half) ^ swz<RB>(o)) << 4));
-#pragma unroll
-                    for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], a, F[t][g]);
-                }
+        int32_t jnext[NGP];
+        if constexpr (PF) {
+            spread_rows(row_of(jn), jnext);
+            jn = lookup(k + 2 < 27 ? k + 2 : 26);
         }
+        // the copies go out in the first half of the groups, so they have half a tap to
+        // land before the wait at its end
+        constexpr int P = PF ? NWP + NGP : 0, GP = G >= 2 ? G / 2 : 1;
+        // A fragments of group g are read during group g - 1 (the groups are kept
+        // apart, so nothing else would hide the LDS latency in front of the MFMAs)
+        auto read_a = [&](int g, uint4 (&a)[RT]) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int o = 32 * (og * RT + r) + l32;
+                a[r] = *(const uint4 *)(wb + o * RB + (((2 * g + half) ^ swz<RB>(o)) << 4));
+            }
+        };
+        uint4 A[2][RT];
+        read_a(0, A[0]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            __builtin_amdgcn_sched_barrier(0);  // keep each group's copies in place
+            if (g + 1 < G) read_a(g + 1, A[(g + 1) & 1]);
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], A[g & 1][r], F[t][g]);
+#pragma unroll
+            for (int p = g * P / GP; p < (g < GP ? (g + 1) * P / GP : 0); ++p) {
+                if (p < NWP) copy_w_piece(k + 1, wnxt, p);
+                else gather_piece(jnext, fnxt, p - NWP);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
-    for (int k = 0; k < 27; k += 2) {
-        step(std::false_type{}, k);
-        if (k + 1 < 27) step(std::true_type{}, k + 1);
+    for (int k = 0; k < 26; k += 2) {
+        step(std::false_type{}, std::true_type{}, k);
+        step(std::true_type{}, std::true_type{}, k + 1);
     }
+    step(std::false_type{}, std::false_type{}, 26);
 
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
