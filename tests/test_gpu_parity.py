@@ -376,6 +376,24 @@ def test_forward_mfma_persistent_rounds(n):
     assert_close(got, expect, "f32", "mfma persistent n=%d" % n)
 
 
+# Sets of 1 to 300 voxels through the automatic kernel choice: one voxel, one ragged
+# 32-voxel column, a column and one voxel, and a few columns (the persistent fp32
+# 128 -> 128 kernel then runs only its partial round, with idle waves; the rows
+# kernel has blocks past the last voxel).  Every row against the oracle.
+@pytest.mark.parametrize("n", [1, 31, 33, 300])
+@pytest.mark.parametrize("cin,cout,dtype", [(128, 128, "f32"), (64, 64, "f32"), (32, 64, "bf16"),
+                                            (64, 64, "bf16"), (128, 128, "bf16")])
+def test_forward_tiny_sets(n, cin, cout, dtype):
+    c = synth.random_coords(n, 8, 1, 40 + n)
+    feats, weight, b = synth.make_values(len(c), cin, cout, 11)
+    tf, tw, tb, f64, w64 = device_values(feats, weight, b, dtype)
+    rb = build(c, 8, 1)
+    note("tiny set n=%d %d->%d %s" % (n, cin, cout, dtype))
+    out = sc.submconv_forward(tf, tw, tb, rb)
+    expect = dense.forward(f64, w64, b, dense.neighbor_table(c, 8, 1), 0)
+    assert_close(to_f64(out), expect, dtype, "tiny n=%d %d->%d %s" % (n, cin, cout, dtype))
+
+
 # Kernels that address bf16 feature rows by 32-bit byte offsets take N * Cin * 2 <=
 # 2^31 - 1 (windowed: 32 channels; persistent: 64 and 128).  Just past the cap,
 # forcing the kernel is refused and the automatic choice runs another one.  A dense
