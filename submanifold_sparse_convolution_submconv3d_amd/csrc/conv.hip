@@ -532,8 +532,10 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
         bool ok;
     };
     auto lookup = [&](int k) -> Look {
-        int32_t e = -1;
-        if (lane < ROWS && vbase + lane < n) e = nbr_at(sN + (colw * ROWS + lane) * NBR_INTS, k);
+        // branch-free (lanes past the column read its last row and are dropped), so that
+        // it can sit between MFMA groups without splitting them
+        const int32_t ev = nbr_at(sN + (colw * ROWS + (lane < ROWS ? lane : ROWS - 1)) * NBR_INTS, k);
+        const int32_t e = lane < ROWS && vbase + lane < n ? ev : -1;
         const bool ok = (uint32_t)e < (uint64_t)n;
         return Look{perm[ok ? e : 0], ok};
     };
@@ -622,11 +624,9 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
         // refills its region; with two, the next gather goes to the other buffer, which
         // every wave of the column finished reading before the barrier above.
         if constexpr (FB == 1) SC_WAIT_LGKM0();
+        // the next tap's row numbers are spread and tap k+2 looked up after the first
+        // group's MFMAs: ahead of them, their LDS round trips held the start of every tap
         int32_t jnext[NGP];
-        if constexpr (PF) {
-            spread_rows(row_of(jn), jnext);
-            jn = lookup(k + 2 < 27 ? k + 2 : 26);
-        }
         // the copies go out in the first half of the groups, so they have half a tap to
         // land before the wait at its end
         constexpr int P = PF ? NWP + NGP : 0, GP = G >= 2 ? G / 2 : 1;
@@ -649,6 +649,12 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
             for (int r = 0; r < RT; ++r)
 #pragma unroll
                 for (int t = 0; t < VT; ++t) Mma<T>::step(acc[r][t], A[g & 1][r], F[t][g]);
+            if constexpr (PF) {
+                if (g == 0) {
+                    spread_rows(row_of(jn), jnext);
+                    jn = lookup(k + 2 < 27 ? k + 2 : 26);
+                }
+            }
 #pragma unroll
             for (int p = g * P / GP; p < (g < GP ? (g + 1) * P / GP : 0); ++p) {
                 if (p < NWP) copy_w_piece(k + 1, wnxt, p);
