@@ -150,6 +150,19 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 
 __device__ uint4 g_zero_row[64] = {};  // 1 KB of zeros: the row of a missing neighbour
 
+// nbr_at with both table words read unconditionally: no branch, so a lookup can sit
+// between MFMA groups without splitting their scheduling region
+__device__ __forceinline__ int32_t nbr_at_flat(const int32_t *row, int k)
+{
+    const int d = k / 3, j = k - 3 * d;
+    const uint32_t m = ((uint32_t)row[9] >> (3 * d)) & 7u;
+    const int32_t first = row[d];
+    // (an OR with the absent mask, not a select: a value used under a condition lets the
+    // compiler move its load into a branch)
+    const int32_t absent = (int32_t)((m >> j) & 1u) - 1;  // 0 present, -1 absent
+    return (first + (int32_t)__popc(m & ((1u << j) - 1u))) | absent;
+}
+
 // s_waitcnt with only the LDS/scalar counter at zero (vector-memory loads may stay in flight)
 #define SC_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
         };
         auto lookup = [&](int k) -> Look {
             const int64_t v = vbase + l32;
-            const int32_t e = v < n ? nbr_at(sN + (srow + l32) * NBR_INTS, k) : -1;
+            const int32_t e = nbr_at_flat(sN + (srow + l32) * NBR_INTS, k) | -(int32_t)(v >= n);
             Look L;
             L.ok = (uint32_t)e < (uint64_t)n;
             L.r = perm[L.ok ? e : 0];
@@ -341,10 +354,11 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
         // apart so that the copies stay spread and the registers of only one group's
         // LDS reads are live.
         auto compute = [&](auto pf, const uint4 *wb, const uint4 (&F)[G], int kn, uint4 *wn,
-                           const T *fsrc, uint4 (&Fn)[G]) {
+                           const T *fsrc, uint4 (&Fn)[G], auto &&after_first) {
             constexpr bool PF = decltype(pf)::value;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
+                if (g == 1) after_first();
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (PF) {
                     if (g < G / 2) {
@@ -377,11 +391,13 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
         // buffers at compile time.  Taps run even where no voxel of the column has the
         // neighbour (well under 1% of column-taps on surface-like sets): a branch
         // around the MFMAs made the compiler copy the accumulators on every tap.
+        // (the lookup of tap k+2 follows the first MFMA group: ahead of it, its LDS and
+        // perm round trips held the start of every tap)
         auto tap = [&](auto odd, int k, uint4 (&Fc)[G], uint4 (&Fn)[G]) {
             constexpr bool O = decltype(odd)::value;
             const T *fsrc = frag_src(Ln);
-            if (k + 2 < 27) Ln = lookup(k + 2);
-            compute(std::true_type{}, O ? sW1[0] : sW0[0], Fc, k + 1, O ? sW0[0] : sW1[0], fsrc, Fn);
+            compute(std::true_type{}, O ? sW1[0] : sW0[0], Fc, k + 1, O ? sW0[0] : sW1[0], fsrc, Fn,
+                    [&] { Ln = lookup(k + 2 < 27 ? k + 2 : 26); });
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };
@@ -390,7 +406,7 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
             tap(std::true_type{}, k + 1, F1, F0);
         }
         // tap 26 (even: buffer 0, register set 0), nothing left to copy
-        compute(std::false_type{}, sW0[0], F0, 26, sW1[0], (const T *)g_zero_row, F1);
+        compute(std::false_type{}, sW0[0], F0, 26, sW1[0], (const T *)g_zero_row, F1, [] {});
 
         const int64_t v = vbase + l32;
         if (v >= n) return;
@@ -534,8 +550,8 @@ __global__ __launch_bounds__(256) void k_conv_mfma_rows(const T *__restrict__ fe
     auto lookup = [&](int k) -> Look {
         // branch-free (lanes past the column read its last row and are dropped), so that
         // it can sit between MFMA groups without splitting them
-        const int32_t ev = nbr_at(sN + (colw * ROWS + (lane < ROWS ? lane : ROWS - 1)) * NBR_INTS, k);
-        const int32_t e = lane < ROWS && vbase + lane < n ? ev : -1;
+        const int32_t e = nbr_at_flat(sN + (colw * ROWS + (lane < ROWS ? lane : ROWS - 1)) * NBR_INTS, k) |
+                          -(int32_t)(lane >= ROWS || vbase + lane >= n);
         const bool ok = (uint32_t)e < (uint64_t)n;
         return Look{perm[ok ? e : 0], ok};
     };
