@@ -293,6 +293,9 @@ struct BigCtx {
             big_lds_barrier();
         };
         big_unroll<0, 27>(tap);
+        // the next round's table block: every read of this one is done (barrier after tap
+        // 23), and the copy overlaps the stores below instead of the next prologue's wait
+        stage_t(col_next);
 
         // epilogue: lane holds output channels 16 (r0 + r) + 4 h .. +3 of its voxel in column c
 #pragma unroll
@@ -309,7 +312,6 @@ struct BigCtx {
                                __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
             }
         }
-        stage_t(col_next);  // every read of this round's table is done (barrier after tap 23)
     }
 };
 
