@@ -342,7 +342,7 @@ def main():
                     help="time the coordinate-set helpers on the 512^3 subdivided shell instead (own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         return 2
     if args.peaks:
