@@ -91,7 +91,12 @@ typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
  * coords[i] + offset(k), or -1.  It is exact (integer work).  Synchronises
  * `stream` once to read the validity status: E_COORD_RANGE if a coordinate is
  * out of range, E_DUPLICATE if two rows are equal (no rulebook is returned).
- * Device memory is taken from the device's stream-ordered pool.
+ * Device memory comes from the library's block cache (submconv_release_cache),
+ * else from the device's stream-ordered pool.
+ *
+ * `batch` is an argument the pages' interface does not have: it bounds the batch
+ * index so the key width is known on the host without reading the coordinates
+ * back (one synchronisation fewer).
  */
 int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t batch,
                        void *stream, submconv_rulebook **out_rb);
@@ -251,12 +256,20 @@ int submconv_weight_convert(const void *src, int32_t layout, int32_t cout, int32
 
 /*
  * The library keeps device blocks it has freed (rulebooks, scratch) for reuse on the
- * same device and stream, up to 16 GiB per device, so that repeated builds make no
- * driver allocation calls.  This returns the cached blocks of `device` (all devices
- * when device < 0) to the driver, stream-ordered on the streams they were freed on.
- * Blocks in use are not affected.
+ * same device, up to a limit per device (2 GiB unless set below), so that repeated
+ * builds make no driver allocation calls.  A block freed while work queued on its
+ * stream may still read it carries an event recorded at the free; the next user's
+ * stream waits for that event before the block is reused, on any stream.
+ *
+ * submconv_release_cache returns the cached blocks of `device` (all devices when
+ * device < 0) to the driver after their last use has finished.  Blocks in use are not
+ * affected.
  */
 int submconv_release_cache(int32_t device);
+
+/* Set the per-device limit of the block cache in bytes (0 disables caching); cached
+ * blocks beyond the new limit are released.  E_INVALID_ARG if bytes < 0. */
+int submconv_set_cache_limit(int64_t bytes);
 
 /* Name of a status code (static string). */
 const char *submconv_status_string(int status);

@@ -12,9 +12,16 @@ Two independent implementations of the same definition:
   loops, built with gcc by `build_oracle()` into `oracle/_lib/`.
 
 Parity status: every function is pinned by CPU tests against brute force,
-dense torch conv3d, closed forms and invariants (see tests/test_oracle_*.py);
-none is "parity unpinned" except the orientation convention relative to the
-upstream sparse library, which no available artefact can settle.
+dense torch conv3d, closed forms, invariants and hand-worked examples
+(tests/test_oracle_*.py, tests/golden/).  Three conventions are fixed here
+where the pages are silent and are "parity unpinned" against the upstream
+implementations, which no available artefact can settle:
+  - the kernel orientation (correlation by default, `flip` for the mirror);
+  - the channel layout inside a space-to-depth row (slot-major: slot s holds
+    channels [s C, (s+1) C));
+  - the order of the coarse rows of space-to-depth and downsample (ascending
+    (b, z, y, x)).
+Within each convention the functions are pinned as above.
 """
 from __future__ import annotations
 

@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 from typing import Optional
 
 import torch
@@ -37,7 +38,7 @@ __all__ = [
     "SubmconvError", "Rulebook", "RulebookCache", "lib_path", "load_library",
     "submconv_build_map", "submconv_forward", "submconv_subdivide",
     "submconv_space_to_depth", "submconv_depth_to_space", "submconv_upsample_masked", "submconv_downsample",
-    "POOL_MAX", "POOL_MEAN", "classify_5d", "weight_to_krsc", "flip_ab", "release_cache",
+    "POOL_MAX", "POOL_MEAN", "classify_5d", "weight_to_krsc", "flip_ab", "release_cache", "set_cache_limit",
     "KERNEL_AUTO", "KERNEL_GENERIC", "KERNEL_LOWC", "KERNEL_MFMA", "KERNEL_WINDOW", "KERNEL_PERSISTENT",
 ]
 
@@ -88,6 +89,7 @@ def load_library():
         "submconv_downsample": [vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64p, vp],
         "submconv_classify_5d": [i64p, i32, i32p],
         "submconv_release_cache": [i32],
+        "submconv_set_cache_limit": [i64],
         "submconv_weight_convert": [vp, i32, i32, i32, i32, i32, vp, vp],
     }
     for name, args in sig.items():
@@ -166,15 +168,22 @@ class Rulebook:
                    "submconv_rulebook_copy_neighbors")
         return out
 
-    def free(self):
+    def free(self, stream: Optional[torch.cuda.Stream] = None):
+        """Release the map, ordered on `stream` (default: the current stream of its
+        device).  Work on other streams that still reads it must be ordered before
+        that stream first, as for any stream-ordered free."""
         if self._h is not None and _lib is not None:
             with torch.cuda.device(self.device):
-                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(self._stream.cuda_stream))
+                s = stream if stream is not None else torch.cuda.current_stream(self.device)
+                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(s.cuda_stream))
         self._h = None
 
     def __del__(self):
         try:
-            self.free()
+            if self._h is not None and _lib is not None:
+                # garbage collection: the release is ordered on the stream the map was built on
+                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(self._stream.cuda_stream))
+                self._h = None
         except Exception:
             pass
 
@@ -293,22 +302,32 @@ def submconv_depth_to_space(coarse: torch.Tensor, coarse_feats: torch.Tensor, ma
 
 class RulebookCache:
     """One rulebook per coordinate set, looked up by a caller-chosen key
-    (the upstream library's indice_key), built on first use."""
+    (the upstream library's indice_key), built on first use.
+
+    A cached map is reused only for the very coordinate tensor it was built from
+    (the same tensor object, not modified in place since: its version counter is
+    unchanged) and the same grid and batch count.  Any other tensor under the key,
+    even one of the same size, rebuilds the map and replaces the entry."""
 
     def __init__(self):
         self._maps = {}
 
     def get(self, key, coords: torch.Tensor, res: int, batch: Optional[int] = None) -> Rulebook:
-        rb = self._maps.get(key)
-        if rb is None or rb.n != coords.shape[0]:
-            rb = submconv_build_map(coords, res, batch)
-            self._maps[key] = rb
+        entry = self._maps.get(key)
+        if entry is not None:
+            rb, ref, version, r, b = entry
+            if (ref() is coords and coords._version == version and r == int(res)
+                    and (batch is None or b == int(batch))):
+                return rb
+            self.drop(key)
+        rb = submconv_build_map(coords, res, batch)
+        self._maps[key] = (rb, weakref.ref(coords), coords._version, int(res), rb.batch)
         return rb
 
     def drop(self, key):
-        rb = self._maps.pop(key, None)
-        if rb is not None:
-            rb.free()
+        entry = self._maps.pop(key, None)
+        if entry is not None:
+            entry[0].free()
 
     def clear(self):
         for k in list(self._maps):
@@ -407,3 +426,8 @@ def flip_ab(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tens
 def release_cache(device: int = -1) -> None:
     """Return the device blocks the library keeps for reuse (all devices when -1)."""
     _check(load_library().submconv_release_cache(int(device)), "submconv_release_cache")
+
+
+def set_cache_limit(nbytes: int) -> None:
+    """Per-device limit of the library's block cache in bytes (0: no caching)."""
+    _check(load_library().submconv_set_cache_limit(int(nbytes)), "submconv_set_cache_limit")

@@ -57,22 +57,31 @@ int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
 // Device memory of the library (rulebooks and scratch) comes from a block cache.
 // The driver's stream-ordered allocator costs tens to hundreds of microseconds of
 // host time per call for large blocks, and a map build allocates and frees its
-// scratch every time; so freed blocks are kept, per device and per stream, and handed
-// out again for requests of up to their size and at least half of it.  A block is
-// reused only on the stream it was freed on, which orders its new use after every
-// pending use.  The cache holds at most CACHE_CAP bytes per device beyond that, blocks
-// are returned to the driver; submconv_release_cache empties it.
+// scratch every time; so freed blocks are kept per device and handed out again for
+// requests of up to their size and at least half of it.
+//
+// Ordering: a block freed while work queued on a stream may still use it carries an
+// event recorded on that stream at the free.  Whoever takes the block next makes its
+// own stream wait for that event (hipStreamWaitEvent), so a block can move between
+// streams, and a stream destroyed meanwhile leaves no dangling ordering.  Blocks
+// freed right after their stream was synchronised carry no event.  Blocks of the
+// caller's stream are preferred, so the usual wait is on an event of the same stream.
+// The cache holds at most g_cap bytes per device (submconv_set_cache_limit; 2 GiB by
+// default); beyond that, freed blocks go back to the driver.  submconv_release_cache
+// empties it.
 namespace {
 struct Cached {
     void *p;
     size_t bytes;
     int device;
-    hipStream_t stream;
+    hipStream_t stream;  // where it was freed (preference only)
+    hipEvent_t ev;       // completes when that stream's prior work is done; nullptr: idle
 };
-constexpr size_t CACHE_CAP = size_t(16) << 30;
 std::mutex g_cache_mu;
+size_t g_cap = size_t(2) << 30;
 std::unordered_map<void *, std::pair<size_t, int>> g_live;  // block -> (bytes, device)
 std::vector<Cached> g_free;
+std::vector<std::pair<int, hipEvent_t>> g_events;  // spare events, by device
 size_t g_cached[64];
 
 size_t size_class(size_t bytes)  // 8 classes per power of two: at most 12.5% slack
@@ -84,12 +93,38 @@ size_t size_class(size_t bytes)  // 8 classes per power of two: at most 12.5% sl
     return (bytes + step - 1) / step * step;
 }
 
-void release_cached(int device)  // caller holds g_cache_mu
+void put_event(int device, hipEvent_t ev)  // caller holds g_cache_mu
 {
+    if (ev) g_events.push_back({device, ev});
+}
+
+hipEvent_t get_event(int device)  // caller holds g_cache_mu; current device == device
+{
+    for (size_t i = 0; i < g_events.size(); ++i)
+        if (g_events[i].first == device) {
+            hipEvent_t ev = g_events[i].second;
+            g_events[i] = g_events.back();
+            g_events.pop_back();
+            return ev;
+        }
+    hipEvent_t ev = nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return nullptr;
+    return ev;
+}
+
+// Return blocks to the driver once their last use has finished.  Caller holds g_cache_mu.
+void release_cached(int device)
+{
+    int cur = -1;
+    (void)hipGetDevice(&cur);
     for (size_t i = 0; i < g_free.size();) {
-        if (device < 0 || g_free[i].device == device) {
-            (void)hipFreeAsync(g_free[i].p, g_free[i].stream);
-            if (g_free[i].device >= 0 && g_free[i].device < 64) g_cached[g_free[i].device] -= g_free[i].bytes;
+        Cached &b = g_free[i];
+        if (device < 0 || b.device == device) {
+            if (b.ev) (void)hipEventSynchronize(b.ev);
+            if (b.device != cur && hipSetDevice(b.device) == hipSuccess) cur = b.device;
+            (void)hipFreeAsync(b.p, nullptr);  // its last use has finished (event above)
+            put_event(b.device, b.ev);
+            if (b.device >= 0 && b.device < 64) g_cached[b.device] -= b.bytes;
             g_free[i] = g_free.back();
             g_free.pop_back();
         } else {
@@ -110,14 +145,20 @@ int dev_alloc(void **p, size_t bytes, hipStream_t stream)
         size_t best = SIZE_MAX;
         for (size_t i = 0; i < g_free.size(); ++i) {
             const Cached &b = g_free[i];
-            if (b.device == dev && b.stream == stream && b.bytes >= bytes && b.bytes / 2 <= bytes &&
-                (best == SIZE_MAX || b.bytes < g_free[best].bytes))
-                best = i;
+            if (b.device != dev || b.bytes < bytes || b.bytes / 2 > bytes) continue;
+            if (best == SIZE_MAX) { best = i; continue; }
+            const Cached &c = g_free[best];
+            const bool bs = b.stream == stream, cs = c.stream == stream;
+            if ((bs && !cs) || (bs == cs && b.bytes < c.bytes)) best = i;
         }
         if (best != SIZE_MAX) {
-            *p = g_free[best].p;
-            g_live[*p] = {g_free[best].bytes, dev};
-            if (dev < 64) g_cached[dev] -= g_free[best].bytes;
+            Cached b = g_free[best];
+            if (b.ev && hipStreamWaitEvent(stream, b.ev, 0) != hipSuccess)
+                return fail(SUBMCONV_E_HIP, "hipStreamWaitEvent failed");
+            put_event(dev, b.ev);
+            *p = b.p;
+            g_live[*p] = {b.bytes, dev};
+            if (dev < 64) g_cached[dev] -= b.bytes;
             g_free[best] = g_free.back();
             g_free.pop_back();
             return SUBMCONV_OK;
@@ -129,7 +170,6 @@ int dev_alloc(void **p, size_t bytes, hipStream_t stream)
             std::lock_guard<std::mutex> lock(g_cache_mu);
             release_cached(dev);
         }
-        (void)hipDeviceSynchronize();
         e = hipMallocAsync(p, bytes, stream);
     }
     if (e != hipSuccess) {
@@ -142,7 +182,7 @@ int dev_alloc(void **p, size_t bytes, hipStream_t stream)
     return SUBMCONV_OK;
 }
 
-void dev_free(void *p, hipStream_t stream)
+static void dev_release(void *p, hipStream_t stream, bool idle)
 {
     if (!p) return;
     std::lock_guard<std::mutex> lock(g_cache_mu);
@@ -154,27 +194,27 @@ void dev_free(void *p, hipStream_t stream)
     const size_t bytes = it->second.first;
     const int dev = it->second.second;
     g_live.erase(it);
-    if (dev >= 0 && dev < 64 && g_cached[dev] + bytes <= CACHE_CAP) {
-        g_free.push_back({p, bytes, dev, stream});
+    int cur = -1;
+    if (dev >= 0 && dev < 64 && g_cached[dev] + bytes <= g_cap && hipGetDevice(&cur) == hipSuccess && cur == dev) {
+        hipEvent_t ev = nullptr;
+        if (!idle) {
+            ev = get_event(dev);
+            if (!ev || hipEventRecord(ev, stream) != hipSuccess) {
+                put_event(dev, ev);
+                (void)hipFreeAsync(p, stream);
+                return;
+            }
+        }
+        g_free.push_back({p, bytes, dev, stream, ev});
         g_cached[dev] += bytes;
     } else {
         (void)hipFreeAsync(p, stream);
     }
 }
 
-// Keep freed pool memory cached (once per device), so repeated builds do not
-// return it to the driver and fetch it again.
-static int keep_pool(int device)
-{
-    static bool done[64];
-    if (device < 0 || device >= 64 || done[device]) return SUBMCONV_OK;
-    hipMemPool_t pool;
-    SC_HIP(hipDeviceGetDefaultMemPool(&pool, device));
-    uint64_t threshold = UINT64_MAX;
-    SC_HIP(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold));
-    done[device] = true;
-    return SUBMCONV_OK;
-}
+void dev_free(void *p, hipStream_t stream) { dev_release(p, stream, false); }
+
+void dev_free_idle(void *p, hipStream_t stream) { dev_release(p, stream, true); }
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -238,8 +278,7 @@ int submconv_build_map(const int32_t *coords, int64_t n, int32_t res, int32_t ba
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) { delete r; return fail(SUBMCONV_E_HIP, "hipGetDevice failed"); }
     r->device = dev;
-    int st = keep_pool(dev);
-    if (st != SUBMCONV_OK) { delete r; return st; }
+    int st = SUBMCONV_OK;
     r->ngroups = (n + 31) / 32;
     r->nbr_in = nullptr;
 
@@ -480,7 +519,24 @@ int submconv_weight_convert(const void *src, int32_t layout, int32_t cout, int32
 int submconv_release_cache(int32_t device)
 {
     std::lock_guard<std::mutex> lock(g_cache_mu);
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(SUBMCONV_E_HIP, "hipGetDevice failed");
     release_cached(device);
+    (void)hipSetDevice(cur);
+    (void)hipDeviceSynchronize();  // the frees are queued on the null stream; let them land
+    return SUBMCONV_OK;
+}
+
+int submconv_set_cache_limit(int64_t bytes)
+{
+    if (bytes < 0) return fail(SUBMCONV_E_INVALID_ARG, "cache limit %lld < 0", (long long)bytes);
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    g_cap = (size_t)bytes;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(SUBMCONV_E_HIP, "hipGetDevice failed");
+    for (int d = 0; d < 64; ++d)  // shrink: drop cached blocks of devices above the new limit
+        if (g_cached[d] > g_cap) release_cached(d);
+    (void)hipSetDevice(cur);
     return SUBMCONV_OK;
 }
 

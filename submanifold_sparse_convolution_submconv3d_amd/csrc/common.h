@@ -62,6 +62,8 @@ int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream);
 
 int dev_alloc(void **p, size_t bytes, hipStream_t stream);
 void dev_free(void *p, hipStream_t stream);
+// dev_free for a block whose stream has just been synchronised (no pending use)
+void dev_free_idle(void *p, hipStream_t stream);
 
 // --------------------------------------------------------------------------
 // key layout: ((b << 3rb | z << 2rb | y << rb | x), rb = bits(res - 1)

@@ -424,6 +424,7 @@ static int coarse_group_bitmap(const int32_t *coords, const void *feats, int64_t
     DevStatus *st = (DevStatus *)(sc + o_st);
     uint32_t *total = (uint32_t *)&st->count;
     int status = SUBMCONV_OK;
+    bool synced = false;  // the status read has synchronised the stream
     do {
         if (hipMemsetAsync(bm, 0, (size_t)(words + 1) * 8, s) != hipSuccess ||
             hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) {
@@ -466,11 +467,13 @@ static int coarse_group_bitmap(const int32_t *coords, const void *feats, int64_t
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in a coarse grouping failed"); break; }
         DevStatus h;
         if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
+        synced = true;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
         else *out_m = (int64_t)h.count;
     } while (0);
-    dev_free(sc, s);
+    if (synced) dev_free_idle(sc, s);
+    else dev_free(sc, s);
     return status;
 }
 
@@ -504,6 +507,7 @@ static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, 
     uint32_t *tot = (uint32_t *)(sc + o_tot);
     DevStatus *st = (DevStatus *)(sc + o_st);
     int status = SUBMCONV_OK;
+    bool synced = false;  // the status read has synchronised the stream
     do {
         if (hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
         const unsigned grid = (unsigned)((n + 255) / 256);
@@ -535,11 +539,13 @@ static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, 
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in %s failed", op == COARSE_S2D ? "space_to_depth" : "downsample"); break; }
         DevStatus h;
         if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
+        synced = true;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
         else *out_m = (int64_t)h.count;
     } while (0);
-    dev_free(sc, s);
+    if (synced) dev_free_idle(sc, s);
+    else dev_free(sc, s);
     return status;
 }
 
@@ -692,6 +698,7 @@ static int expand(const int32_t *cc, const void *cf, const uint8_t *mask, int64_
     uint32_t *cnt = (uint32_t *)(sc + o_cnt), *base = (uint32_t *)(sc + o_base), *tot = (uint32_t *)(sc + o_tot);
     DevStatus *st = (DevStatus *)(sc + o_st);
     int status = SUBMCONV_OK;
+    bool synced = false;  // the status read has synchronised the stream
     do {
         if (hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
         hipLaunchKernelGGL(k_d2s_count, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, mask, m, cnt);
@@ -701,9 +708,11 @@ static int expand(const int32_t *cc, const void *cf, const uint8_t *mask, int64_
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in a masked expansion failed"); break; }
         DevStatus h;
         if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
+        synced = true;
         *out_n = (int64_t)h.count;
     } while (0);
-    dev_free(sc, s);
+    if (synced) dev_free_idle(sc, s);
+    else dev_free(sc, s);
     return status;
 }
 

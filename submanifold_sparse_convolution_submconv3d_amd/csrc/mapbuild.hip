@@ -725,6 +725,7 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     DevStatus *st = (DevStatus *)(scratch + o_stat);
     uint32_t *blk_taps = (uint32_t *)(scratch + o_cnt);
     int status = SUBMCONV_OK;
+    bool synced = false;  // the status read has synchronised the stream
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
         // one launch clears the status block and (dense path) the bitmap
@@ -772,12 +773,14 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
         if ((status = win_plan_build(rb, path >= 2 ? blk_taps : nullptr, (int64_t)grid, st, stream)) != SUBMCONV_OK) break;
         DevStatus h;
         if ((status = read_status(st, &h, stream)) != SUBMCONV_OK) break;
+        synced = true;
         if (path == 2 && !(h.flags & FLAG_RANGE) && (int64_t)(uint32_t)h.count != n) h.flags |= FLAG_DUPLICATE;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
         rb->taps = (int64_t)h.taps;
     } while (0);
-    dev_free(scratch, stream);
+    if (synced) dev_free_idle(scratch, stream);
+    else dev_free(scratch, stream);
     return status;
 }
 

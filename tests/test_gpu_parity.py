@@ -314,29 +314,32 @@ def _auto_kernel(cin, cout, dtype="f32"):
     return "lowc" if cin <= 32 and cout <= 32 else "generic"
 
 
-def sampled_check(c, res, batch, cin, cout, dtype, seed, bias, std, rows=3000, shuffled=False):
+def full_check(c, res, batch, cin, cout, dtype, seed, bias, std, calls=1):
+    """Every output row of a full-size workload against the C oracle (OpenMP, fp64),
+    the table bit-exact, and `calls` forwards on the one rulebook bit-identical to
+    the first (no atomics, so reruns must agree to the bit)."""
     feats, weight, b = synth.make_values(len(c), cin, cout, seed, std, bias)
     tf, tw, tb, f64, w64 = device_values(feats, weight, b, dtype)
     rb = sc.submconv_build_map(coords_dev(c), res, batch)
-    note("sampled forward n=%d %d->%d %s" % (len(c), cin, cout, dtype))
+    note("full forward n=%d %d->%d %s, %d call(s) on one rulebook" % (len(c), cin, cout, dtype, calls))
     out = sc.submconv_forward(tf, tw, tb, rb)
     table = rb.neighbors().cpu().numpy()
     expect_table = dense.neighbor_table(c, res, batch)
     np.testing.assert_array_equal(table, expect_table)
-    pick = np.sort(np.random.default_rng(seed + 7).choice(len(c), size=rows, replace=False))
-    pick = np.unique(np.concatenate([pick, [0, len(c) - 1]]))
-    expect = ref.forward(f64, w64, b, expect_table[pick])
-    got = to_f64(out[torch.from_numpy(pick).to(DEV)])
-    assert_close(got, expect, dtype, "sampled rows")
-    # a property that holds at any size: bit-identical reruns (no atomics)
-    out2 = sc.submconv_forward(tf, tw, tb, rb)
-    assert torch.equal(out, out2)
+    assert rb.taps_present == int((expect_table >= 0).sum())
+    expect = dense.forward(f64, w64, b, expect_table)
+    got = to_f64(out)
+    assert_close(got, expect, dtype, "all %d rows" % len(c))
+    for _ in range(calls - 1):
+        again = sc.submconv_forward(tf, tw, tb, rb)
+        assert torch.equal(out, again)
+    rb.free()
 
 
 # the rows MFMA kernel's three block layouts: on small sets two waves share a
 # 32-voxel column and split Cout (the random-set tests above); from 512 blocks of
 # 128 voxels on, one wave per column; from 2 * 256 * 256 voxels on, two columns per
-# wave.  Checked on sampled output rows against the oracle.
+# wave.  Every output row against the oracle.
 @pytest.mark.parametrize("n,cin,cout,dtype", [(70001, 64, 64, "f32"), (70001, 32, 128, "bf16"),
                                               (140001, 64, 64, "bf16"), (140001, 128, 64, "f32")])
 def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
@@ -346,12 +349,8 @@ def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
     rb = build(c, 64, 1)
     note("mfma rows layout n=%d %d->%d %s" % (n, cin, cout, dtype))
     out = sc.submconv_forward(tf, tw, tb, rb, variant=sc.KERNEL_MFMA)
-    table = dense.neighbor_table(c, 64, 1)
-    pick = np.sort(np.random.default_rng(n).choice(len(c), size=3000, replace=False))
-    pick = np.unique(np.concatenate([pick, [0, len(c) - 1]]))
-    expect = ref.forward(f64, w64, b, table[pick])
-    got = to_f64(out[torch.from_numpy(pick).to(DEV)])
-    assert_close(got, expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
+    expect = dense.forward(f64, w64, b, dense.neighbor_table(c, 64, 1))
+    assert_close(to_f64(out), expect, dtype, "mfma rows n=%d %d->%d %s" % (n, cin, cout, dtype))
 
 
 # The persistent fp32 128 -> 128 kernel: each block of 8 waves (one per CU) walks a
@@ -359,7 +358,7 @@ def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
 # the waves when 1 to 4 columns remain (5 to 7: idle waves).  With 256 blocks the
 # columns per block are: 24576 voxels 3; 40000 voxels 4 or 5; 52000 voxels 6 or 7;
 # 65536 voxels 8 (one full round, no partial one); 146279 voxels 17 or 18 (two full
-# rounds, then 1 or 2).  Sampled rows against the oracle.
+# rounds, then 1 or 2).  Every output row against the oracle.
 @pytest.mark.parametrize("n", [24576, 40000, 52000, 65536, 146279])
 def test_forward_mfma_persistent_rounds(n):
     c = synth.random_coords(n, 64, 1, 23)
@@ -368,12 +367,8 @@ def test_forward_mfma_persistent_rounds(n):
     rb = build(c, 64, 1)
     note("mfma persistent rounds n=%d" % n)
     out = sc.submconv_forward(tf, tw, tb, rb, variant=sc.KERNEL_MFMA)
-    table = dense.neighbor_table(c, 64, 1)
-    pick = np.sort(np.random.default_rng(n + 1).choice(len(c), size=3000, replace=False))
-    pick = np.unique(np.concatenate([pick, [0, len(c) - 1]]))
-    expect = ref.forward(f64, w64, b, table[pick])
-    got = to_f64(out[torch.from_numpy(pick).to(DEV)])
-    assert_close(got, expect, "f32", "mfma persistent n=%d" % n)
+    expect = dense.forward(f64, w64, b, dense.neighbor_table(c, 64, 1))
+    assert_close(to_f64(out), expect, "f32", "mfma persistent n=%d" % n)
 
 
 # Sets of 1 to 300 voxels through the automatic kernel choice: one voxel, one ragged
@@ -437,15 +432,28 @@ def test_forward_size_caps(ch, kernel, depth):
     rb.free()
 
 
-def test_forward_workload4_sampled():
+# Workload 4 (4 x 256^3 shells, 1.19M voxels, 64 -> 64 bf16; the map is built once
+# and the forward runs 4 times on it) and workload 5 (the 512^3 subdivision of a 256^3
+# shell, 3.24M voxels, 32 -> 32 bf16): every output row against the oracle.
+def test_forward_workload4_full():
     w, c = synth.workload(4)
-    sampled_check(c, w.res, w.batch, w.cin, w.cout, "bf16", w.value_seed, w.bias, w.weight_std)
+    full_check(c, w.res, w.batch, w.cin, w.cout, "bf16", w.value_seed, w.bias, w.weight_std, calls=4)
 
 
-def test_forward_workload5_sampled():
+def test_forward_workload5_full():
     w, parent = synth.workload(5)
     kids = dense.subdivide(parent)
-    sampled_check(kids, w.res, 1, w.cin, w.cout, "bf16", w.value_seed, w.bias, w.weight_std)
+    full_check(kids, w.res, 1, w.cin, w.cout, "bf16", w.value_seed, w.bias, w.weight_std, calls=2)
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_forward_workload_shuffled_full(idx):
+    """The same workloads in a seeded random row order (every row against the oracle)."""
+    w, c = synth.workload(idx)
+    if idx == 5:
+        c = dense.subdivide(c)
+    c = np.ascontiguousarray(c[synth.shuffle_rows(len(c), 500 + idx)])
+    full_check(c, w.res, w.batch, w.cin, w.cout, "bf16", w.value_seed + 1, w.bias, w.weight_std)
 
 
 def test_forward_shuffled_rows_permute_output():
@@ -478,6 +486,67 @@ def test_rulebook_cache_reuse():
     assert a is b and len(cache) == 1
     cache.clear()
     assert len(cache) == 0
+
+
+def test_rulebook_cache_rebuilds_for_another_set_of_the_same_size():
+    """Under one key, a different coordinate set with the same row count (another
+    tensor, or the same tensor changed in place) must get its own map, never the
+    cached one."""
+    n = 3000
+    c1 = synth.random_coords(n, 24, 1, 61)
+    c2 = synth.random_coords(n, 24, 1, 62)
+    assert not np.array_equal(c1, c2)
+    cache = sc.RulebookCache()
+    t1, t2 = coords_dev(c1), coords_dev(c2)
+    note("rulebook cache: same size, other set")
+    a = cache.get("k", t1, 24, 1)
+    np.testing.assert_array_equal(a.neighbors().cpu().numpy(), dense.neighbor_table(c1, 24, 1))
+    b = cache.get("k", t2, 24, 1)
+    assert b is not a and len(cache) == 1
+    np.testing.assert_array_equal(b.neighbors().cpu().numpy(), dense.neighbor_table(c2, 24, 1))
+    t2.copy_(t1)                       # in place: the version counter moves, the map is rebuilt
+    c = cache.get("k", t2, 24, 1)
+    assert c is not b
+    np.testing.assert_array_equal(c.neighbors().cpu().numpy(), dense.neighbor_table(c1, 24, 1))
+    assert cache.get("k", t2, 24, 1) is c
+    cache.clear()
+
+
+def test_block_cache_limit_and_cross_stream_reuse():
+    """With caching off every block goes back to the driver; with it on, a block freed
+    on one stream (work still queued there) is reused on another only after that work:
+    the tables built on the second stream stay exact."""
+    w2, c2 = synth.workload(2)
+    e2 = dense.neighbor_table(c2, w2.res, 1)
+    feats, weight, b = synth.make_values(len(c2), 64, 64, 3)
+    tf, tw, tb, f64, w64 = device_values(feats, weight, b, "f32")
+    expect = dense.forward(f64, w64, b, e2)
+    note("block cache limit 0")
+    sc.set_cache_limit(0)
+    rb = build(c2, w2.res, 1)
+    np.testing.assert_array_equal(rb.neighbors().cpu().numpy(), e2)
+    rb.free()
+    sc.set_cache_limit(2 << 30)
+    note("block cache cross-stream reuse")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for it in range(3):
+        with torch.cuda.stream(s1):
+            rb = sc.submconv_build_map(coords_dev(c2), w2.res, 1)
+            out = sc.submconv_forward(tf, tw, tb, rb)
+            outs.append(out)
+            rb.free()                  # queued forward still reads it; an event guards reuse
+        with torch.cuda.stream(s2):
+            rb2 = sc.submconv_build_map(coords_dev(c2), w2.res, 1)
+            got = rb2.neighbors()
+            rb2.free()
+        s2.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), e2)
+    s1.synchronize()
+    for out in outs:
+        assert_close(to_f64(out), expect, "f32", "forward before a cross-stream reuse")
+    with pytest.raises(sc.SubmconvError):
+        sc.set_cache_limit(-1)
 
 
 # ---------------------------------------------------------------- helpers

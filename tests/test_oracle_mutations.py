@@ -105,3 +105,21 @@ def test_partial_mirror_is_caught(monkeypatch):
     monkeypatch.setattr(ref, "mirror_krsc", lambda w: np.ascontiguousarray(np.asarray(w)[:, ::-1, ::-1, :, :]))
     with pytest.raises(AssertionError):
         pins.test_weight_layouts_against_dense_conv3d()
+
+
+def _c_order_child(slot, f=2):
+    return (slot // (f * f) % f, (slot // f) % f, slot % f)
+
+
+def _c_order_slot(z, y, x, f=2):
+    return (z % f) * f * f + (y % f) * f + (x % f)
+
+
+@pytest.mark.parametrize("attr,impl", [("child_offset", _c_order_child), ("s2d_slot", _c_order_slot)])
+def test_c_order_slot_mutations_are_caught(monkeypatch, attr, impl):
+    """Decoding or encoding the slot in C order (subdivide's order) instead of axis 0
+    fastest must fail the hand-worked space-to-depth example."""
+    import test_oracle_pins as pins
+    monkeypatch.setattr(ref, attr, impl)
+    with pytest.raises(AssertionError):
+        pins.test_s2d_hand_example_golden()

@@ -376,6 +376,26 @@ def test_i14_s2d_round_trip_and_zero_fill():
     assert len(all_c) == 8 * len(cc)
 
 
+def test_s2d_hand_example_golden():
+    """Space-to-depth and both inverses against a hand-worked example
+    (tests/golden/s2d_hand_example.json): coarse coordinates and slots, the
+    channel layout, zero rows of unoccupied slots, and the children of the
+    unmasked inverse in slot order."""
+    g = json.load(open(os.path.join(GOLDEN, "s2d_hand_example.json")))
+    coords = np.array(g["fine_coords"], np.int32)
+    feats = np.array(g["fine_feats"], np.float64)
+    cc, cf, mask = ref.space_to_depth(coords, feats)
+    np.testing.assert_array_equal(cc, g["coarse_coords"])
+    np.testing.assert_array_equal(cf, g["coarse_feats"])
+    np.testing.assert_array_equal(mask, g["mask"])
+    all_c, all_f = ref.depth_to_space(cc, cf)
+    np.testing.assert_array_equal(all_c, g["unmasked_children_coords"])
+    np.testing.assert_array_equal(all_f, g["unmasked_children_feats"])
+    kc, kf = ref.depth_to_space(cc, cf, mask)
+    np.testing.assert_array_equal(kc, g["masked_children_coords"])
+    np.testing.assert_array_equal(kf, g["masked_children_feats"])
+
+
 def test_i14_masked_upsample():
     coords = np.array([[0, 1, 2, 3], [0, 4, 4, 4], [1, 0, 0, 0]], np.int32)
     feats = np.array([[1.0], [2.0], [3.0]])
