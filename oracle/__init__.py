@@ -67,6 +67,8 @@ def _load():
                                        ctypes.c_int64, f64p]
         lib.oracle_subdivide.argtypes = [i32p, ctypes.c_int64, i32p]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int32]
+        lib.oracle_set_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -125,6 +127,11 @@ class dense:
     @staticmethod
     def num_threads() -> int:
         return int(_load().oracle_num_threads())
+
+    @staticmethod
+    def set_threads(threads: int) -> None:
+        """Threads of the parallel loops from now on (1 for the single-thread timing)."""
+        _check(_load().oracle_set_threads(int(threads)))
 
 
 __all__ = ["reference", "dense", "build_oracle", "OracleError"]

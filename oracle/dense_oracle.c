@@ -118,3 +118,14 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads used by the parallel loops from now on (timing of the single-thread leg). */
+int oracle_set_threads(int32_t threads)
+{
+    if (threads < 1) return ORACLE_E_ARG;
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(threads);
+#endif
+    return ORACLE_OK;
+}

@@ -184,7 +184,8 @@ def _cfg1():
 
 
 def _cfg2():
-    return _mask_coords([ellipsoid_union_shell(64, 3, seed=1, axes_lo=14, axes_hi=28,
+    # geometry seed 12: 20,384 voxels, inside both "~20k" and 18.9k +- 10%
+    return _mask_coords([ellipsoid_union_shell(64, 3, seed=12, axes_lo=14, axes_hi=28,
                                                centre_jitter=3.5, t=1)])
 
 

@@ -443,7 +443,7 @@ def test_errors(impl):
 # ---------------------------------------------------------------- workloads and bf16
 
 def test_workload_sizes():
-    expect = {1: (450, 450), 2: (18000, 26000), 3: (131000, 161000)}
+    expect = {1: (450, 450), 2: (17010, 20790), 3: (131000, 161000)}   # 18.9k +- 10%; 146k +- 10%
     for idx, (lo, hi) in expect.items():
         _, c = synth.workload(idx)
         assert lo <= len(c) <= hi
