@@ -206,6 +206,29 @@ int submconv_depth_to_space(const int32_t *coarse_coords, const void *coarse_fea
 int submconv_upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int32_t c,
                              int32_t dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream);
 
+/*
+ * submconv_upsample_masked for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as submconv_upsample_masked, and the same kernels, but
+ * the scratch (per-voxel child counts, their scan, the total) lives in one fixed device
+ * array of SUBMCONV_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from the
+ * first call on that GPU until the process ends.  The call makes no hipMalloc, hipFree
+ * or other allocating call; the child count is read back through a host stack word.
+ *
+ *   n : 0 <= n <= SUBMCONV_NOALLOC_MAX_N, else E_UNSUPPORTED (checked before any
+ *       device work).
+ *
+ * Every call on a GPU uses that GPU's one array; nothing in it needs clearing (each
+ * word read is written first by the same call).  Calls that overlap in time on one GPU
+ * (from several host threads or on several streams) race on the array and must be
+ * serialised by the caller.  Synchronises `stream` once to read the count.
+ */
+#define SUBMCONV_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define SUBMCONV_NOALLOC_MAX_N 4000000
+int submconv_upsample_masked_noalloc(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n,
+                                     int32_t c, int32_t dtype, int32_t *out_coords, void *out_feats,
+                                     int64_t *out_n, void *stream);
+
 /* Pooling modes of submconv_downsample. */
 #define SUBMCONV_POOL_MAX 0
 #define SUBMCONV_POOL_MEAN 1

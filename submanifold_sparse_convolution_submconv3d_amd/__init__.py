@@ -86,6 +86,7 @@ def load_library():
         "submconv_space_to_depth": [vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, i64p, vp],
         "submconv_depth_to_space": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
         "submconv_upsample_masked": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
+        "submconv_upsample_masked_noalloc": [vp, vp, vp, i64, i32, i32, vp, vp, i64p, vp],
         "submconv_downsample": [vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64p, vp],
         "submconv_classify_5d": [i64p, i32, i32p],
         "submconv_release_cache": [i32],

@@ -27,6 +27,9 @@ int depth_to_space(const int32_t *cc, const void *cf, const uint8_t *mask, int64
                    int dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
 int upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int c, int dtype,
                     int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
+int upsample_masked_noalloc(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int c,
+                            int dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s);
+size_t noalloc_expand_bytes(int64_t m);
 int downsample(const int32_t *coords, const void *feats, int64_t n, int c, int dtype, int res, int batch,
                int mean, int32_t *out_coords, void *out_feats, int64_t *out_m, hipStream_t s);
 int classify_5d(const int64_t *shape, int hint, int *layout);
@@ -451,12 +454,14 @@ int submconv_depth_to_space(const int32_t *coarse_coords, const void *coarse_fea
                           out_n, (hipStream_t)stream);
 }
 
-int submconv_upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int32_t c,
-                             int32_t dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream)
+static int check_upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n,
+                                 int32_t c, int32_t dtype, int32_t *out_coords, void *out_feats, int64_t *out_n,
+                                 int64_t max_n)
 {
     if (!out_n) return fail(SUBMCONV_E_INVALID_ARG, "out_n is NULL");
     *out_n = 0;
     if (n < 0 || n >= (int64_t(1) << 28)) return fail(SUBMCONV_E_INVALID_ARG, "n = %lld outside [0, 2^28)", (long long)n);
+    if (n > max_n) return fail(SUBMCONV_E_UNSUPPORTED, "n = %lld above the limit %lld", (long long)n, (long long)max_n);
     if (dtype != SUBMCONV_F32 && dtype != SUBMCONV_BF16) return fail(SUBMCONV_E_UNSUPPORTED, "dtype %d", dtype);
     if (c < 1 || c > 65536) return fail(SUBMCONV_E_INVALID_ARG, "c = %d", c);
     if (n == 0) return SUBMCONV_OK;
@@ -468,7 +473,29 @@ int submconv_upsample_masked(const int32_t *coords, const void *feats, const uin
         overlaps(out_feats, (size_t)n * 8 * c * es, mask, (size_t)n * 8) ||
         overlaps(out_coords, (size_t)n * 128, mask, (size_t)n * 8))
         return fail(SUBMCONV_E_ALIAS, "an output overlaps an input");
+    return SUBMCONV_OK;
+}
+
+int submconv_upsample_masked(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int32_t c,
+                             int32_t dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, void *stream)
+{
+    SC_CHECK(check_upsample_masked(coords, feats, mask, n, c, dtype, out_coords, out_feats, out_n, int64_t(1) << 28));
+    if (n == 0) return SUBMCONV_OK;
     return upsample_masked(coords, feats, mask, n, c, dtype, out_coords, out_feats, out_n, (hipStream_t)stream);
+}
+
+int submconv_upsample_masked_noalloc(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n,
+                                     int32_t c, int32_t dtype, int32_t *out_coords, void *out_feats,
+                                     int64_t *out_n, void *stream)
+{
+    static_assert(SUBMCONV_NOALLOC_MAX_N >= 1, "limit");
+    SC_CHECK(check_upsample_masked(coords, feats, mask, n, c, dtype, out_coords, out_feats, out_n,
+                                   SUBMCONV_NOALLOC_MAX_N));
+    if (n == 0) return SUBMCONV_OK;
+    if (noalloc_expand_bytes(n) > SUBMCONV_NOALLOC_SCRATCH_BYTES)  // cannot happen for n <= the limit
+        return fail(SUBMCONV_E_UNSUPPORTED, "n = %lld does not fit the scratch array", (long long)n);
+    return upsample_masked_noalloc(coords, feats, mask, n, c, dtype, out_coords, out_feats, out_n,
+                                   (hipStream_t)stream);
 }
 
 int submconv_downsample(const int32_t *coords, const void *feats, int64_t n, int32_t c, int32_t dtype, int32_t res,

@@ -18,6 +18,8 @@
 // downsample      - pools each coarse voxel's children by max or mean, coarse
 //                   rows ascending (same commit: the mode is explicit); the same
 //                   sort as space_to_depth groups the children.
+#include <mutex>
+
 #include "common.h"
 
 namespace sc {
@@ -208,7 +210,9 @@ __global__ __launch_bounds__(256) void k_excl_to_seg(const uint32_t *__restrict_
 
 __global__ void k_store_count(const uint32_t *__restrict__ total, DevStatus *st)
 {
-    st->count = *total;
+    DevStatus v{};
+    v.count = *total;
+    *st = v;
 }
 
 // Coarse coordinates and the sorted position where each coarse voxel's children start.
@@ -680,6 +684,37 @@ static int launch_expand(const int32_t *cc, const void *cf, const uint8_t *mask,
     return SUBMCONV_OK;
 }
 
+// Scratch of a masked expansion of m voxels: per-voxel child counts, their exclusive
+// scan, the total, the scan's tile sums and a status block.
+struct ExpandScratch {
+    size_t cnt, base, tot, scan, st, bytes;
+    explicit ExpandScratch(int64_t m)
+    {
+        auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+        cnt = 0;
+        base = up((size_t)m * 4);
+        tot = base + up((size_t)m * 4);
+        scan = tot + 256;
+        st = scan + up(scan_scratch_bytes(m));
+        bytes = st + sizeof(DevStatus);
+    }
+};
+
+// Count the flagged slots per voxel, scan the counts and write the children, with the
+// scratch at `sc` (ExpandScratch(m).bytes).  Every scratch word that is read is written
+// first in the same call, so nothing needs clearing.  The child count ends up in the
+// scratch's total word.
+template <bool REPL>
+static int expand_masked_enqueue(const int32_t *cc, const void *cf, const uint8_t *mask, int64_t m, int c, int dtype,
+                                 int32_t *out_coords, void *out_feats, char *sc, hipStream_t s)
+{
+    const ExpandScratch L(m);
+    uint32_t *cnt = (uint32_t *)(sc + L.cnt), *base = (uint32_t *)(sc + L.base), *tot = (uint32_t *)(sc + L.tot);
+    hipLaunchKernelGGL(k_d2s_count, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, mask, m, cnt);
+    SC_CHECK(exclusive_scan_u32(cnt, base, m, tot, sc + L.scan, s));
+    return launch_expand<REPL>(cc, cf, mask, base, m, c, dtype, out_coords, out_feats, s);
+}
+
 template <bool REPL>
 static int expand(const int32_t *cc, const void *cf, const uint8_t *mask, int64_t m, int c, int dtype,
                   int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s)
@@ -690,21 +725,16 @@ static int expand(const int32_t *cc, const void *cf, const uint8_t *mask, int64_
         if (status == SUBMCONV_OK) *out_n = 8 * m;
         return status;
     }
-    auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
-    const size_t o_cnt = 0, o_base = up((size_t)m * 4), o_tot = o_base + up((size_t)m * 4);
-    const size_t o_scan = o_tot + 256, o_st = o_scan + up(scan_scratch_bytes(m));
+    const ExpandScratch L(m);
     char *sc = nullptr;
-    SC_CHECK(dev_alloc((void **)&sc, o_st + sizeof(DevStatus), s));
-    uint32_t *cnt = (uint32_t *)(sc + o_cnt), *base = (uint32_t *)(sc + o_base), *tot = (uint32_t *)(sc + o_tot);
-    DevStatus *st = (DevStatus *)(sc + o_st);
+    SC_CHECK(dev_alloc((void **)&sc, L.bytes, s));
+    DevStatus *st = (DevStatus *)(sc + L.st);
     int status = SUBMCONV_OK;
     bool synced = false;  // the status read has synchronised the stream
     do {
-        if (hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
-        hipLaunchKernelGGL(k_d2s_count, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, mask, m, cnt);
-        if ((status = exclusive_scan_u32(cnt, base, m, tot, sc + o_scan, s)) != SUBMCONV_OK) break;
-        if ((status = launch_expand<REPL>(cc, cf, mask, base, m, c, dtype, out_coords, out_feats, s)) != SUBMCONV_OK) break;
-        hipLaunchKernelGGL(k_store_count, dim3(1), dim3(1), 0, s, tot, st);
+        if ((status = expand_masked_enqueue<REPL>(cc, cf, mask, m, c, dtype, out_coords, out_feats, sc, s)) !=
+            SUBMCONV_OK) break;
+        hipLaunchKernelGGL(k_store_count, dim3(1), dim3(1), 0, s, (const uint32_t *)(sc + L.tot), st);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in a masked expansion failed"); break; }
         DevStatus h;
         if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
@@ -714,6 +744,56 @@ static int expand(const int32_t *cc, const void *cf, const uint8_t *mask, int64_
     if (synced) dev_free_idle(sc, s);
     else dev_free(sc, s);
     return status;
+}
+
+// ---------------------------------------------------------------------------
+// the masked upsample without allocation
+// ---------------------------------------------------------------------------
+
+// The scratch of submconv_upsample_masked_noalloc: one fixed array per device, held
+// until the process ends.  Host code must not pass `scratch` itself to a kernel (on
+// the host it is a stand-in for the symbol, not a device address): its device
+// address is looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_dev.
+constexpr size_t NOALLOC_SCRATCH_BYTES = SUBMCONV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static char *g_scratch_dev[64];
+
+static int noalloc_scratch(char **p)
+{
+    int dev = 0;
+    SC_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(SUBMCONV_E_UNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *q = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !q)
+            return fail(SUBMCONV_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = (char *)q;
+    }
+    *p = g_scratch_dev[dev];
+    return SUBMCONV_OK;
+}
+
+size_t noalloc_expand_bytes(int64_t m) { return ExpandScratch(m).bytes; }
+
+int upsample_masked_noalloc(const int32_t *coords, const void *feats, const uint8_t *mask, int64_t n, int c,
+                            int dtype, int32_t *out_coords, void *out_feats, int64_t *out_n, hipStream_t s)
+{
+    if (n == 0) { *out_n = 0; return SUBMCONV_OK; }
+    if (ExpandScratch(n).bytes > NOALLOC_SCRATCH_BYTES)
+        return fail(SUBMCONV_E_UNSUPPORTED, "n = %lld needs more than the %zu scratch bytes", (long long)n,
+                    NOALLOC_SCRATCH_BYTES);
+    char *sc = nullptr;
+    SC_CHECK(noalloc_scratch(&sc));
+    SC_CHECK(expand_masked_enqueue<true>(coords, feats, mask, n, c, dtype, out_coords, out_feats, sc, s));
+    uint32_t total = 0;  // pageable host word: no pinned staging block is allocated
+    SC_HIP(hipMemcpyAsync(&total, sc + ExpandScratch(n).tot, sizeof(total), hipMemcpyDeviceToHost, s));
+    SC_HIP(hipStreamSynchronize(s));
+    *out_n = (int64_t)total;
+    return SUBMCONV_OK;
 }
 
 int depth_to_space(const int32_t *cc, const void *cf, const uint8_t *mask, int64_t m, int c,

@@ -156,3 +156,16 @@ def test_product_path_does_not_reference_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "dense_oracle" not in text, f
+
+
+def test_noalloc_upsample_host_checks(lib):
+    """The allocation-free masked upsample refuses sizes above its scratch limit and
+    bad arguments on the host, before any device work."""
+    cnt = ctypes.c_int64(-1)
+    assert lib.submconv_upsample_masked_noalloc(None, None, None, 4000001, 8, 0, None, None,
+                                                ctypes.byref(cnt), None) == E_UNSUPPORTED
+    assert lib.submconv_upsample_masked_noalloc(None, None, None, 5, 8, 0, None, None,
+                                                ctypes.byref(cnt), None) == E_INVALID_ARG
+    assert lib.submconv_upsample_masked_noalloc(None, None, None, 5, 8, 0, None, None, None, None) == E_INVALID_ARG
+    assert lib.submconv_upsample_masked_noalloc(None, None, None, 0, 8, 0, None, None,
+                                                ctypes.byref(cnt), None) == 0 and cnt.value == 0
