@@ -137,22 +137,37 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
     return t
 
 
+def _raw_stream(index: int) -> int:
+    """The current HIP stream of device `index` as an integer handle."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
 def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return ctypes.c_void_p(_raw_stream(torch.device(device).index))
 
 
 class Rulebook:
     """A neighbour map built on the device for one coordinate set."""
 
-    def __init__(self, handle: ctypes.c_void_p, device: torch.device, stream: torch.cuda.Stream):
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device, stream: int, n: int, res: int, batch: int):
         self._h = handle
         self.device = device
-        self._stream = stream
-        lib = load_library()
-        n, res, batch, taps = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
-        _check(lib.submconv_rulebook_info(handle, ctypes.byref(n), ctypes.byref(res), ctypes.byref(batch),
-                                          ctypes.byref(taps)), "submconv_rulebook_info")
-        self.n, self.res, self.batch, self.taps_present = n.value, res.value, batch.value, taps.value
+        self._stream = stream          # raw handle of the stream it was built on
+        self.n, self.res, self.batch = n, res, batch
+        self._taps = None
+
+    @property
+    def taps_present(self) -> int:
+        """P, the number of entries of the neighbour table that are not -1."""
+        if self._taps is None:
+            taps = ctypes.c_int64()
+            _check(load_library().submconv_rulebook_info(self.handle, None, None, None, ctypes.byref(taps)),
+                   "submconv_rulebook_info")
+            self._taps = taps.value
+        return self._taps
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -163,7 +178,7 @@ class Rulebook:
     def neighbors(self) -> torch.Tensor:
         """A copy of the int32 [n,27] neighbour table (row i, tap k -> row or -1)."""
         out = torch.empty((self.n, 27), dtype=torch.int32, device=self.device)
-        with torch.cuda.device(self.device):
+        with _on_device(self.device):
             _check(load_library().submconv_rulebook_copy_neighbors(self.handle, ctypes.c_void_p(out.data_ptr()),
                                                                    _stream(self.device)),
                    "submconv_rulebook_copy_neighbors")
@@ -174,19 +189,37 @@ class Rulebook:
         device).  Work on other streams that still reads it must be ordered before
         that stream first, as for any stream-ordered free."""
         if self._h is not None and _lib is not None:
-            with torch.cuda.device(self.device):
-                s = stream if stream is not None else torch.cuda.current_stream(self.device)
-                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(s.cuda_stream))
+            with _on_device(self.device):
+                s = stream.cuda_stream if stream is not None else _raw_stream(self.device.index)
+                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(s))
         self._h = None
 
     def __del__(self):
         try:
             if self._h is not None and _lib is not None:
                 # garbage collection: the release is ordered on the stream the map was built on
-                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(self._stream.cuda_stream))
+                _lib.submconv_rulebook_free(self._h, ctypes.c_void_p(self._stream))
                 self._h = None
         except Exception:
             pass
+
+
+class _on_device:
+    """`with torch.cuda.device(d)` without its cost when d is already current."""
+
+    __slots__ = ("_ctx",)
+
+    def __init__(self, device: torch.device):
+        idx = device.index
+        self._ctx = None if idx is None or idx == torch.cuda.current_device() else torch.cuda.device(idx)
+
+    def __enter__(self):
+        if self._ctx is not None:
+            self._ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self._ctx is not None:
+            self._ctx.__exit__(*exc)
 
 
 def submconv_build_map(coords: torch.Tensor, res: int, batch: Optional[int] = None) -> Rulebook:
@@ -198,14 +231,15 @@ def submconv_build_map(coords: torch.Tensor, res: int, batch: Optional[int] = No
         raise ValueError("coords must be [N,4]")
     if batch is None:
         batch = int(coords[:, 0].max().item()) + 1 if coords.shape[0] else 1
-    lib = load_library()
+    lib = _lib if _lib is not None else load_library()
     h = ctypes.c_void_p()
-    with torch.cuda.device(coords.device):
-        stream = torch.cuda.current_stream(coords.device)
-        _check(lib.submconv_build_map(ctypes.c_void_p(coords.data_ptr()), coords.shape[0], int(res), int(batch),
-                                      ctypes.c_void_p(stream.cuda_stream), ctypes.byref(h)),
+    dev = coords.device
+    n, res, batch = coords.shape[0], int(res), int(batch)
+    with _on_device(dev):
+        stream = _raw_stream(dev.index)
+        _check(lib.submconv_build_map(coords.data_ptr(), n, res, batch, stream, ctypes.byref(h)),
                "submconv_build_map")
-        return Rulebook(h, coords.device, stream)
+        return Rulebook(h, dev, stream, n, res, batch)
 
 
 def submconv_forward(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor], rb: Rulebook,
@@ -230,7 +264,7 @@ def submconv_forward(feats: torch.Tensor, weight: torch.Tensor, bias: Optional[t
         _dev(out, "out", feats.dtype)
         if tuple(out.shape) != (rb.n, cout):
             raise ValueError("out must be [N,Cout]")
-    with torch.cuda.device(feats.device):
+    with _on_device(feats.device):
         _check(load_library().submconv_forward_variant(
             ctypes.c_void_p(feats.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
             ctypes.c_void_p(bias.data_ptr() if bias is not None else None), rb.handle,
@@ -250,7 +284,7 @@ def submconv_subdivide(coords: torch.Tensor, feats: Optional[torch.Tensor] = Non
         c, dt = feats.shape[1], _dtype_code(feats)
         out_f = torch.empty((8 * n, c), dtype=feats.dtype, device=feats.device)
         fp, ofp = feats.data_ptr(), out_f.data_ptr()
-    with torch.cuda.device(coords.device):
+    with _on_device(coords.device):
         _check(load_library().submconv_subdivide(ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(fp), n, c, dt,
                                                  ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(ofp),
                                                  _stream(coords.device)), "submconv_subdivide")
@@ -266,7 +300,7 @@ def submconv_space_to_depth(coords: torch.Tensor, feats: torch.Tensor, res: int,
     out_f = torch.empty((max(n, 1), 8 * c), dtype=feats.dtype, device=feats.device)
     mask = torch.empty((max(n, 1), 8), dtype=torch.uint8, device=feats.device)
     m = ctypes.c_int64()
-    with torch.cuda.device(coords.device):
+    with _on_device(coords.device):
         _check(load_library().submconv_space_to_depth(
             ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(feats.data_ptr()), n, c, _dtype_code(feats),
             int(res), int(batch), ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(out_f.data_ptr()),
@@ -292,7 +326,7 @@ def submconv_depth_to_space(coarse: torch.Tensor, coarse_feats: torch.Tensor, ma
     out_c = torch.empty((max(8 * m, 1), 4), dtype=torch.int32, device=coarse.device)
     out_f = torch.empty((max(8 * m, 1), c), dtype=coarse_feats.dtype, device=coarse.device)
     cnt = ctypes.c_int64()
-    with torch.cuda.device(coarse.device):
+    with _on_device(coarse.device):
         _check(load_library().submconv_depth_to_space(
             ctypes.c_void_p(coarse.data_ptr()), ctypes.c_void_p(coarse_feats.data_ptr()), ctypes.c_void_p(mp), m, c,
             _dtype_code(coarse_feats), ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(out_f.data_ptr()),
@@ -352,7 +386,7 @@ def submconv_upsample_masked(coords: torch.Tensor, feats: torch.Tensor, mask: to
     out_c = torch.empty((max(8 * n, 1), 4), dtype=torch.int32, device=coords.device)
     out_f = torch.empty((max(8 * n, 1), c), dtype=feats.dtype, device=feats.device)
     cnt = ctypes.c_int64()
-    with torch.cuda.device(coords.device):
+    with _on_device(coords.device):
         _check(load_library().submconv_upsample_masked(
             ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(feats.data_ptr()), ctypes.c_void_p(mask.data_ptr()),
             n, c, _dtype_code(feats), ctypes.c_void_p(out_c.data_ptr()), ctypes.c_void_p(out_f.data_ptr()),
@@ -371,7 +405,7 @@ def submconv_downsample(coords: torch.Tensor, feats: torch.Tensor, res: int, bat
     out_c = torch.empty((max(n, 1), 4), dtype=torch.int32, device=coords.device)
     out_f = torch.empty((max(n, 1), c), dtype=feats.dtype, device=feats.device)
     m = ctypes.c_int64()
-    with torch.cuda.device(coords.device):
+    with _on_device(coords.device):
         _check(load_library().submconv_downsample(
             ctypes.c_void_p(coords.data_ptr()), ctypes.c_void_p(feats.data_ptr()), n, c, _dtype_code(feats),
             int(res), int(batch), POOL_MAX if mode == "max" else POOL_MEAN, ctypes.c_void_p(out_c.data_ptr()),
@@ -409,7 +443,7 @@ def weight_to_krsc(weight: torch.Tensor, layout: Optional[str] = None, hint: Opt
     else:
         cout, cin = weight.shape[0], weight.shape[1]
     out = torch.empty((cout, 3, 3, 3, cin), dtype=weight.dtype, device=weight.device)
-    with torch.cuda.device(weight.device):
+    with _on_device(weight.device):
         _check(load_library().submconv_weight_convert(
             ctypes.c_void_p(weight.data_ptr()), _LAYOUTS[layout], cout, cin, _dtype_code(weight), int(bool(flip)),
             ctypes.c_void_p(out.data_ptr()), _stream(weight.device)), "submconv_weight_convert")

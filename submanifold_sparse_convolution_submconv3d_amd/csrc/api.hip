@@ -48,13 +48,32 @@ int fail(int status, const char *fmt, ...)
 
 static thread_local DevStatus *g_pinned = nullptr;
 
-int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
+static thread_local size_t g_pinned_bytes = 0;
+
+int read_status_counts(const DevStatus *d, int64_t ncounts, DevStatus *h, uint64_t *sum, hipStream_t stream)
 {
-    if (!g_pinned) SC_HIP(hipHostMalloc((void **)&g_pinned, sizeof(DevStatus), hipHostMallocDefault));
-    SC_HIP(hipMemcpyAsync(g_pinned, d, sizeof(DevStatus), hipMemcpyDeviceToHost, stream));
+    const size_t bytes = sizeof(DevStatus) + (size_t)ncounts * 4;
+    if (g_pinned_bytes < bytes) {  // grows to the largest read-back seen on this thread
+        if (g_pinned) (void)hipHostFree(g_pinned);
+        g_pinned = nullptr;
+        g_pinned_bytes = 0;
+        const size_t want = bytes < 4096 ? 4096 : bytes;
+        SC_HIP(hipHostMalloc((void **)&g_pinned, want, hipHostMallocDefault));
+        g_pinned_bytes = want;
+    }
+    SC_HIP(hipMemcpyAsync(g_pinned, d, bytes, hipMemcpyDeviceToHost, stream));
     SC_HIP(hipStreamSynchronize(stream));
     *h = *g_pinned;
+    uint64_t t = 0;
+    const uint32_t *c = (const uint32_t *)(g_pinned + 1);
+    for (int64_t i = 0; i < ncounts; ++i) t += c[i];
+    if (sum) *sum = t;
     return SUBMCONV_OK;
+}
+
+int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
+{
+    return read_status_counts(d, 0, h, nullptr, stream);
 }
 
 // Device memory of the library (rulebooks and scratch) comes from a block cache.

@@ -55,6 +55,9 @@ struct DevStatus {
 
 // Enqueue a copy of `d` to a pinned host block, synchronise `stream`, return it in `h`.
 int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream);
+// The same, together with `ncounts` uint32 counters stored right after `d`; their
+// sum is returned in *sum.
+int read_status_counts(const DevStatus *d, int64_t ncounts, DevStatus *h, uint64_t *sum, hipStream_t stream);
 
 // --------------------------------------------------------------------------
 // stream-ordered device memory

@@ -95,27 +95,46 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
     const int gbase = lane - (lane % COUT);                 // first lane of this voxel's group
     const float b = bias ? bias[o] : 0.f;
     const int64_t stride = (int64_t)gridDim.x * VPB;
+    // Taps in groups of G: a group's table decodes, then its row numbers, then its
+    // feature loads are each issued together, so a voxel costs a few memory round
+    // trips instead of two per tap.
+    constexpr int G = PER <= 2 ? 27 : (PER <= 8 ? 9 : 3);
     // every lane of a wave runs the same number of iterations (shuffles need all lanes)
     for (int64_t i0 = (int64_t)blockIdx.x * VPB; i0 < n; i0 += stride) {
         const int64_t s = i0 + threadIdx.x / COUT;
         const int64_t i = s < n ? (int64_t)perm[s] : -1;
         const bool live = (uint64_t)i < (uint64_t)n;
+        int32_t row[NBR_INTS];
+#pragma unroll
+        for (int q = 0; q < NBR_INTS; ++q) row[q] = live ? nbr[s * NBR_INTS + q] : 0;
+        if (!live) row[9] = 0;
         float acc = 0.f;
-        for (int k = 0; k < 27; ++k) {
-            int32_t j = live ? nbr_at(nbr + s * NBR_INTS, k) : -1;
-            j = (uint32_t)j < (uint64_t)n ? perm[j] : -1;
-            if ((uint32_t)j >= (uint64_t)n) j = -1;
-            float f[PER];
 #pragma unroll
-            for (int m = 0; m < PER; ++m) {
-                const int c = o + m * COUT;
-                f[m] = (j >= 0 && c < CIN) ? Elem<T>::to_f32(feats[(int64_t)j * CIN + c]) : 0.f;
+        for (int k0 = 0; k0 < 27; k0 += G) {
+            int32_t j[G];
+#pragma unroll
+            for (int t = 0; t < G; ++t) {
+                const int32_t p = nbr_at(row, k0 + t);
+                j[t] = (uint32_t)p < (uint64_t)n ? perm[p] : -1;
             }
-            const float *wk = s_w + (flip ? 26 - k : k) * CIN * COUT + o;
+            float f[G][PER];
 #pragma unroll
-            for (int c = 0; c < CIN; ++c) {
-                const float fc = __shfl(f[c / COUT], gbase + (c % COUT), 64);
-                acc = fmaf(wk[c * COUT], fc, acc);
+            for (int t = 0; t < G; ++t)
+#pragma unroll
+                for (int m = 0; m < PER; ++m) {
+                    const int c = o + m * COUT;
+                    f[t][m] = ((uint32_t)j[t] < (uint64_t)n && c < CIN)
+                                  ? Elem<T>::to_f32(feats[(int64_t)j[t] * CIN + c]) : 0.f;
+                }
+#pragma unroll
+            for (int t = 0; t < G; ++t) {
+                const int k = k0 + t;
+                const float *wk = s_w + (flip ? 26 - k : k) * CIN * COUT + o;
+#pragma unroll
+                for (int c = 0; c < CIN; ++c) {
+                    const float fc = __shfl(f[t][c / COUT], gbase + (c % COUT), 64);
+                    acc = fmaf(wk[c * COUT], fc, acc);
+                }
             }
         }
         if (live) out[i * COUT + o] = Elem<T>::from_f32(acc + b);

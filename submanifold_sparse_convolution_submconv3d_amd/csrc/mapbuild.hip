@@ -8,27 +8,32 @@
 //
 // What the rulebook keeps, all indexed by sorted position s (C order of
 // (b, z, y, x)):
-//   keys[s], perm[s] (the input row of sorted voxel s),
+//   perm[s]       the input row of sorted voxel s,
 //   nbr_sp[s]     the SORTED POSITIONS of the voxels at key[s] + offset(k), in the
 //                 row form of NBR_INTS ints (common.h): per (dz, dy) row the first
 //                 present position and presence bits, 40 bytes instead of 108,
-//   gwin[g]        per group of 32 consecutive sorted voxels and per (dz, dy)
-//                  row: the first and last sorted position the group's
-//                  neighbours in that row occupy.  A kernel merges the windows
-//                  of the groups it processes into a few ranges of sorted
-//                  positions, stages them in LDS and indexes them directly.
+//   plan[t]       per tile of 128 sorted voxels, the staging plan of the windowed
+//                 forward kernel (winplan.h), built from the group windows: per
+//                 group of 32 consecutive sorted voxels and per (dz, dy) row, the
+//                 first and last sorted position the group's neighbours in that row
+//                 occupy (kept in LDS, or in gwin[] by the sparse path),
+//   keys[s]       the sorted keys.
 // The input-order table nbr[i][k] (input rows) is derived from these on request.
 //
-// Dense key space (2^nbits bitmap bits affordable next to N):
-//   mark     - set the key's bit in an occupancy bitmap (no-return atomicOr;
-//              lanes of a wave that hit the same word are combined first);
-//   scan     - exclusive scan of the bitmap words' popcounts; its total is the
-//              number of distinct keys, so a total below N means a duplicate;
-//   rank     - a key's sorted position is prefix[word] + popcount of the lower
-//              bits of its word: one radix pass whose digit is the whole key
-//              (histogram = bitmap, counts are 0/1 because keys are distinct);
-//   resolve  - per sorted voxel, each neighbour is a bit test plus the same rank
-//              query; no gathers, and table rows are written as coalesced runs.
+// Dense key space (2^nbits bitmap bits affordable next to N), five launches:
+//   clear    - zero the status block, the occupancy bitmap and the scan's flags;
+//   mark     - validate and pack each row's key and set its bit in the bitmap
+//              (a per-block LDS hash of bitmap words first, then one device-scope
+//              OR per distinct word and block);
+//   scan     - single-pass exclusive scan of the words' popcounts (decoupled
+//              look-back across blocks): every word's global prefix and the
+//              distinct-key count (a count below N means a duplicate);
+//   rank     - input row i with key k sits at sorted position prefix[k / 64] + (set
+//              bits of its word below k): one radix pass whose digit is the whole key;
+//   resolve + plan - each block of 256 sorted positions forms each neighbour row
+//              from three bits and one rank query per (dz, dy) row, writes the rows as
+//              coalesced runs, and computes the staging plans of its two tiles from
+//              the group windows in LDS.
 // Sparse key space (huge grid, few voxels):
 //   pack + multi-pass LSD radix sort, then per tile of 256 sorted voxels: the x
 //   neighbours of the centre row are the adjacent sorted entries; for each of the
@@ -40,6 +45,7 @@
 // before packing and every neighbour coordinate is bounds-checked before its key
 // is formed, so a key never wraps into the next row, plane or batch entry.
 #include "common.h"
+#include "winplan.h"
 
 namespace sc {
 
@@ -213,123 +219,266 @@ __global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, i
     }
 }
 
+// Single-pass exclusive scan of the bitmap words' popcounts.  Tile t (one block)
+// covers `chunks` runs of 256 x WPT words.  Its total is published in look[t] at once
+// (flag LB_AGG); wave 0 then walks back over its predecessors 64 at a time, adding
+// aggregates until it meets an inclusive prefix (flag LB_INCL; the space before tile
+// 0 counts as an inclusive 0), and publishes its own inclusive prefix.  Every block
+// waits only on lower-numbered blocks, and the grid is kept small enough
+// (SK_MAX_TILES) to be resident at once, so every wait ends.  Every word then gets its
+// global exclusive prefix.  The grand total goes to st->count (below n means a
+// duplicate or an invalid row).
+constexpr int SK_MAX_TILES = 1024;
+constexpr unsigned long long LB_AGG = 1ull << 62, LB_INCL = 1ull << 63, LB_VAL = 0xffffffffull;
+
+template <int WPT>
+__device__ __forceinline__ void sk_words(const unsigned long long *__restrict__ bm, int64_t words, int64_t w0,
+                                         unsigned long long (&v)[WPT])
+{
+    if (w0 + WPT <= words) {
+        const ulonglong2 *src = (const ulonglong2 *)(bm + w0);  // w0 is a multiple of WPT (even)
+#pragma unroll
+        for (int h = 0; h < WPT / 2; ++h) {
+            const ulonglong2 x = src[h];
+            v[2 * h] = x.x;
+            v[2 * h + 1] = x.y;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < WPT; ++e) v[e] = w0 + e < words ? bm[w0 + e] : 0ull;
+    }
+}
+
+template <int WPT>
+__global__ __launch_bounds__(256) void k_scan_words(const unsigned long long *__restrict__ bm, int64_t words,
+                                                    int chunks, uint32_t *__restrict__ prefix,
+                                                    unsigned long long *look, DevStatus *st)
+{
+    constexpr int CH = 256 * WPT;  // words per chunk
+    __shared__ uint32_t s_red[4];
+    __shared__ uint32_t s_excl;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t t = blockIdx.x;
+    const int64_t base = t * (int64_t)chunks * CH;
+    uint32_t local = 0;
+    for (int c = 0; c < chunks; ++c) {
+        unsigned long long v[WPT];
+        sk_words<WPT>(bm, words, base + (int64_t)c * CH + tid * WPT, v);
+#pragma unroll
+        for (int e = 0; e < WPT; ++e) local += (uint32_t)__popcll(v[e]);
+    }
+    uint32_t tile_total;
+    const uint32_t incl = block_incl_scan256(local, s_red, &tile_total);
+    if (tid == 0)
+        __hip_atomic_store(look + t, (t == 0 ? LB_INCL : LB_AGG) | tile_total, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 64) {
+        uint32_t excl = 0;
+        int64_t j = t - 1;  // newest predecessor not yet added
+        while (j >= 0) {
+            const int64_t idx = j - lane;
+            unsigned long long v = LB_INCL;  // before tile 0: an inclusive prefix of 0
+            if (idx >= 0) {
+                v = __hip_atomic_load(look + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                while (!(v & (LB_AGG | LB_INCL))) {
+                    __builtin_amdgcn_s_sleep(1);
+                    v = __hip_atomic_load(look + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            const uint64_t inc = __ballot((v & LB_INCL) != 0);
+            const int stop = inc ? __ffsll((unsigned long long)inc) - 1 : 63;  // first inclusive lane
+            uint32_t add = lane <= stop ? (uint32_t)(v & LB_VAL) : 0u;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) add += __shfl_xor(add, off, 64);
+            excl += add;
+            if (inc) break;
+            j -= 64;
+        }
+        if (lane == 0) {
+            if (t > 0)
+                __hip_atomic_store(look + t, LB_INCL | (excl + tile_total), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            s_excl = excl;
+            if (t == (int64_t)gridDim.x - 1) st->count = (unsigned long long)(excl + tile_total);
+        }
+    }
+    __syncthreads();
+    uint32_t run = s_excl + incl - local;
+    for (int c = 0; c < chunks; ++c) {
+        const int64_t cw0 = base + (int64_t)c * CH;
+        const int64_t w0 = cw0 + tid * WPT;
+        unsigned long long v[WPT];
+        sk_words<WPT>(bm, words, w0, v);
+        uint32_t pre[WPT];
+#pragma unroll
+        for (int e = 0; e < WPT; ++e) {
+            pre[e] = run;
+            run += (uint32_t)__popcll(v[e]);
+        }
+        if (w0 + WPT <= words) {
+            if constexpr (WPT % 4 == 0) {
+                uint4 *dst = (uint4 *)(prefix + w0);
+#pragma unroll
+                for (int h = 0; h < WPT / 4; ++h) dst[h] = make_uint4(pre[4 * h], pre[4 * h + 1], pre[4 * h + 2], pre[4 * h + 3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < WPT; ++e) prefix[w0 + e] = pre[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < WPT; ++e)
+                if (w0 + e < words) prefix[w0 + e] = pre[e];
+        }
+    }
+}
+
+// Rank: input row i with key k sits at sorted position prefix[k / 64] + (set bits of
+// its word below k), one radix pass whose digit is the whole key: perm[s] = i and
+// sk[s] = k.
 template <typename K>
-__global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys, int64_t n,
+__global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys_in, int64_t n,
                                               const unsigned long long *__restrict__ bm,
-                                              const uint32_t *__restrict__ prefix,
-                                              const uint32_t *__restrict__ tsum,
-                                              K *__restrict__ sk, int32_t *__restrict__ perm)
+                                              const uint32_t *__restrict__ prefix, K *__restrict__ sk,
+                                              int32_t *__restrict__ perm)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
-    const K key = keys[i];
-    if (key == (K)~K(0)) return;  // out-of-range row (the build reports it)
-    const unsigned long long word = bm[key >> 6];
+    const K key = keys_in[i];
+    if (key == (K)~K(0)) return;  // an invalid row (reported by the build) has no position
     const uint64_t w = (uint64_t)(key >> 6);
-    const int64_t r = (int64_t)prefix[w] + tsum[w / SCAN_TILE_ITEMS] +
-                      __popcll(word & ((1ull << (uint32_t)(key & 63)) - 1ull));
-    if (r < n) {
+    const uint32_t r = prefix[w] + (uint32_t)__popcll(bm[w] & ((1ull << (uint32_t)(key & 63)) - 1ull));
+    if (r < (uint64_t)n) {
         sk[r] = key;
         perm[r] = (int32_t)i;
     }
 }
 
+// Resolve and staging plan: each block resolves RR_T sorted positions (two plan
+// tiles).  For each (dz, dy) row d the voxel's neighbours at x - 1, x, x + 1 are three
+// consecutive bits of the occupancy bitmap, read as one funnel shift of two 32-bit
+// halves, and the first of them has the rank prefix + (set bits before it); the
+// present cells of a row take consecutive positions from there.  The rows are written
+// as coalesced runs through LDS; the group windows (per 32 voxels and row d: first and
+// last position of the neighbours) stay in LDS and give the plans of the block's two
+// tiles (plan_tile_team).  The block's present count goes to blk_taps, summed on the
+// host with the status.  Positions at or past st->count (the distinct keys; fewer than
+// n only for an invalid set, which the build reports) are not resolved.
+constexpr int RR_T = 256;  // sorted voxels per resolve block
+static_assert(RR_T == 2 * WIN_TILE, "a resolve block plans two tiles");
+
 template <typename K>
-__global__ __launch_bounds__(256) void k_resolve_bm(const K *__restrict__ sk, int64_t n, int res, int rb,
-                                                    int batch, const unsigned long long *__restrict__ bm,
-                                                    const uint32_t *__restrict__ prefix,
-                                                    const uint32_t *__restrict__ tsum,
-                                                    int32_t *__restrict__ nbr_sp,
-                                                    int32_t *__restrict__ gwin,
-                                                    uint32_t *__restrict__ blk_taps)
+__global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, int64_t n, int res, int rb,
+                                                      const unsigned long long *__restrict__ bm,
+                                                      const uint32_t *__restrict__ prefix,
+                                                      int32_t *__restrict__ nbr_sp, int32_t *__restrict__ plan,
+                                                      int64_t ntiles, const DevStatus *st,
+                                                      uint32_t *__restrict__ blk_taps)
 {
-    __shared__ int32_t s_rows[256 * NBR_INTS];
-    __shared__ uint32_t s_taps;
-    const int tid = threadIdx.x;
-    const int64_t s0 = (int64_t)blockIdx.x * 256;
-    const int count = (int)((n - s0) < 256 ? (n - s0) : 256);
-    if (tid == 0) s_taps = 0;
-    __syncthreads();
-    // the packed row (first position per (dz, dy) row, presence bits), built
-    // straight from each row's three occupancy bits and the rank of its first cell
-    int32_t r[NBR_INTS];
+    __shared__ __attribute__((aligned(16))) int32_t s_rows[RR_T * NBR_INTS];
+    __shared__ int32_t s_win[8 * GWIN_INTS];
+    __shared__ __attribute__((aligned(16))) int32_t s_rec[2 * PLAN_INTS];
+    __shared__ uint32_t s_wt[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t blk = blockIdx.x;
+    const int64_t s0 = blk * RR_T;
+    const int count = (int)((n - s0) < RR_T ? (n - s0) : RR_T);
+    const int64_t limit = (int64_t)st->count < n ? (int64_t)st->count : n;
+    const int64_t s = s0 + tid;
+    const bool valid = s < limit;
+    const K key = valid ? sk[s] : K(0);
+    const K m = (K(1) << rb) - 1;
+    const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
+    const bool xlo = x > 0, xhi = x + 1 < res;
+    const K base = key - (xlo ? K(1) : K(0));  // each row's window starts at cell x - 1 (x when x = 0)
+    const uint32_t shift = xlo ? 0u : 1u;      // window bit j <-> cell x - 1 + j
+    const uint32_t valid3 = (xlo ? 1u : 0u) | 2u | (xhi ? 4u : 0u);
+    const bool zok[3] = {z > 0, true, z + 1 < res}, yok[3] = {y > 0, true, y + 1 < res};
+    const uint32_t *bm32 = (const uint32_t *)bm;
+    // every load first (rows off the grid read word 0 and are masked): one round trip
+    unsigned long long wv[9];
+    uint32_t nx[9], pre[9], bsh[9];
+    bool rok[9];
 #pragma unroll
-    for (int q = 0; q < NBR_INTS; ++q) r[q] = 0;
-    uint32_t present = 0;
-    K key = K(0);
-    if (tid < count) key = sk[s0 + tid];
-    // positions past the last distinct key are never written when the set holds
-    // a duplicate or an invalid row (the build then reports an error): skip them
-    const bool valid = tid < count && key_valid(key, rb, res, batch);
-    if (valid) {
-        const uint32_t s = (uint32_t)(s0 + tid), un = (uint32_t)n;  // positions fit in 31 bits
-        const K m = (K(1) << rb) - 1;
-        const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
-        const K bpart = (key >> (3 * rb)) << (3 * rb);
-        const int xs = x > 0 ? x - 1 : 0;                      // first cell of each row window
-        const uint32_t valid3 = (x > 0 ? 1u : 0u) | 2u | (x + 1 < res ? 4u : 0u);  // cells x-1, x, x+1 on the grid
-        const uint32_t shift = x > 0 ? 0u : 1u;                // window bit j <-> cell x-1+j
-        // Each row (dz, dy): the occupancy of cells x-1 .. x+1 (3 bits, from one or
-        // two words) and the rank of the row's first cell; the present cells take
-        // consecutive positions from there.  All loads are issued without branching
-        // (rows off the grid read word 0 and are masked), so the whole neighbourhood
-        // costs one memory round trip.
-        K wd[9];
-        uint32_t bsh[9];
-        bool rok[9];
-#pragma unroll
-        for (int d = 0; d < 9; ++d) {
-            const int nz = z + d / 3 - 1, ny = y + d % 3 - 1;
-            rok[d] = nz >= 0 && nz < res && ny >= 0 && ny < res;
-            const K c0 = rok[d] ? (K)(bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)xs) : K(0);
-            wd[d] = c0 >> 6;
-            bsh[d] = (uint32_t)(c0 & 63);
-        }
-        // Of the next word only the low two bits can fall in the window: load its low
-        // half only (the bitmap has one word of padding).  A 64-bit load whose upper
-        // half is dead lets the compiler reuse that register at once, which makes it
-        // wait for the load there and serialises the round trips.
-        unsigned long long lo_w[9];
-        uint32_t hi_w[9], pre[9];
-        const uint32_t *bm32 = (const uint32_t *)bm;
-#pragma unroll
-        for (int d = 0; d < 9; ++d) {
-            lo_w[d] = bm[wd[d]];
-            hi_w[d] = bm32[2 * wd[d] + 2];
-            pre[d] = prefix[wd[d]] + tsum[wd[d] / SCAN_TILE_ITEMS];
-        }
-        uint32_t mask = 0;
-#pragma unroll
-        for (int d = 0; d < 9; ++d) {
-            const uint32_t b = bsh[d];
-            unsigned long long v = lo_w[d] >> b;
-            if (b > 61) v |= (unsigned long long)hi_w[d] << (64 - b);
-            uint32_t bits = rok[d] ? (((uint32_t)(v & 7ull) << shift) & valid3) : 0u;
-            // keys below the row window's first cell (the centre row: the voxel is at s)
-            const uint32_t q = (d == 4) ? s - (bits & 1u)
-                                        : pre[d] + (uint32_t)__popcll(lo_w[d] & ((1ull << b) - 1ull));
-            // a cell whose position would be n or more (a set with duplicates or
-            // invalid rows, which the build reports) is dropped
-            if (q + (uint32_t)__popc(bits) > un) {
-                uint32_t keep = q < un ? un - q : 0u, kept = 0;
-#pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    if (((bits >> j) & 1u) && keep) { kept |= 1u << j; --keep; }
-                bits = kept;
-            }
-            r[d] = bits ? (int32_t)q : 0;
-            mask |= bits << (3 * d);
-        }
-        r[9] = (int32_t)mask;
-        present = (uint32_t)__popc(mask);
+    for (int d = 0; d < 9; ++d) {
+        const int dz = d / 3 - 1, dy = d % 3 - 1;
+        rok[d] = valid && zok[dz + 1] && yok[dy + 1];
+        const K off = (K)((int64_t)dz << (2 * rb)) + (K)((int64_t)dy << rb);  // wraps correctly for dz, dy < 0
+        const K c0 = rok[d] ? (K)(base + off) : K(0);
+        const uint64_t w = (uint64_t)(c0 >> 6);
+        bsh[d] = (uint32_t)(c0 & 63);
+        wv[d] = bm[w];
+        nx[d] = bm32[2 * w + 2];  // low half of the next word (the bitmap has one word of padding)
+        pre[d] = d == 4 ? 0u : prefix[w];
     }
+    int32_t r[NBR_INTS];
+    uint32_t mask = 0;
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+        const uint32_t b = bsh[d], lo32 = (uint32_t)wv[d], hi32 = (uint32_t)(wv[d] >> 32);
+        const bool up = b >= 32;
+        const uint32_t cur = up ? hi32 : lo32, nxt = up ? nx[d] : hi32, below = up ? lo32 : 0u;
+        const uint32_t sh = b & 31u;
+        uint32_t bits = __builtin_amdgcn_alignbit(nxt, cur, sh) & 7u;
+        bits = rok[d] ? ((bits << shift) & valid3) : 0u;
+        // the centre row's window starts at the voxel itself or the one before it
+        r[d] = d == 4 ? (int32_t)((uint32_t)s - (bits & 1u))
+                      : (int32_t)(pre[d] + (uint32_t)__popc(below) + (uint32_t)__popc(cur & ((1u << sh) - 1u)));
+        mask |= bits << (3 * d);
+    }
+    r[9] = (int32_t)mask;
     if (tid < count) {
 #pragma unroll
         for (int q = 0; q < NBR_INTS; ++q) s_rows[tid * NBR_INTS + q] = r[q];
     }
-    if (present) atomicAdd(&s_taps, present);
-    group_windows_write_row(r, valid, (s0 + tid) >> 5, (n + 31) >> 5, gwin);
-    block_finish(s_rows, count, nbr_sp + s0 * NBR_INTS, &s_taps, blk_taps);
+    // group windows of the block's 8 groups of 32 (lanes 0-31 and 32-63 of each wave)
+    {
+        const int half = lane >> 5, g = tid >> 5;
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const uint32_t bits = (mask >> (3 * d)) & 7u;
+            const uint64_t bal = __ballot(bits != 0u);
+            const uint32_t mm = (uint32_t)(bal >> (32 * half));
+            const int first = mm ? __ffs((int)mm) - 1 : 0;
+            const int last = mm ? 31 - __clz((int)mm) : 0;
+            if ((lane & 31) == first) s_win[g * GWIN_INTS + d] = mm ? r[d] : GWIN_NONE;
+            if ((lane & 31) == last) s_win[g * GWIN_INTS + 9 + d] = mm ? r[d] + (int32_t)__popc(bits) - 1 : -1;
+        }
+    }
+    uint32_t present = (uint32_t)__popc(mask);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) present += __shfl_xor(present, off, 64);
+    if (lane == 0) s_wt[tid >> 6] = present;
+    __syncthreads();
+    // rows out as one contiguous run (the block's rows start 16-byte aligned)
+    {
+        const int ints = count * NBR_INTS, v4 = ints >> 2;
+        int4 *dst = (int4 *)(nbr_sp + s0 * NBR_INTS);
+        const int4 *src = (const int4 *)s_rows;
+        for (int e = tid; e < v4; e += 256) dst[e] = src[e];
+        for (int e = 4 * v4 + tid; e < ints; e += 256) nbr_sp[s0 * NBR_INTS + e] = s_rows[e];
+    }
+    if (tid == 0) blk_taps[blk] = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
+    // the two tiles' staging plans (wave 0: a team of 16 lanes per tile)
+    if (tid < 64) {
+        const int team = (tid >> 4) & 1, q = tid & 15;
+        int32_t lo = GWIN_NONE, hi = -1;
+        if (q < 9) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int32_t wl = s_win[(4 * team + g) * GWIN_INTS + q], wh = s_win[(4 * team + g) * GWIN_INTS + 9 + q];
+                if (wh >= 0) {
+                    lo = min(lo, wl);
+                    hi = max(hi, wh);
+                }
+            }
+        }
+        if (tid < 32) plan_tile_team(lo, hi, q, WIN_CAP, s_rec + team * PLAN_INTS);
+    }
+    __syncthreads();
+    if (tid < 2 * PLAN_INTS) {
+        const int64_t tile = 2 * blk + (tid >> 5);
+        if (tile < ntiles) plan[tile * PLAN_INTS + (tid & 31)] = s_rec[tid];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -449,19 +598,64 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
 // small sets: one block
 // ---------------------------------------------------------------------------
 
+// End of a single-block build (every thread calls it, rows of all n sorted voxels in
+// s_rows): the rows go out as one run, the group windows are formed per 32 sorted
+// voxels in LDS, each tile's staging plan is computed by a team of 16 lanes, and the
+// status block is written whole (no clearing launch is needed for these builds).
+__device__ void small_finish(const int32_t *s_rows, int n, int32_t *__restrict__ nbr_sp,
+                             int32_t *__restrict__ plan, int32_t *s_gwin, int32_t *s_rec, uint32_t flags,
+                             uint32_t taps, DevStatus *st)
+{
+    const int tid = threadIdx.x;
+    for (int e = tid; e < n * NBR_INTS; e += 1024) nbr_sp[e] = s_rows[e];
+    const int ngroups = (n + 31) >> 5;
+    for (int h = 0; h < SMALL_N / 1024; ++h) {
+        const int s = tid + 1024 * h;
+        int32_t r[NBR_INTS];
+#pragma unroll
+        for (int q = 0; q < NBR_INTS; ++q) r[q] = s < n ? s_rows[s * NBR_INTS + q] : 0;
+        group_windows_write_row(r, s < n, s >> 5, ngroups, s_gwin);
+    }
+    __syncthreads();
+    const int ntiles = (n + WIN_TILE - 1) / WIN_TILE, team = tid >> 4, q = tid & 15;
+    int32_t lo = GWIN_NONE, hi = -1;
+    if (team < ntiles && q < 9) {
+        for (int g = 4 * team; g < 4 * team + 4 && g < ngroups; ++g) {
+            const int32_t wl = s_gwin[g * GWIN_INTS + q], wh = s_gwin[g * GWIN_INTS + 9 + q];
+            if (wh >= 0) {
+                lo = min(lo, wl);
+                hi = max(hi, wh);
+            }
+        }
+    }
+    if (team < SMALL_N / WIN_TILE) plan_tile_team(lo, hi, q, WIN_CAP, s_rec + team * PLAN_INTS);
+    __syncthreads();
+    for (int e = tid; e < ntiles * PLAN_INTS; e += 1024) plan[e] = s_rec[e];
+    if (tid == 0) {
+        DevStatus v{};
+        v.flags = flags;
+        v.taps = taps;
+        *st = v;
+    }
+}
+
 // Key space of at most 2^16 bits: bitmap and prefix in LDS.
 template <typename K>
 __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict__ coords, int n,
                                                          int res, int batch, int rb, int nbits,
                                                          K *__restrict__ keys_out,
                                                          int32_t *__restrict__ perm_out,
-                                                         int32_t *__restrict__ nbr_sp, DevStatus *st)
+                                                         int32_t *__restrict__ nbr_sp, int32_t *__restrict__ plan,
+                                                         DevStatus *st)
 {
     constexpr int WORDS = (1 << SMALL_BITS) / 32;
     __shared__ uint32_t s_bm[WORDS];
     __shared__ uint32_t s_pre[WORDS];
     __shared__ uint32_t s_wave[16];
     __shared__ uint32_t s_flags, s_taps;
+    __shared__ int32_t s_rows[SMALL_N * NBR_INTS];
+    __shared__ int32_t s_gwin[SMALL_N / 32 * GWIN_INTS];
+    __shared__ int32_t s_rec[SMALL_N / 16 * PLAN_INTS];
     const int tid = threadIdx.x;
     const int words = nbits > 5 ? (1 << (nbits - 5)) : 1;
     for (int w = tid; w < words; w += 1024) s_bm[w] = 0;
@@ -508,7 +702,11 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
     }
     __syncthreads();
     if (s_flags) {  // invalid set: report only
-        if (tid == 0) atomicOr(&st->flags, s_flags);
+        if (tid == 0) {
+            DevStatus v{};
+            v.flags = s_flags;
+            *st = v;
+        }
         return;
     }
     const K m = (K(1) << rb) - 1;
@@ -537,11 +735,11 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
         int32_t rr[NBR_INTS];
         nbr_pack(p, rr);
 #pragma unroll
-        for (int q = 0; q < NBR_INTS; ++q) nbr_sp[(int64_t)s * NBR_INTS + q] = rr[q];
+        for (int q = 0; q < NBR_INTS; ++q) s_rows[s * NBR_INTS + q] = rr[q];
     }
     if (present) atomicAdd(&s_taps, present);
     __syncthreads();
-    if (tid == 0 && s_taps) atomicAdd(&st->taps, (unsigned long long)s_taps);
+    small_finish(s_rows, n, nbr_sp, plan, s_gwin, s_rec, 0u, s_taps, st);
 }
 
 // Larger key space: bitonic sort of (key, row) in LDS, binary search in LDS.
@@ -550,11 +748,15 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
                                                       int res, int batch, int rb,
                                                       K *__restrict__ keys_out,
                                                       int32_t *__restrict__ perm_out,
-                                                      int32_t *__restrict__ nbr_sp, DevStatus *st)
+                                                      int32_t *__restrict__ nbr_sp, int32_t *__restrict__ plan,
+                                                      DevStatus *st)
 {
     __shared__ K s_key[SMALL_N];
     __shared__ int32_t s_row[SMALL_N];
-    __shared__ uint32_t s_red[1];
+    __shared__ uint32_t s_red[2];
+    __shared__ int32_t s_rows[SMALL_N * NBR_INTS];
+    __shared__ int32_t s_gwin[SMALL_N / 32 * GWIN_INTS];
+    __shared__ int32_t s_rec[SMALL_N / 16 * PLAN_INTS];
     const int tid = threadIdx.x;
     int np = 1;
     while (np < n) np <<= 1;
@@ -572,9 +774,9 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
             s_row[i] = 0x7fffffff;
         }
     }
-    if (tid == 0) s_red[0] = 0;
-    if (bad_any) atomicOr(&st->flags, FLAG_RANGE);
+    if (tid == 0) s_red[0] = s_red[1] = 0;
     __syncthreads();
+    if (bad_any) atomicOr(&s_red[1], FLAG_RANGE);
     // bitonic sort of (key, row) pairs, ordered by key then row, so that padding
     // (all-ones key, largest row) lands behind every real entry even when a real
     // key is all ones
@@ -604,7 +806,7 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
         const K key = s_key[s];
         keys_out[s] = key;
         perm_out[s] = s_row[s];
-        if (s + 1 < n && s_key[s + 1] == key) atomicOr(&st->flags, FLAG_DUPLICATE);
+        if (s + 1 < n && s_key[s + 1] == key) atomicOr(&s_red[1], FLAG_DUPLICATE);
         const int x = (int)(key & m), y = (int)((key >> rb) & m), z = (int)((key >> (2 * rb)) & m);
         const K bpart = (key >> (3 * rb)) << (3 * rb);
         int32_t p[27];
@@ -623,11 +825,11 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
         int32_t rr[NBR_INTS];
         nbr_pack(p, rr);
 #pragma unroll
-        for (int q = 0; q < NBR_INTS; ++q) nbr_sp[(int64_t)s * NBR_INTS + q] = rr[q];
+        for (int q = 0; q < NBR_INTS; ++q) s_rows[s * NBR_INTS + q] = rr[q];
     }
     if (present) atomicAdd(&s_red[0], present);
     __syncthreads();
-    if (tid == 0 && s_red[0]) atomicAdd(&st->taps, (unsigned long long)s_red[0]);
+    small_finish(s_rows, n, nbr_sp, plan, s_gwin, s_rec, s_red[1], s_red[0], st);
 }
 
 // Group windows from a finished table (used after the single-block builds).
@@ -678,8 +880,10 @@ int input_order_table(const submconv_rulebook *rb, int32_t *out, hipStream_t s)
 int win_plan_build(submconv_rulebook *rb, const uint32_t *blk_taps, int64_t nblk, DevStatus *st,
                    hipStream_t s);  // conv_win.hip
 
-// Zero the status block and `words` 64-bit words (the bitmap); grid-stride.
-__global__ __launch_bounds__(256) void k_clear(DevStatus *st, unsigned long long *__restrict__ w, int64_t words)
+// Zero the status block, `words` 64-bit words at w (the bitmap) and `words2` at w2
+// (the scan's look-back flags); grid-stride.
+__global__ __launch_bounds__(256) void k_clear(DevStatus *st, unsigned long long *__restrict__ w, int64_t words,
+                                               unsigned long long *__restrict__ w2, int64_t words2)
 {
     if (blockIdx.x == 0 && threadIdx.x == 0) *st = DevStatus{};
     // pairs of words as 16-byte stores (w is 16-byte aligned), then an odd last word
@@ -687,6 +891,7 @@ __global__ __launch_bounds__(256) void k_clear(DevStatus *st, unsigned long long
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pairs; i += (int64_t)gridDim.x * 256)
         ((ulonglong2 *)w)[i] = make_ulonglong2(0ull, 0ull);
     if ((words & 1) && blockIdx.x == 0 && threadIdx.x == 0) w[words - 1] = 0ull;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words2; i += (int64_t)gridDim.x * 256) w2[i] = 0ull;
 }
 
 static bool use_bitmap(int64_t n, int nbits)
@@ -705,56 +910,71 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     const int path = n <= SMALL_N ? (rb->nbits <= SMALL_BITS ? 0 : 1) : (use_bitmap(n, rb->nbits) ? 2 : 3);
     auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
     const int64_t words = rb->nbits > 6 ? (int64_t(1) << (rb->nbits - 6)) : 1;  // 64-bit bitmap words
-    size_t off = 0, o_keys = 0, o_vals = 0, o_bm = 0, o_pre = 0, o_aux = 0;
-    const size_t o_cnt = off;  // present count per block of 256 voxels
-    off += up((size_t)grid_blocks(n) * 4);
+    const int64_t ntiles = (n + WIN_TILE - 1) / WIN_TILE;
+    // dense path: scan tiles of `chunks` x 256 x wpt words, at most SK_MAX_TILES of them (2 words per
+    // thread while that keeps enough tiles busy, else 8)
+    const int wpt = words <= (int64_t)512 * SK_MAX_TILES ? 2 : 8;
+    const int64_t chw = (int64_t)256 * wpt;
+    const int chunks = (int)((words + chw * SK_MAX_TILES - 1) / (chw * SK_MAX_TILES));
+    const int64_t stiles = (words + (int64_t)chunks * chw - 1) / ((int64_t)chunks * chw);
+    const int64_t rblocks = (n + RR_T - 1) / RR_T;  // resolve blocks of the dense path
+    // the status block first, then the per-block present counts: one read-back copies both
+    size_t off = up(sizeof(DevStatus) + (size_t)(path == 2 ? rblocks : grid_blocks(n)) * 4);
+    size_t o_keys = 0, o_vals = 0, o_bm = 0, o_pre = 0, o_aux = 0;
     if (path == 2) {
         o_keys = off; off += up((size_t)n * sizeof(K));
         o_bm = off; off += up((size_t)(words + 1) * 8);  // +1: a 3-cell window may touch the next word
         o_pre = off; off += up((size_t)words * 4);
-        o_aux = off; off += up(scan_scratch_bytes(words));
+        o_aux = off; off += up((size_t)stiles * 8);      // look-back flags of the scan
     } else if (path == 3) {
         o_keys = off; off += up((size_t)n * sizeof(K));
         o_vals = off; off += up((size_t)n * 4);
         o_aux = off; off += up(sort_scratch_bytes(n));
     }
-    const size_t o_stat = off;
-    off += sizeof(DevStatus);
     char *scratch = nullptr;
     SC_CHECK(dev_alloc((void **)&scratch, off, stream));
-    DevStatus *st = (DevStatus *)(scratch + o_stat);
-    uint32_t *blk_taps = (uint32_t *)(scratch + o_cnt);
+    DevStatus *st = (DevStatus *)scratch;
+    uint32_t *blk_taps = (uint32_t *)(scratch + sizeof(DevStatus));
     int status = SUBMCONV_OK;
     bool synced = false;  // the status read has synchronised the stream
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
-        // one launch clears the status block and (dense path) the bitmap
+        // one launch clears the status block and (dense path) the bitmap and the scan's flags;
+        // the single-block builds write their status block whole
         const int64_t clear_words = path == 2 ? words + 1 : 0;
-        hipLaunchKernelGGL(k_clear, dim3((unsigned)(clear_words > 0 ? (clear_words + 4095) / 4096 : 1)), dim3(256), 0,
-                           stream, st, (unsigned long long *)(scratch + o_bm), clear_words);
+        if (path >= 2)
+            hipLaunchKernelGGL(k_clear, dim3((unsigned)(clear_words > 0 ? (clear_words + 4095) / 4096 : 1)), dim3(256),
+                               0, stream, st, (unsigned long long *)(scratch + o_bm), clear_words,
+                               (unsigned long long *)(scratch + o_aux), path == 2 ? stiles : int64_t(0));
         if (path == 0 || path == 1) {
             if (path == 0)
                 hipLaunchKernelGGL(k_build_small_bm<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
-                                   (int)n, rb->res, rb->batch, rb->rb, rb->nbits, (K *)rb->keys, rb->perm, rb->nbr_sp, st);
+                                   (int)n, rb->res, rb->batch, rb->rb, rb->nbits, (K *)rb->keys, rb->perm, rb->nbr_sp,
+                                   rb->plan, st);
             else
                 hipLaunchKernelGGL(k_build_small<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
-                                   (int)n, rb->res, rb->batch, rb->rb, (K *)rb->keys, rb->perm, rb->nbr_sp, st);
-            hipLaunchKernelGGL(k_group_windows, dim3(grid), dim3(256), 0, stream, rb->nbr_sp, n, rb->gwin);
+                                   (int)n, rb->res, rb->batch, rb->rb, (K *)rb->keys, rb->perm, rb->nbr_sp, rb->plan,
+                                   st);
         } else if (path == 2) {
             K *tmp = (K *)(scratch + o_keys);
             unsigned long long *bm = (unsigned long long *)(scratch + o_bm);
             uint32_t *pre = (uint32_t *)(scratch + o_pre);
             hipLaunchKernelGGL(k_mark<K>, dim3((unsigned)((n + 256 * MARK_ROWS - 1) / (256 * MARK_ROWS))), dim3(256),
                                0, stream, (const int4 *)coords, n, rb->res, rb->batch, rb->rb, tmp, bm, st);
-            // the total number of set bits lands in st->count: below n means a duplicate.  The
-            // scan leaves per-tile prefixes; rank and resolve add the tile offsets (tsum).
-            if ((status = exclusive_scan_u32((const uint32_t *)bm, pre, words, (uint32_t *)&st->count,
-                                             scratch + o_aux, stream, SCAN_POPC64, false)) != SUBMCONV_OK) break;
-            const uint32_t *tsum = (const uint32_t *)(scratch + o_aux);
-            hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n, bm, pre, tsum,
-                               (K *)rb->keys, rb->perm);
-            hipLaunchKernelGGL(k_resolve_bm<K>, dim3(grid), dim3(256), 0, stream, (const K *)rb->keys, n,
-                               rb->res, rb->rb, rb->batch, bm, pre, tsum, rb->nbr_sp, rb->gwin, blk_taps);
+            // global prefixes of the words and the distinct count in st->count
+            if (wpt == 2)
+                hipLaunchKernelGGL(k_scan_words<2>, dim3((unsigned)stiles), dim3(256), 0, stream,
+                                   (const unsigned long long *)bm, words, chunks, pre,
+                                   (unsigned long long *)(scratch + o_aux), st);
+            else
+                hipLaunchKernelGGL(k_scan_words<8>, dim3((unsigned)stiles), dim3(256), 0, stream,
+                                   (const unsigned long long *)bm, words, chunks, pre,
+                                   (unsigned long long *)(scratch + o_aux), st);
+            hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n,
+                               (const unsigned long long *)bm, (const uint32_t *)pre, (K *)rb->keys, rb->perm);
+            hipLaunchKernelGGL(k_resolve_plan<K>, dim3((unsigned)rblocks), dim3(256), 0, stream, (const K *)rb->keys, n,
+                               rb->res, rb->rb, (const unsigned long long *)bm, (const uint32_t *)pre, rb->nbr_sp,
+                               rb->plan, ntiles, (const DevStatus *)st, blk_taps);
         } else {
             K *keys_b = (K *)(scratch + o_keys);
             int32_t *vals_b = (int32_t *)(scratch + o_vals);
@@ -768,16 +988,17 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
                                rb->res, rb->rb, rb->nbr_sp, rb->gwin, blk_taps, st);
         }
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "kernel launch in build_map failed"); break; }
-        // The staging plan is queued before the status read so it runs under the host
-        // round trip; it also sums the per-block tap counts of the large-set paths.
-        if ((status = win_plan_build(rb, path >= 2 ? blk_taps : nullptr, (int64_t)grid, st, stream)) != SUBMCONV_OK) break;
+        // The other paths plan from the group windows; the plan kernel also sums the sparse
+        // path's per-block present counts.
+        if (path == 3 && (status = win_plan_build(rb, blk_taps, (int64_t)grid, st, stream)) != SUBMCONV_OK) break;
         DevStatus h;
-        if ((status = read_status(st, &h, stream)) != SUBMCONV_OK) break;
+        uint64_t taps = 0;
+        if ((status = read_status_counts(st, path == 2 ? rblocks : 0, &h, &taps, stream)) != SUBMCONV_OK) break;
         synced = true;
-        if (path == 2 && !(h.flags & FLAG_RANGE) && (int64_t)(uint32_t)h.count != n) h.flags |= FLAG_DUPLICATE;
+        if (path == 2 && !(h.flags & FLAG_RANGE) && (int64_t)h.count != n) h.flags |= FLAG_DUPLICATE;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
-        rb->taps = (int64_t)h.taps;
+        rb->taps = (int64_t)(h.taps + taps);
     } while (0);
     if (synced) dev_free_idle(scratch, stream);
     else dev_free(scratch, stream);
