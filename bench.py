@@ -39,8 +39,14 @@ METRIC = "SubMConv3d fwd active-voxels/s + TFLOP/s at 128^3/128ch; map-build ms"
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_submconv3d_amd", "csrc")
-CONV_SRCS = [os.path.join(CSRC, f) for f in ("conv.hip", "conv_win.hip", "conv_big.hip")]
-MAP_SRCS = [os.path.join(CSRC, f) for f in ("mapbuild.hip", "sort_scan.hip", "conv_win.hip")]
+COMMON_SRCS = [os.path.join(CSRC, f) for f in ("common.h", "winplan.h")]
+
+
+def kernel_sources(kernel: str):
+    """The sources a forward kernel's code depends on (counter figures are valid while
+    their hash is unchanged)."""
+    f = "conv_win.hip" if "win32" in kernel else ("conv_big.hip" if "conv_big" in kernel else "conv.hip")
+    return [os.path.join(CSRC, f)] + COMMON_SRCS
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 BOUND = {1: "hbm", 2: "mfma", 3: "mfma", 4: "mfma", 5: "hbm"}
 
@@ -62,8 +68,8 @@ def load_traffic(workload: str, dtype: str, kernel: str, algorithmic_bytes: floa
     entry = data.get("%s/%s/%s" % (workload, dtype, kernel))
     if not entry:
         return None
-    srcs = CONV_SRCS if kernel == "forward" else MAP_SRCS
-    if entry.get("source_hash") != src_hash(srcs) or entry.get("algorithmic_bytes") != float(algorithmic_bytes):
+    if (entry.get("source_hash") != src_hash(kernel_sources(entry.get("kernel", "")))
+            or entry.get("algorithmic_bytes") != float(algorithmic_bytes)):
         return None
     return entry.get("bytes_per_launch")
 
@@ -711,7 +717,8 @@ def ingest_traffic(root):
         data = {}
     data["_note"] = ("HBM bytes per forward launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each "
                      "scaled by what the same counter reads for a 1 GiB device copy; keyed workload/dtype/kernel; "
-                     "valid while source_hash matches the forward sources (conv.hip + conv_win.hip + conv_big.hip).")
+                     "valid while source_hash matches the kernel's source file with common.h and winplan.h, and "
+                     "the workload's algorithmic bytes are unchanged.")
     data["calibration"] = {"copy_bytes": 1 << 30, "fetch_kib": cal["FETCH_SIZE"], "write_kib": cal["WRITE_SIZE"],
                            "fetch_scale": fscale, "write_scale": wscale}
     import synth
@@ -720,24 +727,26 @@ def ingest_traffic(root):
         if tag == "copy":
             continue
         wname, dt = tag.rsplit("_", 1)
-        fetch = per_dispatch(d, lambda k: k.startswith("sc::k_conv"))
-        write = per_dispatch(os.path.join(root, "pmc_%s_WRITE_SIZE" % tag), lambda k: k.startswith("sc::k_conv"))
+        fetch = per_dispatch(d, lambda k: "sc::k_conv" in k)
+        write = per_dispatch(os.path.join(root, "pmc_%s_WRITE_SIZE" % tag), lambda k: "sc::k_conv" in k)
         if not fetch:
             continue
-        kname = max(fetch, key=lambda k: fetch[k])           # the forward kernel of the run
+        kfull = max(fetch, key=lambda k: fetch[k])           # the forward kernel of the run
+        kname = kfull.split("(")[0].replace("void ", "")
         idx = [i for i, w in synth.WORKLOADS.items() if wname.startswith(w.name)][0]
         w, coords = synth.workload(idx)
         n = len(coords) * (8 if w.subdivide_parent else 1)
-        rb, wbytes = fetch[kname] * 1024 * fscale, write.get(kname, 0.0) * 1024 * wscale
+        rb, wbytes = fetch[kfull] * 1024 * fscale, write.get(kfull, 0.0) * 1024 * wscale
         s_el = 4 if dt == "f32" else 2
         data["%s/%s/forward" % (wname, dt)] = {
-            "kernel": kname, "fetch_kib_raw": fetch[kname], "write_kib_raw": write.get(kname, 0.0),
+            "kernel": kname, "fetch_kib_raw": fetch[kfull], "write_kib_raw": write.get(kfull, 0.0),
             "read_bytes": rb, "write_bytes": wbytes, "bytes_per_launch": rb + wbytes,
             "algorithmic_bytes": float(n * (w.cin * s_el + w.cout * s_el + 108) + 27 * w.cin * w.cout * s_el
                                        + 4 * w.cout),
-            "source_hash": src_hash(CONV_SRCS)}
+            "source_hash": src_hash(kernel_sources(kname))}
     json.dump(data, open(TRAFFIC_FILE, "w"), indent=1)
-    print(json.dumps({k: v.get("bytes_per_launch") for k, v in data.items() if isinstance(v, dict)}))
+    print(json.dumps({k: (v.get("bytes_per_launch"), v.get("algorithmic_bytes")) for k, v in data.items()
+                      if isinstance(v, dict) and "bytes_per_launch" in v}))
     return 0
 
 
