@@ -258,12 +258,15 @@ struct MfmaShape {
 };
 
 // Persistent: one block of 8 waves per CU (two per SIMD, so that one wave's
-// copy-issue and LDS stalls hide behind the other's MFMAs) takes a balanced
-// contiguous run of 32-voxel columns and walks it in rounds.  In a full round each
-// wave owns one column and all Cout; in the last, partial round the waves share the
-// remaining columns and split Cout so that no SIMD carries more than it must.  With
-// one block per CU, a grid of fixed-size blocks ran whole extra rounds on some CUs
-// while the rest idled.
+// copy-issue and LDS stalls hide behind the other's MFMAs) walks 32-voxel columns
+// in rounds: the blocks of an XCD take its eighth of the columns together, one
+// round of 8 columns each in turn, and then split the columns left over evenly.
+// In a full round each wave owns one column and all Cout; in the last, partial
+// round the waves share the remaining columns and split Cout so that no SIMD
+// carries more than it must.  With one block per CU, a grid of fixed-size blocks
+// ran whole extra rounds on some CUs while the rest idled; with each block on its
+// own contiguous run, an XCD's L2 saw 32 separate windows of rows and fetched each
+// row from memory about twice as often.
 constexpr int MFMA_P_WAVES = 8;
 
 template <typename T, int CIN, int COUT, int VT>
@@ -291,10 +294,32 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t ncols = (n + 31) / 32;
-    const int64_t blk = xcd_block();
-    const int64_t c0 = ncols * blk / gridDim.x, c1 = ncols * (blk + 1) / gridDim.x;
+    // Columns: with a grid of whole XCDs (workgroup id mod 8), each XCD takes a
+    // contiguous eighth of the columns and its blocks walk it together, full rounds
+    // dealt in turn (round rd of block j: columns xs + (rd * bpx + j) * WV ..), so the
+    // XCD's gathers stay within a narrow window of sorted voxels that its L2 holds;
+    // the columns left over are then split evenly among the XCD's blocks.  Otherwise
+    // each block takes one balanced contiguous run.
+    int64_t full_base = 0, full_step = 0, c0, c1;
+    int full;
+    if ((gridDim.x & 7) == 0) {
+        const int64_t xcd = blockIdx.x & 7, bpx = gridDim.x >> 3, jb = blockIdx.x >> 3;
+        const int64_t xs = ncols * xcd / 8, xe = ncols * (xcd + 1) / 8;
+        const int64_t nfull = (xe - xs) / (WV * bpx);
+        full = (int)nfull;
+        full_base = xs + jb * WV;
+        full_step = bpx * WV;
+        const int64_t rb0 = xs + nfull * WV * bpx, rt = xe - rb0;
+        c0 = rb0 + rt * jb / bpx;
+        c1 = rb0 + rt * (jb + 1) / bpx;
+    } else {
+        const int64_t blk = xcd_block();
+        c0 = ncols * blk / gridDim.x;
+        c1 = ncols * (blk + 1) / gridDim.x;
+        full = 0;
+    }
     const int m = (int)(c1 - c0);
-    if (m <= 0) return;
+    if (m <= 0 && full == 0) return;
 
     // copy weight fragment f of tap k (kernel tap k' = flip ? 26-k : k) into `dst`
     auto copy_w = [&](int k, uint4 *dst, int f) {
@@ -448,10 +473,14 @@ __global__ __launch_bounds__(64 * MFMA_P_WAVES) void k_conv_mfma(const T *__rest
     using Q = std::integral_constant<int, RT / 4>;
     using H = std::integral_constant<int, RT / 2>;
     using A = std::integral_constant<int, RT>;
-    const int full = m / WV, rem = m % WV;
-    for (int rd = 0; rd < full; ++rd)
+    for (int rd = 0; rd < full; ++rd) {
+        const int64_t cf = full_base + full_step * rd;
+        round(A{}, cf, cf + wave, 0, true);
+    }
+    const int mfull = m / WV, rem = m % WV;
+    for (int rd = 0; rd < mfull; ++rd)
         round(A{}, c0 + WV * rd, c0 + WV * rd + wave, 0, true);
-    const int64_t ct = c0 + WV * full;
+    const int64_t ct = c0 + WV * mfull;
     if (rem == 1)  // waves 0..3 (one per SIMD): a quarter of Cout each
         round(Q{}, ct, ct, (wave & 3) * (RT / 4), wave < 4);
     else if (rem == 2)  // 4 waves per column, a quarter each

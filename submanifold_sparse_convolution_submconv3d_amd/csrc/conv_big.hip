@@ -42,15 +42,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-#ifndef BIG_WAVES
-#define BIG_WAVES 8
-#endif
-#ifndef BIG_QUAD
-#define BIG_QUAD 1
-#endif
-#ifndef BIG_AHEAD
-#define BIG_AHEAD 2
-#endif
+constexpr int BIG_WAVES = 8;  // one block of 8 waves (two per SIMD) per CU
 
 template <int CIN, int COUT, int NW>
 struct BigShape {
@@ -64,7 +56,7 @@ struct BigShape {
     static constexpr int WCH = COUT * ROWCH;    // chunks per weight tap
     static constexpr int WCOPY = (WCH + 64 * WAVES - 1) / (64 * WAVES);
     static constexpr int WBUF = WCOPY * 64 * WAVES;  // chunks per buffer (copies past WCH land in padding)
-    static constexpr int AHEAD = BIG_AHEAD;        // weight fragments read ahead of their MFMAs
+    static constexpr int AHEAD = 2;                // weight fragments read ahead of their MFMAs
     static constexpr int TCH = ROUND * 16 * NBR_INTS / 4;  // table chunks of a full round
     static constexpr int TCOPY = (TCH + 64 * WAVES - 1) / (64 * WAVES);
     static_assert(CIN % 32 == 0 && COUT % 16 == 0 && 16 % RT == 0, "tile shape");
@@ -168,7 +160,7 @@ struct BigCtx {
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
             const int colr = cg * CW + c;
-            gvloc[c] = colr * 16 + (BIG_QUAD ? (lane >> 2) : s16);
+            gvloc[c] = colr * 16 + (lane >> 2);
             gvok[c] = colr < ncols && col * 16 + gvloc[c] < n;
             const int64_t ov = col * 16 + colr * 16 + s16;
             ovok[c] = colr < ncols && ov < n;
@@ -191,14 +183,13 @@ struct BigCtx {
         auto perm_of = [&](int32_t e) -> int32_t { return __builtin_amdgcn_raw_buffer_load_b32(rp, e * 4, 0, 0); };
         auto offset_of = [&](int32_t r, int32_t e) -> uint32_t {
             const uint32_t miss = (uint32_t)e < (uint64_t)n ? 0u : 0x80000000u;
-            return ((uint32_t)r * (CIN * 2) + 16 * (BIG_QUAD ? (lane & 3) : h)) | miss;
+            return ((uint32_t)r * (CIN * 2) + 16 * (lane & 3)) | miss;
         };
         auto fload = [&](uint32_t off, int g) -> uint4 {
             return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rf, off + 64 * g, 0, 0));
         };
         const int tsrc = 4 * (4 * s16 + h);  // operand lane l takes quad lane 4 (l % 16) + l / 16
         auto tr = [&](const uint4 v) -> uint4 {
-            if constexpr (!BIG_QUAD) return v;
             return uint4{(uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.x),
                          (uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.y),
                          (uint32_t)__builtin_amdgcn_ds_bpermute(tsrc, (int)v.z),
