@@ -32,7 +32,7 @@
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = null stream).  All
  * work is enqueued on it.  Only calls that must return a device-computed value
- * (build_map's validity status, output row counts) synchronise that stream.
+ * (build_map's validity status, output row counts) wait for that stream's work.
  *
  * Errors: every call returns a status (0 = success, < 0 = error); no call aborts
  * or throws.  Host-side argument checks run before any HIP call.
@@ -88,9 +88,13 @@ typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
  *   out_rb : receives the rulebook on success, NULL on failure.
  *
  * The table computed is nbr int32 [n,27]: nbr[i,k] = row of the voxel at
- * coords[i] + offset(k), or -1.  It is exact (integer work).  Synchronises
- * `stream` once to read the validity status: E_COORD_RANGE if a coordinate is
- * out of range, E_DUPLICATE if two rows are equal (no rulebook is returned).
+ * coords[i] + offset(k), or -1.  It is exact (integer work).  It waits for the
+ * build to finish to learn the validity status: E_COORD_RANGE if a coordinate is
+ * out of range, E_DUPLICATE if two rows are equal (no rulebook is returned).  On
+ * the bitmap path (grids of at most 2^31 keys) the build's last kernel writes the
+ * status to pinned host memory and the call polls it instead of synchronising the
+ * stream (for at most ~2 ms, then it synchronises); when it returns, the rulebook's
+ * contents are complete, though the stream may not yet be idle.
  * Device memory comes from the library's block cache (submconv_release_cache),
  * else from the device's stream-ordered pool.
  *

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <chrono>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -74,6 +75,60 @@ int read_status_counts(const DevStatus *d, int64_t ncounts, DevStatus *h, uint64
 int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
 {
     return read_status_counts(d, 0, h, nullptr, stream);
+}
+
+static thread_local Mailbox *g_mailbox = nullptr;      // host address
+static thread_local Mailbox *g_mailbox_dev = nullptr;  // its device address
+static thread_local uint32_t g_mailbox_seq = 0;
+
+int mailbox_acquire(Mailbox **mb, uint32_t *seq)
+{
+    if (!g_mailbox) {
+        // coherent: the device's stores reach host memory while the kernel runs; portable:
+        // usable from every device
+        Mailbox *h = nullptr;
+        SC_HIP(hipHostMalloc((void **)&h, sizeof(Mailbox),
+                             hipHostMallocCoherent | hipHostMallocMapped | hipHostMallocPortable));
+        __atomic_store_n(&h->seq, 0u, __ATOMIC_RELAXED);
+        void *dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, h, 0) != hipSuccess) {
+            (void)hipHostFree(h);
+            return fail(SUBMCONV_E_HIP, "hipHostGetDevicePointer failed for the status mailbox");
+        }
+        g_mailbox = h;
+        g_mailbox_dev = (Mailbox *)dp;
+    }
+    g_mailbox_seq = g_mailbox_seq + 1 ? g_mailbox_seq + 1 : 1;  // never 0, the initial value
+    *mb = g_mailbox_dev;
+    *seq = g_mailbox_seq;
+    return SUBMCONV_OK;
+}
+
+int mailbox_wait(Mailbox *mb_dev, uint32_t seq, DevStatus *h, hipStream_t stream)
+{
+    (void)mb_dev;
+    Mailbox *mb = g_mailbox;
+    // poll for up to ~2 ms (a build of a few million voxels takes well under that); past
+    // it, or if the post never comes (a failed launch), synchronise and check once more
+    const auto t0 = std::chrono::steady_clock::now();
+    bool seen = false;
+    for (uint32_t it = 0;; ++it) {
+        if (__atomic_load_n(&mb->seq, __ATOMIC_ACQUIRE) == seq) {
+            seen = true;
+            break;
+        }
+        if ((it & 255u) == 255u && std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(2000)) break;
+    }
+    if (!seen) {
+        SC_HIP(hipStreamSynchronize(stream));
+        if (__atomic_load_n(&mb->seq, __ATOMIC_ACQUIRE) != seq)
+            return fail(SUBMCONV_E_HIP, "the build's status was not posted");
+    }
+    *h = DevStatus{};
+    h->flags = mb->flags;
+    h->taps = mb->taps;
+    h->count = mb->count;
+    return SUBMCONV_OK;
 }
 
 // Device memory of the library (rulebooks and scratch) comes from a block cache.

@@ -59,6 +59,22 @@ int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream);
 // sum is returned in *sum.
 int read_status_counts(const DevStatus *d, int64_t ncounts, DevStatus *h, uint64_t *sum, hipStream_t stream);
 
+// A status block in coherent pinned host memory that a kernel writes itself, so the
+// host learns the result by polling `seq` instead of enqueueing a copy and
+// synchronising the stream.  One per host thread.
+struct Mailbox {
+    uint32_t seq;                // written last, to the value the host expects
+    uint32_t flags;
+    unsigned long long taps;
+    unsigned long long count;
+};
+// This thread's mailbox (device-visible) and the sequence number the next post must carry.
+int mailbox_acquire(Mailbox **mb, uint32_t *seq);
+// Wait until `mb` carries `seq` (polling, then a stream synchronisation as a fallback)
+// and return its fields in `h`.
+int mailbox_wait(Mailbox *mb, uint32_t seq, DevStatus *h, hipStream_t stream);
+
+
 // --------------------------------------------------------------------------
 // stream-ordered device memory
 // --------------------------------------------------------------------------

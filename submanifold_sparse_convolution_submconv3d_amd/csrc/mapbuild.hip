@@ -161,7 +161,7 @@ __device__ __forceinline__ void block_finish(const int32_t *s_rows, int count, i
 
 constexpr int MARK_ROWS = 4;        // rows per thread in k_mark
 constexpr int MARK_SLOTS = 2048;    // LDS hash slots per block (2 x the block's rows)
-constexpr unsigned long long MARK_EMPTY = ~0ull;
+constexpr uint32_t MARK_EMPTY = ~0u;  // word indices are below 2^25 (keys of at most 31 bits)
 
 // Validate and pack each row's key, and set its bit in the occupancy bitmap.  A
 // block first ORs its rows' bits into an LDS hash table keyed by bitmap word, so
@@ -173,11 +173,11 @@ __global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, i
                                               int batch, int rb, K *__restrict__ keys,
                                               unsigned long long *__restrict__ bm, DevStatus *st)
 {
-    __shared__ unsigned long long s_word[MARK_SLOTS], s_bits[MARK_SLOTS];
-    for (int i = threadIdx.x; i < MARK_SLOTS; i += 256) {
-        s_word[i] = MARK_EMPTY;
-        s_bits[i] = 0ull;
-    }
+    __shared__ __attribute__((aligned(16))) uint32_t s_word[MARK_SLOTS];
+    __shared__ __attribute__((aligned(16))) unsigned long long s_bits[MARK_SLOTS];
+    for (int i = threadIdx.x; i < MARK_SLOTS / 4; i += 256)
+        ((uint4 *)s_word)[i] = make_uint4(MARK_EMPTY, MARK_EMPTY, MARK_EMPTY, MARK_EMPTY);
+    for (int i = threadIdx.x; i < MARK_SLOTS / 2; i += 256) ((ulonglong2 *)s_bits)[i] = make_ulonglong2(0ull, 0ull);
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * (256 * MARK_ROWS) + threadIdx.x;
     bool bad_any = false;
@@ -199,11 +199,11 @@ __global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, i
         K key = (K)~K(0);  // marks an invalid row for the rank pass
         if (!bad) {
             key = pack_key<K>(c.x, c.y, c.z, c.w, rb);
-            const unsigned long long w = (unsigned long long)(key >> 6);
-            uint32_t h = ((uint32_t)w * 0x9E3779B1u) >> (32 - 11);
+            const uint32_t w = (uint32_t)(key >> 6);
+            uint32_t h = (w * 0x9E3779B1u) >> (32 - 11);
             // linear probing; the table has twice the block's rows, so it never fills
             for (;;) {
-                const unsigned long long prev = atomicCAS(&s_word[h], MARK_EMPTY, w);
+                const uint32_t prev = atomicCAS(&s_word[h], MARK_EMPTY, w);
                 if (prev == MARK_EMPTY || prev == w) break;
                 h = (h + 1) & (MARK_SLOTS - 1);
             }
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_mark(const int4 *__restrict__ coords, i
     if (bad_any) atomicOr(&st->flags, FLAG_RANGE);
     __syncthreads();
     for (int i = threadIdx.x; i < MARK_SLOTS; i += 256) {
-        const unsigned long long w = s_word[i];
+        const uint32_t w = s_word[i];
         if (w != MARK_EMPTY) atomicOr(&bm[w], s_bits[i]);
     }
 }
@@ -358,24 +358,24 @@ __global__ __launch_bounds__(256) void k_rank(const K *__restrict__ keys_in, int
 // consecutive bits of the occupancy bitmap, read as one funnel shift of two 32-bit
 // halves, and the first of them has the rank prefix + (set bits before it); the
 // present cells of a row take consecutive positions from there.  The rows are written
-// as coalesced runs through LDS; the group windows (per 32 voxels and row d: first and
-// last position of the neighbours) stay in LDS and give the plans of the block's two
-// tiles (plan_tile_team).  The block's present count goes to blk_taps, summed on the
-// host with the status.  Positions at or past st->count (the distinct keys; fewer than
-// n only for an invalid set, which the build reports) are not resolved.
+// as coalesced runs through LDS; the row windows of each wave (per 64 voxels and row d:
+// first and last position of the neighbours) stay in LDS and give the plans of the
+// block's two tiles (plan_tile_team).  The block's present count goes to blk_taps
+// (summed by k_post_status).  Positions at or past st->count (the distinct keys; fewer
+// than n only for an invalid set, which the build reports) are not resolved.
 constexpr int RR_T = 256;  // sorted voxels per resolve block
 static_assert(RR_T == 2 * WIN_TILE, "a resolve block plans two tiles");
 
-template <typename K>
+template <typename K, bool WORDROWS>
 __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, int64_t n, int res, int rb,
-                                                      const unsigned long long *__restrict__ bm,
-                                                      const uint32_t *__restrict__ prefix,
+                                                      const unsigned long long *__restrict__ bm, int bm_bytes,
+                                                      const uint32_t *__restrict__ prefix, int pre_bytes,
                                                       int32_t *__restrict__ nbr_sp, int32_t *__restrict__ plan,
                                                       int64_t ntiles, const DevStatus *st,
                                                       uint32_t *__restrict__ blk_taps)
 {
     __shared__ __attribute__((aligned(16))) int32_t s_rows[RR_T * NBR_INTS];
-    __shared__ int32_t s_win[8 * GWIN_INTS];
+    __shared__ int32_t s_win[4 * 18];
     __shared__ __attribute__((aligned(16))) int32_t s_rec[2 * PLAN_INTS];
     __shared__ uint32_t s_wt[4];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -393,55 +393,106 @@ __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, 
     const uint32_t shift = xlo ? 0u : 1u;      // window bit j <-> cell x - 1 + j
     const uint32_t valid3 = (xlo ? 1u : 0u) | 2u | (xhi ? 4u : 0u);
     const bool zok[3] = {z > 0, true, z + 1 < res}, yok[3] = {y > 0, true, y + 1 < res};
-    const uint32_t *bm32 = (const uint32_t *)bm;
-    // every load first (rows off the grid read word 0 and are masked): one round trip
-    unsigned long long wv[9];
-    uint32_t nx[9], pre[9], bsh[9];
-    bool rok[9];
-#pragma unroll
-    for (int d = 0; d < 9; ++d) {
-        const int dz = d / 3 - 1, dy = d % 3 - 1;
-        rok[d] = valid && zok[dz + 1] && yok[dy + 1];
-        const K off = (K)((int64_t)dz << (2 * rb)) + (K)((int64_t)dy << rb);  // wraps correctly for dz, dy < 0
-        const K c0 = rok[d] ? (K)(base + off) : K(0);
-        const uint64_t w = (uint64_t)(c0 >> 6);
-        bsh[d] = (uint32_t)(c0 & 63);
-        wv[d] = bm[w];
-        nx[d] = bm32[2 * w + 2];  // low half of the next word (the bitmap has one word of padding)
-        pre[d] = d == 4 ? 0u : prefix[w];
-    }
     int32_t r[NBR_INTS];
     uint32_t mask = 0;
-#pragma unroll
-    for (int d = 0; d < 9; ++d) {
-        const uint32_t b = bsh[d], lo32 = (uint32_t)wv[d], hi32 = (uint32_t)(wv[d] >> 32);
+    if constexpr (WORDROWS) {
+        // At least 6 bits per axis: every (dz, dy) row offset is a whole number of 64-bit
+        // words, so the nine windows share their bit position in the word, and their words
+        // are the centre word plus per-row constants.  Words and prefixes are read through
+        // bounds-checked buffers (a row off the grid may form an offset outside them, which
+        // reads zeros; its bits are masked either way).
+        const __amdgpu_buffer_rsrc_t rbm = __builtin_amdgcn_make_buffer_rsrc((void *)bm, (short)0, bm_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rpre = __builtin_amdgcn_make_buffer_rsrc((void *)prefix, (short)0, pre_bytes, 0x00020000);
+        const uint32_t wb = (uint32_t)((uint64_t)base >> 6), b = (uint32_t)(base & 63);
         const bool up = b >= 32;
-        const uint32_t cur = up ? hi32 : lo32, nxt = up ? nx[d] : hi32, below = up ? lo32 : 0u;
-        const uint32_t sh = b & 31u;
-        uint32_t bits = __builtin_amdgcn_alignbit(nxt, cur, sh) & 7u;
-        bits = rok[d] ? ((bits << shift) & valid3) : 0u;
-        // the centre row's window starts at the voxel itself or the one before it
-        r[d] = d == 4 ? (int32_t)((uint32_t)s - (bits & 1u))
-                      : (int32_t)(pre[d] + (uint32_t)__popc(below) + (uint32_t)__popc(cur & ((1u << sh) - 1u)));
-        mask |= bits << (3 * d);
+        const uint32_t sh = b & 31u, m = (1u << sh) - 1u;
+        const uint32_t mlo = up ? ~0u : m, mhi = up ? m : 0u;  // bits of the word before the window
+        const int32_t row_w = 1 << (rb - 6), plane_w = 1 << (2 * rb - 6);
+        uint32_t lo[9], hi[9], nx[9], pre[9];
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const int dz = d / 3 - 1, dy = d % 3 - 1;
+            const uint32_t w = wb + (uint32_t)(dz * plane_w + dy * row_w);
+            // the word and the low half of the next one (the bitmap has one word of padding)
+            const auto v = __builtin_amdgcn_raw_buffer_load_b96(rbm, w * 8u, 0, 0);
+            lo[d] = v[0];
+            hi[d] = v[1];
+            nx[d] = v[2];
+            pre[d] = d == 4 ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rpre, w * 4u, 0, 0);
+        }
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const int dz = d / 3 - 1, dy = d % 3 - 1;
+            // cells of the row on the grid (none for a row off it): a mask, not a branch
+            const uint32_t vm = (valid && zok[dz + 1] && yok[dy + 1]) ? valid3 : 0u;
+            const uint32_t cur = up ? hi[d] : lo[d], nxt = up ? nx[d] : hi[d];
+            const uint32_t bits = (__builtin_amdgcn_alignbit(nxt, cur, sh) << shift) & vm;
+            // the centre row's window starts at the voxel itself or the one before it
+            r[d] = d == 4 ? (int32_t)((uint32_t)s - (bits & 1u))
+                          : (int32_t)(pre[d] + (uint32_t)__popc(lo[d] & mlo) + (uint32_t)__popc(hi[d] & mhi));
+            mask |= bits << (3 * d);
+        }
+    } else {
+        const uint32_t *bm32 = (const uint32_t *)bm;
+        // every load first (rows off the grid read word 0 and are masked): one round trip
+        unsigned long long wv[9];
+        uint32_t nx[9], pre[9], bsh[9];
+        bool rok[9];
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const int dz = d / 3 - 1, dy = d % 3 - 1;
+            rok[d] = valid && zok[dz + 1] && yok[dy + 1];
+            const K off = (K)((int64_t)dz << (2 * rb)) + (K)((int64_t)dy << rb);  // wraps correctly for dz, dy < 0
+            const K c0 = rok[d] ? (K)(base + off) : K(0);
+            const uint64_t w = (uint64_t)(c0 >> 6);
+            bsh[d] = (uint32_t)(c0 & 63);
+            wv[d] = bm[w];
+            nx[d] = bm32[2 * w + 2];  // low half of the next word (the bitmap has one word of padding)
+            pre[d] = d == 4 ? 0u : prefix[w];
+        }
+#pragma unroll
+        for (int d = 0; d < 9; ++d) {
+            const uint32_t b = bsh[d], lo32 = (uint32_t)wv[d], hi32 = (uint32_t)(wv[d] >> 32);
+            const bool up = b >= 32;
+            const uint32_t cur = up ? hi32 : lo32, nxt = up ? nx[d] : hi32, below = up ? lo32 : 0u;
+            const uint32_t sh = b & 31u;
+            uint32_t bits = __builtin_amdgcn_alignbit(nxt, cur, sh) & 7u;
+            bits = rok[d] ? ((bits << shift) & valid3) : 0u;
+            r[d] = d == 4 ? (int32_t)((uint32_t)s - (bits & 1u))
+                          : (int32_t)(pre[d] + (uint32_t)__popc(below) + (uint32_t)__popc(cur & ((1u << sh) - 1u)));
+            mask |= bits << (3 * d);
+        }
     }
     r[9] = (int32_t)mask;
     if (tid < count) {
 #pragma unroll
         for (int q = 0; q < NBR_INTS; ++q) s_rows[tid * NBR_INTS + q] = r[q];
     }
-    // group windows of the block's 8 groups of 32 (lanes 0-31 and 32-63 of each wave)
+    // The window of each (dz, dy) row over the wave's 64 voxels: the row's first position
+    // in the first lane that has the row, its last in the last such lane (windows are
+    // monotone in sorted order, see group_windows_write).  Found with one ballot and
+    // scalar lane lookups per row; lane 0 stores the wave's 9 starts, then its 9 ends.
     {
-        const int half = lane >> 5, g = tid >> 5;
+        int32_t wlo[9], whi[9];
 #pragma unroll
         for (int d = 0; d < 9; ++d) {
             const uint32_t bits = (mask >> (3 * d)) & 7u;
             const uint64_t bal = __ballot(bits != 0u);
-            const uint32_t mm = (uint32_t)(bal >> (32 * half));
-            const int first = mm ? __ffs((int)mm) - 1 : 0;
-            const int last = mm ? 31 - __clz((int)mm) : 0;
-            if ((lane & 31) == first) s_win[g * GWIN_INTS + d] = mm ? r[d] : GWIN_NONE;
-            if ((lane & 31) == last) s_win[g * GWIN_INTS + 9 + d] = mm ? r[d] + (int32_t)__popc(bits) - 1 : -1;
+            wlo[d] = GWIN_NONE;
+            whi[d] = -1;
+            if (bal) {
+                const int f = __builtin_ctzll(bal), l = 63 - __builtin_clzll(bal);
+                wlo[d] = __builtin_amdgcn_readlane(r[d], f);
+                whi[d] = __builtin_amdgcn_readlane(r[d], l) +
+                         __popc((uint32_t)__builtin_amdgcn_readlane((int)bits, l)) - 1;
+            }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int d = 0; d < 9; ++d) {
+                s_win[(tid >> 6) * 18 + d] = wlo[d];
+                s_win[(tid >> 6) * 18 + 9 + d] = whi[d];
+            }
         }
     }
     uint32_t present = (uint32_t)__popc(mask);
@@ -457,19 +508,16 @@ __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, 
         for (int e = tid; e < v4; e += 256) dst[e] = src[e];
         for (int e = 4 * v4 + tid; e < ints; e += 256) nbr_sp[s0 * NBR_INTS + e] = s_rows[e];
     }
-    if (tid == 0) blk_taps[blk] = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
-    // the two tiles' staging plans (wave 0: a team of 16 lanes per tile)
+    // the two tiles' staging plans (wave 0: a team of 16 lanes per tile, the tile's two
+    // waves' windows joined; an empty window is (GWIN_NONE, -1))
     if (tid < 64) {
         const int team = (tid >> 4) & 1, q = tid & 15;
         int32_t lo = GWIN_NONE, hi = -1;
         if (q < 9) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int32_t wl = s_win[(4 * team + g) * GWIN_INTS + q], wh = s_win[(4 * team + g) * GWIN_INTS + 9 + q];
-                if (wh >= 0) {
-                    lo = min(lo, wl);
-                    hi = max(hi, wh);
-                }
+            for (int g = 0; g < 2; ++g) {
+                lo = min(lo, s_win[(2 * team + g) * 18 + q]);
+                hi = max(hi, s_win[(2 * team + g) * 18 + 9 + q]);
             }
         }
         if (tid < 32) plan_tile_team(lo, hi, q, WIN_CAP, s_rec + team * PLAN_INTS);
@@ -478,6 +526,33 @@ __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, 
     if (tid < 2 * PLAN_INTS) {
         const int64_t tile = 2 * blk + (tid >> 5);
         if (tile < ntiles) plan[tile * PLAN_INTS + (tid & 31)] = s_rec[tid];
+    }
+    if (tid == 0) blk_taps[blk] = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
+}
+
+// The build's status and the sum of the resolve blocks' present counts, posted to the
+// host's mailbox by one block after the resolve has ended (so every write of the build
+// is visible device-wide when the host sees the post).  Counting the blocks inside the
+// resolve instead cost more: a device-scope fence per block writes back the XCD's L2,
+// and a returning device atomic per block holds each block for a round trip to memory.
+__global__ __launch_bounds__(1024) void k_post_status(const DevStatus *st, const uint32_t *__restrict__ blk_taps,
+                                                      int64_t nblk, Mailbox *mb, uint32_t seq)
+{
+    __shared__ unsigned long long s_part[16];
+    unsigned long long t = 0;
+    for (int64_t i = threadIdx.x; i < nblk; i += 1024) t += blk_taps[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long taps = st->taps;
+        for (int w = 0; w < 16; ++w) taps += s_part[w];
+        mb->flags = st->flags;
+        mb->taps = taps;
+        mb->count = st->count;
+        __threadfence_system();
+        __hip_atomic_store(&mb->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
@@ -918,8 +993,8 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     const int chunks = (int)((words + chw * SK_MAX_TILES - 1) / (chw * SK_MAX_TILES));
     const int64_t stiles = (words + (int64_t)chunks * chw - 1) / ((int64_t)chunks * chw);
     const int64_t rblocks = (n + RR_T - 1) / RR_T;  // resolve blocks of the dense path
-    // the status block first, then the per-block present counts: one read-back copies both
-    size_t off = up(sizeof(DevStatus) + (size_t)(path == 2 ? rblocks : grid_blocks(n)) * 4);
+    // the status block first, then the per-block present counts (dense and sparse paths)
+    size_t off = up(sizeof(DevStatus) + (size_t)(path == 2 ? rblocks : (path == 3 ? grid_blocks(n) : 0)) * 4);
     size_t o_keys = 0, o_vals = 0, o_bm = 0, o_pre = 0, o_aux = 0;
     if (path == 2) {
         o_keys = off; off += up((size_t)n * sizeof(K));
@@ -937,6 +1012,8 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     uint32_t *blk_taps = (uint32_t *)(scratch + sizeof(DevStatus));
     int status = SUBMCONV_OK;
     bool synced = false;  // the status read has synchronised the stream
+    Mailbox *mb = nullptr;
+    uint32_t mb_seq = 0;
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
         // one launch clears the status block and (dense path) the bitmap and the scan's flags;
@@ -972,9 +1049,21 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
                                    (unsigned long long *)(scratch + o_aux), st);
             hipLaunchKernelGGL(k_rank<K>, dim3(grid), dim3(256), 0, stream, (const K *)tmp, n,
                                (const unsigned long long *)bm, (const uint32_t *)pre, (K *)rb->keys, rb->perm);
-            hipLaunchKernelGGL(k_resolve_plan<K>, dim3((unsigned)rblocks), dim3(256), 0, stream, (const K *)rb->keys, n,
-                               rb->res, rb->rb, (const unsigned long long *)bm, (const uint32_t *)pre, rb->nbr_sp,
-                               rb->plan, ntiles, (const DevStatus *)st, blk_taps);
+            // the bitmap (words + 1 of padding) and the prefixes are below 2^28 bytes (nbits <= 31)
+            const int bm_bytes = (int)((words + 1) * 8), pre_bytes = (int)(words * 4);
+            if ((status = mailbox_acquire(&mb, &mb_seq)) != SUBMCONV_OK) break;
+            if (rb->rb >= 6)
+                hipLaunchKernelGGL((k_resolve_plan<K, true>), dim3((unsigned)rblocks), dim3(256), 0, stream,
+                                   (const K *)rb->keys, n, rb->res, rb->rb, (const unsigned long long *)bm, bm_bytes,
+                                   (const uint32_t *)pre, pre_bytes, rb->nbr_sp, rb->plan, ntiles,
+                                   (const DevStatus *)st, blk_taps);
+            else
+                hipLaunchKernelGGL((k_resolve_plan<K, false>), dim3((unsigned)rblocks), dim3(256), 0, stream,
+                                   (const K *)rb->keys, n, rb->res, rb->rb, (const unsigned long long *)bm, bm_bytes,
+                                   (const uint32_t *)pre, pre_bytes, rb->nbr_sp, rb->plan, ntiles,
+                                   (const DevStatus *)st, blk_taps);
+            hipLaunchKernelGGL(k_post_status, dim3(1), dim3(1024), 0, stream, (const DevStatus *)st,
+                               (const uint32_t *)blk_taps, rblocks, mb, mb_seq);
         } else {
             K *keys_b = (K *)(scratch + o_keys);
             int32_t *vals_b = (int32_t *)(scratch + o_vals);
@@ -993,8 +1082,13 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
         if (path == 3 && (status = win_plan_build(rb, blk_taps, (int64_t)grid, st, stream)) != SUBMCONV_OK) break;
         DevStatus h;
         uint64_t taps = 0;
-        if ((status = read_status_counts(st, path == 2 ? rblocks : 0, &h, &taps, stream)) != SUBMCONV_OK) break;
-        synced = true;
+        if (path == 2) {
+            // the resolve's last block posts the status: no copy, no stream synchronisation
+            if ((status = mailbox_wait(mb, mb_seq, &h, stream)) != SUBMCONV_OK) break;
+        } else {
+            if ((status = read_status_counts(st, 0, &h, &taps, stream)) != SUBMCONV_OK) break;
+            synced = true;
+        }
         if (path == 2 && !(h.flags & FLAG_RANGE) && (int64_t)h.count != n) h.flags |= FLAG_DUPLICATE;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
