@@ -539,8 +539,15 @@ __global__ __launch_bounds__(1024) void k_post_status(const DevStatus *st, const
                                                       int64_t nblk, Mailbox *mb, uint32_t seq)
 {
     __shared__ unsigned long long s_part[16];
+    // eight independent loads per step, so a step costs one round trip to memory
     unsigned long long t = 0;
-    for (int64_t i = threadIdx.x; i < nblk; i += 1024) t += blk_taps[i];
+    for (int64_t i0 = threadIdx.x; i0 < nblk; i0 += 8 * 1024) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + u * 1024 < nblk ? blk_taps[i0 + u * 1024] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t += v[u];
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
     if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = t;

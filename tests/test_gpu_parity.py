@@ -512,6 +512,41 @@ def test_rulebook_cache_rebuilds_for_another_set_of_the_same_size():
     cache.clear()
 
 
+def test_builds_on_two_host_threads():
+    """Dense-path builds post their status to a mailbox of the calling host thread:
+    builds running on two threads at once, each on its own stream, return exact
+    tables and their own present counts."""
+    import threading
+    w2, c2 = synth.workload(2)
+    w3, c3 = synth.workload(3)
+    e2 = dense.neighbor_table(c2, w2.res, 1)
+    e3 = dense.neighbor_table(c3, w3.res, 1)
+    jobs = {"64^3": (c2, w2.res, e2), "128^3": (c3, w3.res, e3)}
+    got = {}
+
+    def work(name):
+        c, res, e = jobs[name]
+        s = torch.cuda.Stream()
+        ok = True
+        with torch.cuda.stream(s):
+            for it in range(6):
+                rb = sc.submconv_build_map(coords_dev(c), res, 1)
+                table = rb.neighbors()
+                s.synchronize()
+                ok = ok and np.array_equal(table.cpu().numpy(), e) and rb.taps_present == int((e >= 0).sum())
+                rb.free()
+        s.synchronize()
+        got[name] = ok
+
+    note("builds on two host threads")
+    threads = [threading.Thread(target=work, args=(name,)) for name in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert got == {name: True for name in jobs}
+
+
 def test_block_cache_limit_and_cross_stream_reuse():
     """With caching off every block goes back to the driver; with it on, a block freed
     on one stream (work still queued there) is reused on another only after that work:
