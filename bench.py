@@ -2,7 +2,7 @@
 """Benchmark of the submanifold 3x3x3 convolution on one MI355X.
 
 One step = the whole path on one synthetic batch: build the neighbour map of
-the coordinate set (pack, sort, resolve, status read-back), then run the
+the coordinate set (pack, sort, resolve, the wait for its status), then run the
 forward pass on it (4 forward passes reusing the map for the 4-grid workload).
 Inputs are resident in device memory before the timed region starts.
 
@@ -12,7 +12,7 @@ outside the timed spans, so no input is left in the 256 MB last-level cache.
 `value` is forward active voxels per second (N divided by the mean forward
 kernel time from HIP events on the launch stream); `ms_per_step` is the GPU
 time of a whole step (map build + forward, HIP events; the map build's span
-includes its host-side status read-back); `host_ms_per_step` is the host wall
+includes the host's wait for its status); `host_ms_per_step` is the host wall
 time of a step, which also holds a short spin kernel that keeps the GPU busy
 while the forward is enqueued.  `roofline` is taken from the same cold reps.
 

@@ -20,7 +20,7 @@
 //   keys[s]       the sorted keys.
 // The input-order table nbr[i][k] (input rows) is derived from these on request.
 //
-// Dense key space (2^nbits bitmap bits affordable next to N), five launches:
+// Dense key space (2^nbits bitmap bits affordable next to N), six launches:
 //   clear    - zero the status block, the occupancy bitmap and the scan's flags;
 //   mark     - validate and pack each row's key and set its bit in the bitmap
 //              (a per-block LDS hash of bitmap words first, then one device-scope
@@ -33,7 +33,10 @@
 //   resolve + plan - each block of 256 sorted positions forms each neighbour row
 //              from three bits and one rank query per (dz, dy) row, writes the rows as
 //              coalesced runs, and computes the staging plans of its two tiles from
-//              the group windows in LDS.
+//              its waves' row windows in LDS;
+//   post     - one block sums the resolve blocks' present counts and writes the
+//              status to the host's pinned mailbox, which the call polls (no copy and
+//              no stream synchronisation).
 // Sparse key space (huge grid, few voxels):
 //   pack + multi-pass LSD radix sort, then per tile of 256 sorted voxels: the x
 //   neighbours of the centre row are the adjacent sorted entries; for each of the
