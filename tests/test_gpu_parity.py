@@ -101,6 +101,32 @@ def test_map_full_cube_boundary(res):
     np.testing.assert_array_equal(got, dense.neighbor_table(c, res, 1))
 
 
+@pytest.mark.parametrize("res,batch", [(33, 2), (64, 1), (100, 3)])
+def test_map_grid_faces_dense_path(res, batch):
+    """A hollow box three voxels thick on all six faces of the grid (60% of its cells),
+    in every batch entry: more than 2048 voxels and at least 6 key bits per axis, so the
+    bitmap path forms all nine rows from one word offset.  Rows that fall off the grid
+    (below 0, past res - 1 into the next row, plane or batch entry, or past the bitmap's
+    end) must come out absent."""
+    rng = np.random.default_rng(1000 + res)
+    g = np.arange(res)
+    z, y, x = np.meshgrid(g, g, g, indexing="ij")
+    box = (np.minimum(np.minimum(z, y), x) < 3) | (np.maximum(np.maximum(z, y), x) >= res - 3)
+    zyx = np.argwhere(box).astype(np.int32)
+    parts = []
+    for b in range(batch):
+        keep = zyx[rng.random(len(zyx)) < 0.6]
+        parts.append(np.concatenate([np.full((len(keep), 1), b, np.int32), keep], 1))
+    c = np.concatenate(parts)
+    c = c[synth.shuffle_rows(len(c), res)]
+    assert len(c) > 2048
+    note("map grid faces res=%d batch=%d n=%d" % (res, batch, len(c)))
+    rb = build(c, res, batch)
+    got = rb.neighbors().cpu().numpy()
+    np.testing.assert_array_equal(got, dense.neighbor_table(c, res, batch))
+    assert rb.taps_present == int((got >= 0).sum())
+
+
 def test_map_batches_isolated():
     # the same set in batch 0 and 2, batch 1 empty: no voxel may see another batch
     base = synth.random_coords(500, 8, 1, 9)
