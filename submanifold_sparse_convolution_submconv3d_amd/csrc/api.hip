@@ -47,26 +47,57 @@ int fail(int status, const char *fmt, ...)
     return status;
 }
 
-static thread_local DevStatus *g_pinned = nullptr;
-
-static thread_local size_t g_pinned_bytes = 0;
+// Pinned host blocks of a host thread: the status read-back buffer and the status
+// mailbox.  A thread's blocks go back to a process-wide list when the thread exits
+// (no HIP call there: the runtime may already be shutting down) and are handed to the
+// next thread that needs one, so short-lived threads do not pile up pinned memory.
+namespace {
+struct PinnedSet {
+    DevStatus *pinned = nullptr;   // read-back buffer
+    size_t pinned_bytes = 0;
+    Mailbox *mb = nullptr;         // host address of the mailbox
+    Mailbox *mb_dev = nullptr;     // its device address
+    uint32_t seq = 0;              // the last sequence number used on it
+};
+std::mutex g_pinned_mu;
+std::vector<PinnedSet> g_pinned_free;
+struct PinnedHolder {
+    PinnedSet p;
+    PinnedHolder()
+    {
+        std::lock_guard<std::mutex> lk(g_pinned_mu);
+        if (!g_pinned_free.empty()) {
+            p = g_pinned_free.back();
+            g_pinned_free.pop_back();
+        }
+    }
+    ~PinnedHolder()
+    {
+        if (!p.pinned && !p.mb) return;
+        std::lock_guard<std::mutex> lk(g_pinned_mu);
+        g_pinned_free.push_back(p);
+    }
+};
+thread_local PinnedHolder g_pin;
+}  // namespace
 
 int read_status_counts(const DevStatus *d, int64_t ncounts, DevStatus *h, uint64_t *sum, hipStream_t stream)
 {
     const size_t bytes = sizeof(DevStatus) + (size_t)ncounts * 4;
-    if (g_pinned_bytes < bytes) {  // grows to the largest read-back seen on this thread
-        if (g_pinned) (void)hipHostFree(g_pinned);
-        g_pinned = nullptr;
-        g_pinned_bytes = 0;
+    PinnedSet &ps = g_pin.p;
+    if (ps.pinned_bytes < bytes) {  // grows to the largest read-back seen on this thread
+        if (ps.pinned) (void)hipHostFree(ps.pinned);
+        ps.pinned = nullptr;
+        ps.pinned_bytes = 0;
         const size_t want = bytes < 4096 ? 4096 : bytes;
-        SC_HIP(hipHostMalloc((void **)&g_pinned, want, hipHostMallocDefault));
-        g_pinned_bytes = want;
+        SC_HIP(hipHostMalloc((void **)&ps.pinned, want, hipHostMallocDefault));
+        ps.pinned_bytes = want;
     }
-    SC_HIP(hipMemcpyAsync(g_pinned, d, bytes, hipMemcpyDeviceToHost, stream));
+    SC_HIP(hipMemcpyAsync(ps.pinned, d, bytes, hipMemcpyDeviceToHost, stream));
     SC_HIP(hipStreamSynchronize(stream));
-    *h = *g_pinned;
+    *h = *ps.pinned;
     uint64_t t = 0;
-    const uint32_t *c = (const uint32_t *)(g_pinned + 1);
+    const uint32_t *c = (const uint32_t *)(ps.pinned + 1);
     for (int64_t i = 0; i < ncounts; ++i) t += c[i];
     if (sum) *sum = t;
     return SUBMCONV_OK;
@@ -77,13 +108,10 @@ int read_status(const DevStatus *d, DevStatus *h, hipStream_t stream)
     return read_status_counts(d, 0, h, nullptr, stream);
 }
 
-static thread_local Mailbox *g_mailbox = nullptr;      // host address
-static thread_local Mailbox *g_mailbox_dev = nullptr;  // its device address
-static thread_local uint32_t g_mailbox_seq = 0;
-
 int mailbox_acquire(Mailbox **mb, uint32_t *seq)
 {
-    if (!g_mailbox) {
+    PinnedSet &ps = g_pin.p;
+    if (!ps.mb) {
         // coherent: the device's stores reach host memory while the kernel runs; portable:
         // usable from every device
         Mailbox *h = nullptr;
@@ -95,19 +123,22 @@ int mailbox_acquire(Mailbox **mb, uint32_t *seq)
             (void)hipHostFree(h);
             return fail(SUBMCONV_E_HIP, "hipHostGetDevicePointer failed for the status mailbox");
         }
-        g_mailbox = h;
-        g_mailbox_dev = (Mailbox *)dp;
+        ps.mb = h;
+        ps.mb_dev = (Mailbox *)dp;
+        ps.seq = 0;
     }
-    g_mailbox_seq = g_mailbox_seq + 1 ? g_mailbox_seq + 1 : 1;  // never 0, the initial value
-    *mb = g_mailbox_dev;
-    *seq = g_mailbox_seq;
+    // the sequence goes on from the mailbox's last one (it may come from an exited thread),
+    // so a stale post never matches; never 0, the initial value
+    ps.seq = ps.seq + 1 ? ps.seq + 1 : 1;
+    *mb = ps.mb_dev;
+    *seq = ps.seq;
     return SUBMCONV_OK;
 }
 
 int mailbox_wait(Mailbox *mb_dev, uint32_t seq, DevStatus *h, hipStream_t stream)
 {
     (void)mb_dev;
-    Mailbox *mb = g_mailbox;
+    Mailbox *mb = g_pin.p.mb;
     // poll for up to ~2 ms (a build of a few million voxels takes well under that); past
     // it, or if the post never comes (a failed launch), synchronise and check once more
     const auto t0 = std::chrono::steady_clock::now();
