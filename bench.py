@@ -342,6 +342,8 @@ def _forward_kernel(cin, cout, dtype, n):
     """Name of the kernel the automatic choice runs (for the record; the library decides)."""
     if dtype == "bf16" and cin == cout == 32 and n * 64 <= 2 ** 31 - 1:
         return "k_conv_win32"
+    if dtype == "bf16" and cin == cout == 64 and n >= 2 ** 19:
+        return "k_conv_mfma_rows"
     if dtype == "bf16" and cin == cout and cin in (64, 128) and n * cin * 2 <= 2 ** 31 - 1:
         return "k_conv_big<%d,%d,8>" % (cin, cout)
     if dtype == "f32" and cin == cout == 128:
