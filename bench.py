@@ -58,9 +58,10 @@ def src_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, dtype: str, kernel: str, algorithmic_bytes: float):
-    """HBM bytes per launch from the committed counter summary, if it was taken on
-    the current kernel source and the same input (same algorithmic bytes); else None."""
+def load_traffic(workload: str, dtype: str, kernel: str, algorithmic_bytes: float, runs: str = ""):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    kernel that runs now (`runs`: its name without namespace or template arguments), on
+    that kernel's current source and on the same input (same algorithmic bytes); else None."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -68,7 +69,10 @@ def load_traffic(workload: str, dtype: str, kernel: str, algorithmic_bytes: floa
     entry = data.get("%s/%s/%s" % (workload, dtype, kernel))
     if not entry:
         return None
-    if (entry.get("source_hash") != src_hash(kernel_sources(entry.get("kernel", "")))
+    recorded = entry.get("kernel", "")
+    if runs and recorded.replace("sc::", "").split("<")[0] != runs.split("<")[0]:
+        return None
+    if (entry.get("source_hash") != src_hash(kernel_sources(recorded))
             or entry.get("algorithmic_bytes") != float(algorithmic_bytes)):
         return None
     return entry.get("bytes_per_launch")
@@ -491,7 +495,8 @@ def config_record(wb, dt, warm, cold):
         "map_build_hbm_frac_warm": wb.n * 124.0 / (mw * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "step_ms": cold["step_ms"], "step_ms_warm": warm["step_ms"],
         "roofline": {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
-                     "frac_warm": ach_w / peak, "traffic": load_traffic(w.name, dt, "forward", abytes),
+                     "frac_warm": ach_w / peak,
+                     "traffic": load_traffic(w.name, dt, "forward", abytes, _forward_kernel(w.cin, w.cout, dt, wb.n)),
                      "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
     }
     if bound == "mfma":
@@ -648,7 +653,8 @@ def main():
         "map_build_ms_min": float(np.min(res["t_map"])),
         "map_algorithmic_GBps": n * 124.0 / (map_ms * 1e-3) / 1e9,
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                     "traffic": load_traffic(w.name + ("_shuffled" if args.shuffled else ""), dtype, "forward", abytes),
+                     "traffic": load_traffic(w.name + ("_shuffled" if args.shuffled else ""), dtype, "forward", abytes,
+                                             _forward_kernel(w.cin, w.cout, dtype, n) if variant == 0 else "(forced)"),
                      "kernel": _forward_kernel(w.cin, w.cout, dtype, n) if variant == 0 else args.variant,
                      "kernel_ms": fwd_ms, "reps": "cold" if cold else "warm",
                      "per_launch": {"flops": flops, "algorithmic_bytes": abytes}},
