@@ -318,11 +318,23 @@ __global__ __launch_bounds__(256) void k_cg_mark(const int4 *__restrict__ coords
         if (s_word[i] != ~0ull) atomicOr(&bm[s_word[i]], s_bits[i]);
 }
 
-// Child lists of the M coarse rows to -1 (M known on the device only); one row per thread.
+// The coarse kernels below run over the M coarse rows, a count known on the device only.
+// Sized for the fine count n (M's upper bound), most blocks of a launch would only read
+// M and exit, each holding its slot for that load (M is n / 8 on a subdivided set); so
+// they take a grid of at most CG_BLOCKS blocks, enough to fill the chip, and walk M in
+// grid-sized strides.
+constexpr int64_t CG_BLOCKS = 2048;
+static unsigned cg_grid(int64_t threads)
+{
+    const int64_t blocks = (threads + 255) / 256;
+    return (unsigned)(blocks < 1 ? 1 : (blocks < CG_BLOCKS ? blocks : CG_BLOCKS));
+}
+
+// Child lists of the M coarse rows to -1.
 __global__ __launch_bounds__(256) void k_cg_init(int4 *__restrict__ child, const uint32_t *__restrict__ total)
 {
-    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over the capacity, n rows
-    if (m < (int64_t)*total) {
+    const int64_t mend = *total, stride = (int64_t)gridDim.x * 256;
+    for (int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x; m < mend; m += stride) {
         child[2 * m] = make_int4(-1, -1, -1, -1);
         child[2 * m + 1] = make_int4(-1, -1, -1, -1);
     }
@@ -351,17 +363,12 @@ __global__ __launch_bounds__(256) void k_cg_rank(const uint32_t *__restrict__ ck
                               (int)(key & msk));
 }
 
-// Downsample output: one thread per (coarse row, group of V channels), V = 16 bytes of
+// Downsample output: one item per (coarse row, group of V channels), V = 16 bytes of
 // channels when rows are whole 16-byte vectors, else 1; children in slot order.
 template <typename T, int V, bool MEAN>
-__global__ __launch_bounds__(256) void k_cg_pool(const int32_t *__restrict__ child, const uint32_t *__restrict__ total,
-                                                 int c, const T *__restrict__ feats, T *__restrict__ out_feats)
+__device__ __forceinline__ void cg_pool_item(const int32_t *__restrict__ child, int c, const T *__restrict__ feats,
+                                             T *__restrict__ out_feats, int64_t m, int gi)
 {
-    const int groups = c / V;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int gi;
-    const int64_t m = split_index(e, groups, gi);
-    if (m >= (int64_t)*total) return;
     const int c0 = gi * V;
     float acc[V];
 #pragma unroll
@@ -388,22 +395,34 @@ __global__ __launch_bounds__(256) void k_cg_pool(const int32_t *__restrict__ chi
     else out_feats[m * c + c0] = y[0];
 }
 
-// Space-to-depth output: one thread per (coarse row, slot, unit of a row), units U of
+template <typename T, int V, bool MEAN>
+__global__ __launch_bounds__(256) void k_cg_pool(const int32_t *__restrict__ child, const uint32_t *__restrict__ total,
+                                                 int c, const T *__restrict__ feats, T *__restrict__ out_feats)
+{
+    const int groups = c / V;
+    const int64_t end = (int64_t)*total * groups, stride = (int64_t)gridDim.x * 256;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < end; e += stride) {
+        int gi;
+        const int64_t m = split_index(e, groups, gi);
+        cg_pool_item<T, V, MEAN>(child, c, feats, out_feats, m, gi);
+    }
+}
+
+// Space-to-depth output: one item per (coarse row, slot, unit of a row), units U of
 // 16 bytes when rows are whole vectors, else elements; empty slots zero.
 template <typename U>
 __global__ __launch_bounds__(256) void k_cg_s2d(const int32_t *__restrict__ child, const uint32_t *__restrict__ total,
                                                 int upr, const U *__restrict__ feats, U *__restrict__ out_feats,
                                                 uint8_t *__restrict__ out_mask)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over rows x 8 slots x units per row
-    int ui;
-    const int64_t ms = split_index(e, upr, ui);
-    const int64_t m = ms >> 3;
-    if (m >= (int64_t)*total) return;
-
-    const int32_t r = child[ms];
-    out_feats[e] = r >= 0 ? feats[(int64_t)r * upr + ui] : U{};
-    if (ui == 0 && out_mask) out_mask[ms] = r >= 0;
+    const int64_t end = (int64_t)*total * 8 * upr, stride = (int64_t)gridDim.x * 256;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < end; e += stride) {  // rows x 8 slots x units
+        int ui;
+        const int64_t ms = split_index(e, upr, ui);
+        const int32_t r = child[ms];
+        out_feats[e] = r >= 0 ? feats[(int64_t)r * upr + ui] : U{};
+        if (ui == 0 && out_mask) out_mask[ms] = r >= 0;
+    }
 }
 
 template <typename T>
@@ -440,21 +459,21 @@ static int coarse_group_bitmap(const int32_t *coords, const void *feats, int64_t
         if ((status = exclusive_scan_u32((const uint32_t *)bm, pre, words, total, sc + o_scan, s, SCAN_POPC64, true)) !=
             SUBMCONV_OK)
             break;
-        hipLaunchKernelGGL(k_cg_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (int4 *)child, total);
+        hipLaunchKernelGGL(k_cg_init, dim3(cg_grid(n)), dim3(256), 0, s, (int4 *)child, total);
         hipLaunchKernelGGL(k_cg_rank, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ckey, (const int4 *)coords, n,
                            rbc, bm, pre, child, (int4 *)out_coords, st);
         constexpr int V = 16 / sizeof(T);  // elements of a 16-byte vector
         const bool vec = (c * sizeof(T)) % 16 == 0 && ((uintptr_t)feats & 15) == 0 && ((uintptr_t)out_feats & 15) == 0;
         if (op == COARSE_S2D) {
             if (vec)
-                hipLaunchKernelGGL(k_cg_s2d<uint4>, dim3((unsigned)((n * 8 * (c / V) + 255) / 256)), dim3(256), 0, s,
+                hipLaunchKernelGGL(k_cg_s2d<uint4>, dim3(cg_grid(n * 8 * (c / V))), dim3(256), 0, s,
                                    child, total, c / V, (const uint4 *)feats, (uint4 *)out_feats, out_mask);
             else
-                hipLaunchKernelGGL(k_cg_s2d<T>, dim3((unsigned)((n * 8 * c + 255) / 256)), dim3(256), 0, s, child, total,
+                hipLaunchKernelGGL(k_cg_s2d<T>, dim3(cg_grid(n * 8 * c)), dim3(256), 0, s, child, total,
                                    c, (const T *)feats, (T *)out_feats, out_mask);
         } else {
             const int gv = vec ? V : 1;
-            const unsigned grid = (unsigned)((n * (c / gv) + 255) / 256);
+            const unsigned grid = cg_grid(n * (c / gv));
             if (vec && op == COARSE_MEAN)
                 hipLaunchKernelGGL((k_cg_pool<T, V, true>), dim3(grid), dim3(256), 0, s, child, total, c, (const T *)feats,
                                    (T *)out_feats);
@@ -607,13 +626,30 @@ __global__ __launch_bounds__(256) void k_d2s_count(const uint8_t *__restrict__ m
     cnt[i] = c;
 }
 
-// Children of the two expansions: one thread per (voxel, vector of a child row), over
-// the 8 slots in order; V = uint4 when rows are whole 16-byte vectors, else the element
-// type.  REPL: the child copies the parent's whole row (masked upsample, read once);
-// otherwise it takes the slot's channels of an 8-times-wider row (depth_to_space).
-// mask == nullptr: every slot, child 8 cell + slot; else the masked slots, in slot
-// order, from base[cell].  MASK8: mask rows are 8-byte aligned and read as one word.
-template <typename V, bool REPL, bool MASK8>
+// Mask bits of a voxel's 8 slots (bit q set when mask byte q is nonzero).  MASK8: the
+// mask row is 8-byte aligned and read as one word.
+template <bool MASK8>
+__device__ __forceinline__ uint32_t slot_bits(const uint8_t *__restrict__ mask, int64_t cell)
+{
+    uint32_t bits = 0;
+    if (MASK8) {
+        const unsigned long long w = *(const unsigned long long *)(mask + cell * 8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) bits |= ((w >> (8 * q)) & 0xFFull) ? 1u << q : 0u;
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) bits |= mask[cell * 8 + q] ? 1u << q : 0u;
+    }
+    return bits;
+}
+
+// Children of the two expansions.  V = uint4 when rows are whole 16-byte vectors, else
+// the element type.  mask == nullptr: every slot, child 8 cell + slot; else the masked
+// slots, in slot order, from base[cell].
+//
+// Masked upsample: the child copies the parent's whole row.  One thread per (voxel,
+// vector of the row), over the 8 slots in order, so the parent row is read once.
+template <typename V, bool MASK8>
 __global__ __launch_bounds__(256) void k_expand(const int4 *__restrict__ cc, const V *__restrict__ cf,
                                                 const uint8_t *__restrict__ mask, const uint32_t *__restrict__ base,
                                                 int64_t m, int vpr, int4 *__restrict__ out_coords,
@@ -626,29 +662,49 @@ __global__ __launch_bounds__(256) void k_expand(const int4 *__restrict__ cc, con
     uint32_t bits = 0xFFu;
     int64_t dst = cell * 8;
     if (mask) {
-        bits = 0;
-        if (MASK8) {
-            const unsigned long long w = *(const unsigned long long *)(mask + cell * 8);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) bits |= ((w >> (8 * q)) & 0xFFull) ? 1u << q : 0u;
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) bits |= mask[cell * 8 + q] ? 1u << q : 0u;
-        }
+        bits = slot_bits<MASK8>(mask, cell);
         dst = base[cell];
     }
-    V v{};
-    if (REPL) v = cf[cell * vpr + vi];
+    const V v = cf[cell * vpr + vi];
     int4 p = make_int4(0, 0, 0, 0);
     if (vi == 0) p = cc[cell];
 #pragma unroll
     for (int slot = 0; slot < 8; ++slot) {
         if (!((bits >> slot) & 1u)) continue;
         if (dst >= 8 * m) break;
-        out_feats[dst * vpr + vi] = REPL ? v : cf[(cell * 8 + slot) * vpr + vi];
+        out_feats[dst * vpr + vi] = v;
         if (vi == 0)
             out_coords[dst] = make_int4(p.x, 2 * p.y + (slot & 1), 2 * p.z + ((slot >> 1) & 1), 2 * p.w + (slot >> 2));
         ++dst;
+    }
+}
+
+// depth_to_space: child `slot` takes that slot's channels of the voxel's 8-times-wider
+// row.  One thread per (voxel, slot, vector of a child row): thread e copies input
+// element e, so a voxel's whole row is read as one contiguous run, and its present
+// children, which take consecutive output rows, are written as one.
+template <typename V, bool MASK8>
+__global__ __launch_bounds__(256) void k_d2s(const int4 *__restrict__ cc, const V *__restrict__ cf,
+                                             const uint8_t *__restrict__ mask, const uint32_t *__restrict__ base,
+                                             int64_t m, int vpr, int4 *__restrict__ out_coords,
+                                             V *__restrict__ out_feats)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over m x 8 x vpr
+    if (e >= m * 8 * vpr) return;
+    int r, vi;
+    const int64_t cell = split_index(e, 8 * vpr, r);
+    const int slot = (int)split_index(r, vpr, vi);
+    int64_t dst = cell * 8 + slot;
+    if (mask) {
+        const uint32_t bits = slot_bits<MASK8>(mask, cell);
+        if (!((bits >> slot) & 1u)) return;
+        dst = base[cell] + __popc(bits & ((1u << slot) - 1u));
+        if (dst >= 8 * m) return;
+    }
+    out_feats[dst * vpr + vi] = cf[e];
+    if (vi == 0) {
+        const int4 p = cc[cell];
+        out_coords[dst] = make_int4(p.x, 2 * p.y + (slot & 1), 2 * p.z + ((slot >> 1) & 1), 2 * p.w + (slot >> 2));
     }
 }
 
@@ -656,13 +712,23 @@ template <typename V, bool REPL>
 static void launch_expand_v(const int32_t *cc, const V *cf, const uint8_t *mask, const uint32_t *base, int64_t m,
                             int vpr, int32_t *out_coords, V *out_feats, hipStream_t s)
 {
-    const unsigned grid = (unsigned)((m * vpr + 255) / 256);
-    if (mask && ((uintptr_t)mask & 7) == 0)
-        hipLaunchKernelGGL((k_expand<V, REPL, true>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, cf, mask, base, m,
-                           vpr, (int4 *)out_coords, out_feats);
-    else
-        hipLaunchKernelGGL((k_expand<V, REPL, false>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, cf, mask, base,
-                           m, vpr, (int4 *)out_coords, out_feats);
+    if constexpr (!REPL) {
+        const unsigned g8 = (unsigned)((m * 8 * vpr + 255) / 256);
+        if (mask && ((uintptr_t)mask & 7) == 0)
+            hipLaunchKernelGGL((k_d2s<V, true>), dim3(g8), dim3(256), 0, s, (const int4 *)cc, cf, mask, base, m, vpr,
+                               (int4 *)out_coords, out_feats);
+        else
+            hipLaunchKernelGGL((k_d2s<V, false>), dim3(g8), dim3(256), 0, s, (const int4 *)cc, cf, mask, base, m, vpr,
+                               (int4 *)out_coords, out_feats);
+    } else {
+        const unsigned grid = (unsigned)((m * vpr + 255) / 256);
+        if (mask && ((uintptr_t)mask & 7) == 0)
+            hipLaunchKernelGGL((k_expand<V, true>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, cf, mask, base, m,
+                               vpr, (int4 *)out_coords, out_feats);
+        else
+            hipLaunchKernelGGL((k_expand<V, false>), dim3(grid), dim3(256), 0, s, (const int4 *)cc, cf, mask, base,
+                               m, vpr, (int4 *)out_coords, out_feats);
+    }
 }
 
 template <bool REPL>
