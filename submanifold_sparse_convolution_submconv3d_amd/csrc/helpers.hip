@@ -232,8 +232,20 @@ __global__ __launch_bounds__(256) void k_down_rows(const K *__restrict__ sk, con
     start[m] = (uint32_t)s;
 }
 
+// Kernels that run over the M coarse rows, a count known on the device only.
+// Sized for the fine count n (M's upper bound), most blocks of a launch would only read
+// M and exit, each holding its slot for that load (M is n / 8 on a subdivided set); so
+// they take a grid of at most CG_BLOCKS blocks, enough to fill the chip, and walk M in
+// grid-sized strides.
+constexpr int64_t CG_BLOCKS = 2048;
+static unsigned cg_grid(int64_t threads)
+{
+    const int64_t blocks = (threads + 255) / 256;
+    return (unsigned)(blocks < 1 ? 1 : (blocks < CG_BLOCKS ? blocks : CG_BLOCKS));
+}
+
 // Pool one coarse voxel's children (at most 8, contiguous in sorted order and in slot
-// order): one thread per (coarse voxel, channel).  MEAN: the fp32 sum in slot order
+// order): one item per (coarse voxel, channel).  MEAN: the fp32 sum in slot order
 // divided by the count, one rounding to the output type; else the maximum (exact).
 template <typename T, bool MEAN>
 __global__ __launch_bounds__(256) void k_down_reduce(const int32_t *__restrict__ perm,
@@ -242,21 +254,22 @@ __global__ __launch_bounds__(256) void k_down_reduce(const int32_t *__restrict__
                                                      const uint32_t *__restrict__ total, int64_t n, int c,
                                                      const T *__restrict__ feats, T *__restrict__ out_feats)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over (at most n coarse voxels) x c
-    int ci;
-    const int64_t m = split_index(e, c, ci);
-    if (m >= (int64_t)*total) return;
-    const int64_t s0 = start[m];
-    float acc = MEAN ? 0.f : -__builtin_huge_valf();
-    int cnt = 0;
-    for (int q = 0; q < 8; ++q) {
-        const int64_t s = s0 + q;
-        if (s >= n || (int64_t)seg[s] != m) break;
-        const float v = Elem<T>::to_f32(feats[(int64_t)perm[s] * c + ci]);
-        acc = MEAN ? acc + v : fmaxf(acc, v);
-        ++cnt;
+    const int64_t end = (int64_t)*total * c, stride = (int64_t)gridDim.x * 256;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < end; e += stride) {
+        int ci;
+        const int64_t m = split_index(e, c, ci);
+        const int64_t s0 = start[m];
+        float acc = MEAN ? 0.f : -__builtin_huge_valf();
+        int cnt = 0;
+        for (int q = 0; q < 8; ++q) {
+            const int64_t s = s0 + q;
+            if (s >= n || (int64_t)seg[s] != m) break;
+            const float v = Elem<T>::to_f32(feats[(int64_t)perm[s] * c + ci]);
+            acc = MEAN ? acc + v : fmaxf(acc, v);
+            ++cnt;
+        }
+        out_feats[m * c + ci] = Elem<T>::from_f32(MEAN ? acc / (float)cnt : acc);
     }
-    out_feats[m * c + ci] = Elem<T>::from_f32(MEAN ? acc / (float)cnt : acc);
 }
 
 // Operations of the coarse-grouping pipelines below.
@@ -316,18 +329,6 @@ __global__ __launch_bounds__(256) void k_cg_mark(const int4 *__restrict__ coords
     __syncthreads();
     for (int i = threadIdx.x; i < CG_SLOTS; i += 256)
         if (s_word[i] != ~0ull) atomicOr(&bm[s_word[i]], s_bits[i]);
-}
-
-// The coarse kernels below run over the M coarse rows, a count known on the device only.
-// Sized for the fine count n (M's upper bound), most blocks of a launch would only read
-// M and exit, each holding its slot for that load (M is n / 8 on a subdivided set); so
-// they take a grid of at most CG_BLOCKS blocks, enough to fill the chip, and walk M in
-// grid-sized strides.
-constexpr int64_t CG_BLOCKS = 2048;
-static unsigned cg_grid(int64_t threads)
-{
-    const int64_t blocks = (threads + 255) / 256;
-    return (unsigned)(blocks < 1 ? 1 : (blocks < CG_BLOCKS ? blocks : CG_BLOCKS));
 }
 
 // Child lists of the M coarse rows to -1.
@@ -552,10 +553,10 @@ static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, 
             hipLaunchKernelGGL(k_down_rows<K>, dim3(grid), dim3(256), 0, s, ka, head, seg, n, rbc,
                                (int4 *)out_coords, start);
             if (op == COARSE_MEAN)
-                hipLaunchKernelGGL((k_down_reduce<T, true>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                hipLaunchKernelGGL((k_down_reduce<T, true>), dim3(cg_grid(total)), dim3(256), 0,
                                    s, va, seg, start, tot, n, c, (const T *)feats, (T *)out_feats);
             else
-                hipLaunchKernelGGL((k_down_reduce<T, false>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                hipLaunchKernelGGL((k_down_reduce<T, false>), dim3(cg_grid(total)), dim3(256), 0,
                                    s, va, seg, start, tot, n, c, (const T *)feats, (T *)out_feats);
         }
         hipLaunchKernelGGL(k_store_count, dim3(1), dim3(1), 0, s, tot, st);

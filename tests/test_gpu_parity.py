@@ -626,13 +626,17 @@ def test_subdivide(dtype, ch):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n,res,batch", [(1, 2, 1), (900, 12, 2), (5000, 33, 1), (3000, 2048, 2)])
-def test_space_to_depth_and_back(dtype, n, res, batch):
-    """Dense coarse key spaces group through a bitmap, sparse ones (2048^3) through a sort."""
+@pytest.mark.parametrize("n,res,batch,ch", [(1, 2, 1, 5), (900, 12, 2, 5), (5000, 33, 1, 5), (3000, 2048, 2, 5),
+                                            (900, 12, 2, 32), (3000, 2048, 2, 32), (200000, 128, 1, 32)])
+def test_space_to_depth_and_back(dtype, n, res, batch, ch):
+    """Dense coarse key spaces group through a bitmap, sparse ones (2048^3) through a sort.
+    5 channels take the per-element kernels, 32 the 16-byte vector ones; 200k voxels make
+    the output kernels, which walk the device-side coarse count in grid-sized strides, take
+    several strides."""
     c = synth.random_coords(n, res, batch, 8)
-    feats, _, _ = synth.make_values(n, 5, 1, 8)
-    tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, 5), np.float32), None, dtype)
-    note("s2d %s n=%d res=%d" % (dtype, n, res))
+    feats, _, _ = synth.make_values(n, ch, 1, 8)
+    tf, _, _, f64, _ = device_values(feats, np.zeros((1, 3, 3, 3, ch), np.float32), None, dtype)
+    note("s2d %s n=%d res=%d ch=%d" % (dtype, n, res, ch))
     cc, cf, mask = sc.submconv_space_to_depth(coords_dev(c), tf, res, batch)
     ecc, ecf, emask = ref.space_to_depth(c, f64)
     np.testing.assert_array_equal(cc.cpu().numpy(), ecc)
@@ -686,10 +690,12 @@ def test_upsample_masked(dtype, n, c):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["max", "mean"])
 @pytest.mark.parametrize("n,res,batch,c", [(1, 2, 1, 4), (900, 12, 2, 5), (5000, 33, 1, 32), (60000, 64, 2, 64),
-                                           (3000, 2048, 2, 8)])
+                                           (3000, 2048, 2, 8), (60000, 2048, 1, 16)])
 def test_downsample(dtype, mode, n, res, batch, c):
     """Pooling by 2: coarse coords exact and ascending; max exact; mean within the
-    feature tolerance (fp32 sum in slot order vs the oracle's fp64 mean)."""
+    feature tolerance (fp32 sum in slot order vs the oracle's fp64 mean).  The two
+    60000-voxel sets (bitmap and sort grouping) make the pooling kernels, which walk the
+    device-side coarse count in grid-sized strides, take more than one stride."""
     coords = synth.random_coords(n, res, batch, 22)
     coords = coords[synth.shuffle_rows(len(coords), 22)]
     feats, _, _ = synth.make_values(len(coords), c, 1, 22)
