@@ -138,8 +138,10 @@ int submconv_rulebook_free(submconv_rulebook *rb, void *stream);
  *            one round-to-nearest-even of the fp32 sum.
  *   flip   : 0 = correlation, 1 = mirrored kernel (weight tap 26 - k for tap k).
  *
- * Pointers must be aligned to 16 bytes.  Asynchronous: never synchronises and
- * allocates nothing.
+ * Pointers must be aligned to 16 bytes.  Asynchronous: never synchronises,
+ * allocates nothing and clears no memory; it is one kernel launch on `stream`, so a
+ * caller may capture it in a HIP graph and replay it (the rulebook, the buffers and
+ * the weights must then stay allocated, and a replay reads their current contents).
  */
 int submconv_forward(const void *feats, const void *weight, const float *bias,
                      const submconv_rulebook *rb, void *out, int32_t cin, int32_t cout,
