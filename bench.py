@@ -354,6 +354,8 @@ def _forward_kernel(cin, cout, dtype, n):
         return "k_conv_mfma<float,128,128>"
     if cin in (32, 64, 128) and cout in (32, 64, 128):
         return "k_conv_mfma_rows"
+    if cin == cout == 16 and n * 16 * (4 if dtype == "f32" else 2) <= 2 ** 31 - 1:
+        return "k_conv_mfma16<%s>" % ("float" if dtype == "f32" else "unsigned short")
     return "k_conv_lowc" if cin <= 32 and cout <= 32 else "k_conv_generic"
 
 

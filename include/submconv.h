@@ -66,7 +66,7 @@ extern "C" {
 #define SUBMCONV_KERNEL_AUTO 0    /* pick by (Cin, Cout, dtype, N) */
 #define SUBMCONV_KERNEL_GENERIC 1 /* one thread per output element, any channel counts */
 #define SUBMCONV_KERNEL_LOWC 2    /* narrow channels (<= 32), wave shuffles, no matrix cores */
-#define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128} */
+#define SUBMCONV_KERNEL_MFMA 3    /* implicit GEMM on matrix cores, Cin/Cout in {32,64,128}, or 16 -> 16 */
 #define SUBMCONV_KERNEL_WINDOW 4  /* matrix cores fed from a tile's neighbourhood staged in LDS
                                      (bf16, Cin = Cout = 32, N * 64 <= 2^31 - 1; otherwise
                                      SUBMCONV_E_UNSUPPORTED) */
@@ -132,8 +132,8 @@ int submconv_rulebook_free(submconv_rulebook *rb, void *stream);
  *   weight : device KRSC [cout, 3, 3, 3, cin] of dtype.
  *   bias   : device fp32 [cout], or NULL for none (added once).
  *   out    : device [n, cout] of dtype; must not overlap feats or weight (E_ALIAS).
- *   cin, cout : 1..1024; the matrix-core path takes {32, 64, 128}, the rest
- *            runs on the generic kernels.
+ *   cin, cout : 1..1024; the matrix-core path takes {32, 64, 128} x {32, 64, 128}
+ *            and 16 -> 16, the rest runs on the generic kernels.
  *   dtype  : SUBMCONV_F32 or SUBMCONV_BF16; accumulation is fp32, bf16 output is
  *            one round-to-nearest-even of the fp32 sum.
  *   flip   : 0 = correlation, 1 = mirrored kernel (weight tap 26 - k for tap k).

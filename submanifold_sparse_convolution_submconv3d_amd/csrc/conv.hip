@@ -84,10 +84,12 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
     static_assert(COUT <= 64 && (64 % COUT) == 0, "group must divide the wave");
     constexpr int VPB = 256 / COUT;                         // voxels per block pass
     constexpr int PER = (CIN + COUT - 1) / COUT;            // feature elements per lane
-    __shared__ float s_w[27 * CIN * COUT];                  // [27][CIN][COUT]
+    constexpr int WS = COUT + 1;                            // padded row: the scatter below hits distinct banks
+    __shared__ float s_w[27 * CIN * WS];                    // [27][CIN][COUT (+1)]
+    // the KRSC weights [COUT][27][CIN] read in order (whole lines), scattered transposed
     for (int e = threadIdx.x; e < 27 * CIN * COUT; e += 256) {
-        const int o = e % COUT, c = (e / COUT) % CIN, k = e / (COUT * CIN);
-        s_w[e] = Elem<T>::to_f32(w[((int64_t)o * 27 + k) * CIN + c]);
+        const int c = e % CIN, k = (e / CIN) % 27, o = e / (27 * CIN);
+        s_w[(k * CIN + c) * WS + o] = Elem<T>::to_f32(w[e]);
     }
     __syncthreads();
     const int o = threadIdx.x % COUT;
@@ -102,12 +104,15 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
     // every lane of a wave runs the same number of iterations (shuffles need all lanes)
     for (int64_t i0 = (int64_t)blockIdx.x * VPB; i0 < n; i0 += stride) {
         const int64_t s = i0 + threadIdx.x / COUT;
-        const int64_t i = s < n ? (int64_t)perm[s] : -1;
-        const bool live = (uint64_t)i < (uint64_t)n;
+        // the output row and the table row are loaded together (one round trip): both
+        // loads are unconditional, at a clamped position, and checked afterwards
+        const int64_t sc = s < n ? s : n - 1;
         int32_t row[NBR_INTS];
 #pragma unroll
-        for (int q = 0; q < NBR_INTS; ++q) row[q] = live ? nbr[s * NBR_INTS + q] : 0;
-        if (!live) row[9] = 0;
+        for (int q = 0; q < NBR_INTS; ++q) row[q] = nbr[sc * NBR_INTS + q];
+        const int64_t i = s < n ? (int64_t)perm[sc] : -1;
+        const bool live = (uint64_t)i < (uint64_t)n;
+        if (!live) row[9] = 0;  // no present taps
         float acc = 0.f;
 #pragma unroll
         for (int k0 = 0; k0 < 27; k0 += G) {
@@ -129,16 +134,133 @@ __global__ __launch_bounds__(256) void k_conv_lowc(const T *__restrict__ feats,
 #pragma unroll
             for (int t = 0; t < G; ++t) {
                 const int k = k0 + t;
-                const float *wk = s_w + (flip ? 26 - k : k) * CIN * COUT + o;
+                const float *wk = s_w + (flip ? 26 - k : k) * CIN * WS + o;
 #pragma unroll
                 for (int c = 0; c < CIN; ++c) {
                     const float fc = __shfl(f[t][c / COUT], gbase + (c % COUT), 64);
-                    acc = fmaf(wk[c * COUT], fc, acc);
+                    acc = fmaf(wk[c * WS], fc, acc);
                 }
             }
         }
         if (live) out[i * COUT + o] = Elem<T>::from_f32(acc + b);
     }
+}
+
+// ---------------------------------------------------------------------------
+// mfma16: Cin = Cout = 16 on the matrix cores
+//
+// One wave per column of 16 sorted voxels, computed transposed (out^T = W_k . F_k^T:
+// rows = output channels, columns = voxels).  Lane l = 16 q + m holds weight row m
+// (output channel m) and voxel m of the column, at input channels 4q .. 4q + 3; fp32
+// contracts them in four v_mfma_f32_16x16x4f32 steps (step e: channel 4q + e on both
+// operands), bf16 in one v_mfma_f32_16x16x16bf16_1k.  The result leaves lane l with
+// output channels 4q .. 4q + 3 of voxel m.  All 27 weight taps stay in registers, and
+// a column's neighbour rows are fetched through buffer resources: a missing neighbour
+// is an offset past the end, which reads zeros, so no load sits behind a branch.
+// ---------------------------------------------------------------------------
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Mfma16 {
+    static constexpr int G = 9;                                      // taps per batch of loads
+    using Frag = floatx4;                                            // 4 input channels
+    static __device__ __forceinline__ Frag load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    static __device__ __forceinline__ void mma(floatx4 &acc, const Frag &a, const Frag &b)
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma16<uint16_t> {
+    static constexpr int G = 27;
+    using Frag = shortx4;
+    static __device__ __forceinline__ Frag load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(shortx4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+    static __device__ __forceinline__ void mma(floatx4 &acc, const Frag &a, const Frag &b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(64) void k_conv_mfma16(const T *__restrict__ feats, const T *__restrict__ w,
+                                                    const float *__restrict__ bias,
+                                                    const int32_t *__restrict__ nbr,
+                                                    const int32_t *__restrict__ perm, T *__restrict__ out,
+                                                    int64_t n, int flip)
+{
+    using M = Mfma16<T>;
+    using Frag = typename M::Frag;
+    constexpr uint32_t ROW = 16 * sizeof(T), OOB = 0x80000000u;  // bytes per feature row; past every end
+    const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc((void *)feats, (short)0, (int)(n * ROW), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc((void *)perm, (short)0, (int)(n * 4), 0x00020000);
+    Frag wf[27];
+#pragma unroll
+    for (int k = 0; k < 27; ++k)
+        wf[k] = *(const Frag *)(w + ((int64_t)m * 27 + (flip ? 26 - k : k)) * 16 + 4 * q);
+    float bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bv[r] = bias ? bias[4 * q + r] : 0.f;
+    const int64_t ncol = (n + 15) / 16;
+    for (int64_t col = blockIdx.x; col < ncol; col += gridDim.x) {
+        // the voxel's table row and its output row, loaded together at a clamped position
+        const int64_t s = col * 16 + m, sc = s < n ? s : n - 1;
+        int32_t row[NBR_INTS];
+#pragma unroll
+        for (int e = 0; e < NBR_INTS; ++e) row[e] = nbr[sc * NBR_INTS + e];
+        const int64_t i = s < n ? (int64_t)perm[sc] : -1;
+        const bool live = (uint64_t)i < (uint64_t)n;
+        if (!live) row[9] = 0;  // no present taps
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < 27; k0 += M::G) {
+            bool ok[M::G];
+            int32_t j[M::G];
+#pragma unroll
+            for (int t = 0; t < M::G; ++t) {
+                const int32_t p = nbr_at(row, k0 + t);
+                ok[t] = (uint32_t)p < (uint64_t)n;
+                j[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, ok[t] ? (uint32_t)p * 4u : OOB, 0, 0);
+            }
+            Frag f[M::G];
+#pragma unroll
+            for (int t = 0; t < M::G; ++t)
+                f[t] = M::load(rf, ok[t] ? (uint32_t)j[t] * ROW + (uint32_t)q * (ROW / 4) : OOB);
+#pragma unroll
+            for (int t = 0; t < M::G; ++t) M::mma(acc, wf[k0 + t], f[t]);
+        }
+        if (live) {
+            T y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = Elem<T>::from_f32(acc[r] + bv[r]);
+            if constexpr (sizeof(T) == 4) *(float4 *)(out + i * 16 + 4 * q) = *(const float4 *)y;
+            else *(uint2 *)(out + i * 16 + 4 * q) = *(const uint2 *)y;
+        }
+    }
+}
+
+bool mfma16_supported(int cin, int cout, int dtype, int64_t n)
+{
+    // feature rows are addressed by 32-bit byte offsets (a buffer resource)
+    return cin == 16 && cout == 16 && n * 16 * (dtype == SUBMCONV_F32 ? 4 : 2) <= INT32_MAX;
+}
+
+template <typename T>
+static void launch_mfma16_t(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm,
+                            void *o, int64_t n, int flip, hipStream_t s)
+{
+    int64_t waves = (n + 15) / 16;  // one 16-voxel column per wave; up to 8 waves per CU
+    if (waves > 2048) waves = 2048;
+    hipLaunchKernelGGL(k_conv_mfma16<T>, dim3((unsigned)waves), dim3(64), 0, s, (const T *)f, (const T *)w, b, nbr,
+                       perm, (T *)o, n, flip);
 }
 
 // ---------------------------------------------------------------------------
@@ -899,12 +1021,21 @@ static int launch_mfma_cout(const void *f, const void *w, const float *b, const 
 static int launch_mfma(const void *f, const void *w, const float *b, const int32_t *nbr, const int32_t *perm, void *o,
                        int64_t n, int cin, int cout, int dtype, int flip, hipStream_t s)
 {
+    if (cin == 16 || cout == 16) {
+        if (!mfma16_supported(cin, cout, dtype, n))
+            return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: 16 channels need Cin = Cout = 16 and N * 16 * %d <= 2^31 - 1",
+                        dtype == SUBMCONV_F32 ? 4 : 2);
+        if (dtype == SUBMCONV_BF16) launch_mfma16_t<uint16_t>(f, w, b, nbr, perm, o, n, flip, s);
+        else launch_mfma16_t<float>(f, w, b, nbr, perm, o, n, flip, s);
+        SC_LAUNCHED("conv_mfma16");
+        return SUBMCONV_OK;
+    }
     switch (cin) {
     case 32: return launch_mfma_cout<32>(f, w, b, nbr, perm, o, n, cout, dtype, flip, s);
     case 64: return launch_mfma_cout<64>(f, w, b, nbr, perm, o, n, cout, dtype, flip, s);
     case 128: return launch_mfma_cout<128>(f, w, b, nbr, perm, o, n, cout, dtype, flip, s);
     }
-    return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: Cin must be 32, 64 or 128");
+    return fail(SUBMCONV_E_UNSUPPORTED, "mfma kernel: Cin must be 16, 32, 64 or 128");
 }
 
 bool window_supported(int cin, int cout, int dtype, int64_t n);
@@ -923,6 +1054,9 @@ int choose_forward_kernel(int cin, int cout, int dtype, int64_t n)
     if (dtype == SUBMCONV_BF16 && cin == 64 && cout == 64 && n >= (int64_t(1) << 19)) return SUBMCONV_KERNEL_MFMA;
     if (big_supported(cin, cout, dtype, n)) return SUBMCONV_KERNEL_PERSISTENT;
     if (mfma_size(cin) && mfma_size(cout)) return SUBMCONV_KERNEL_MFMA;
+    // 16 -> 16 on the matrix cores: 8.0 us against 27.3 us for the shuffle kernel on the
+    // 450-voxel 16^3 sphere (whose 27 x 16 unrolled shuffles the compiler serialises)
+    if (mfma16_supported(cin, cout, dtype, n)) return SUBMCONV_KERNEL_MFMA;
     if (pow2_le32(cin) && pow2_le32(cout)) return SUBMCONV_KERNEL_LOWC;
     (void)dtype;
     return SUBMCONV_KERNEL_GENERIC;

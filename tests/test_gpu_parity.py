@@ -223,7 +223,7 @@ def run_forward(c, res, batch, cin, cout, dtype, kernel, flip, seed=0, bias="uni
 @pytest.mark.parametrize("flip", [0, 1])
 @pytest.mark.parametrize("kernel,cin,cout", [("generic", 16, 16), ("generic", 3, 5), ("generic", 24, 40),
                                              ("lowc", 16, 16), ("lowc", 8, 32), ("lowc", 32, 16), ("lowc", 32, 32),
-                                             ("mfma", 32, 32), ("mfma", 64, 64), ("mfma", 128, 128),
+                                             ("mfma", 16, 16), ("mfma", 32, 32), ("mfma", 64, 64), ("mfma", 128, 128),
                                              ("mfma", 32, 128), ("mfma", 128, 64), ("mfma", 32, 64),
                                              ("mfma", 64, 128), ("mfma", 64, 32), ("mfma", 128, 32),
                                              ("persistent", 64, 64), ("persistent", 128, 128)])
@@ -306,7 +306,7 @@ def test_forward_window_shuffled_and_f32_rejected():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("kernel,c", [("generic", 8), ("lowc", 16), ("mfma", 32), ("mfma", 128), ("window", 32),
+@pytest.mark.parametrize("kernel,c", [("generic", 8), ("lowc", 16), ("mfma", 16), ("mfma", 32), ("mfma", 128), ("window", 32),
                                       ("persistent", 64), ("persistent", 128)])
 def test_forward_identity_kernel_exact(dtype, kernel, c):
     if kernel in ("window", "persistent") and dtype == "f32":
@@ -335,7 +335,7 @@ def _auto_kernel(cin, cout, dtype="f32"):
         return "window"
     if dtype == "bf16" and (cin, cout) in ((64, 64), (128, 128)):
         return "persistent"
-    if cin in (32, 64, 128) and cout in (32, 64, 128):
+    if (cin in (32, 64, 128) and cout in (32, 64, 128)) or cin == cout == 16:
         return "mfma"
     return "lowc" if cin <= 32 and cout <= 32 else "generic"
 
@@ -365,9 +365,11 @@ def full_check(c, res, batch, cin, cout, dtype, seed, bias, std, calls=1):
 # the rows MFMA kernel's three block layouts: on small sets two waves share a
 # 32-voxel column and split Cout (the random-set tests above); from 512 blocks of
 # 128 voxels on, one wave per column; from 2 * 256 * 256 voxels on, two columns per
-# wave.  Every output row against the oracle.
+# wave.  The 16 -> 16 sets take the 16-channel kernel, whose at most 2048 waves each walk
+# several 16-voxel columns at 70k voxels.  Every output row against the oracle.
 @pytest.mark.parametrize("n,cin,cout,dtype", [(70001, 64, 64, "f32"), (70001, 32, 128, "bf16"),
-                                              (140001, 64, 64, "bf16"), (140001, 128, 64, "f32")])
+                                              (140001, 64, 64, "bf16"), (140001, 128, 64, "f32"),
+                                              (70001, 16, 16, "f32"), (70001, 16, 16, "bf16")])
 def test_forward_mfma_rows_layouts(n, cin, cout, dtype):
     c = synth.random_coords(n, 64, 1, 21)
     feats, weight, b = synth.make_values(len(c), cin, cout, 5)
@@ -403,7 +405,7 @@ def test_forward_mfma_persistent_rounds(n):
 # kernel has blocks past the last voxel).  Every row against the oracle.
 @pytest.mark.parametrize("n", [1, 31, 33, 300])
 @pytest.mark.parametrize("cin,cout,dtype", [(128, 128, "f32"), (64, 64, "f32"), (32, 64, "bf16"),
-                                            (64, 64, "bf16"), (128, 128, "bf16")])
+                                            (64, 64, "bf16"), (128, 128, "bf16"), (16, 16, "f32"), (16, 16, "bf16")])
 def test_forward_tiny_sets(n, cin, cout, dtype):
     c = synth.random_coords(n, 8, 1, 40 + n)
     feats, weight, b = synth.make_values(len(c), cin, cout, 11)
