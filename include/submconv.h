@@ -91,10 +91,11 @@ typedef struct submconv_rulebook submconv_rulebook; /* opaque, library-owned */
  * coords[i] + offset(k), or -1.  It is exact (integer work).  It waits for the
  * build to finish to learn the validity status: E_COORD_RANGE if a coordinate is
  * out of range, E_DUPLICATE if two rows are equal (no rulebook is returned).  On
- * the bitmap path (grids of at most 2^31 keys) the build's last kernel writes the
- * status to pinned host memory and the call polls it instead of synchronising the
- * stream (for at most ~2 ms, then it synchronises); when it returns, the rulebook's
- * contents are complete, though the stream may not yet be idle.
+ * the bitmap path (grids of at most 2^31 keys) and for sets of at most 2048 voxels,
+ * the build's last kernel writes the status to pinned host memory and the call polls
+ * it instead of synchronising the stream (for at most ~2 ms, then it synchronises);
+ * when it returns, the rulebook's contents are complete, though the stream may not
+ * yet be idle.
  * Device memory comes from the library's block cache (submconv_release_cache),
  * else from the device's stream-ordered pool.
  *

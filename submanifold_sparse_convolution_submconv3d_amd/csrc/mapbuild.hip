@@ -44,7 +44,8 @@
 //   (off = the row's key offset), so the block copies that window of sorted keys
 //   into LDS and binary-searches there (a window too big for LDS is searched in
 //   place).
-// Small sets (n <= 2048) build in one block.  Coordinates are range-checked
+// Small sets (n <= 2048) build in one block, which also posts the status to the
+// host's mailbox itself (one launch in all).  Coordinates are range-checked
 // before packing and every neighbour coordinate is bounds-checked before its key
 // is formed, so a key never wraps into the next row, plane or batch entry.
 #include "common.h"
@@ -533,6 +534,18 @@ __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, 
     if (tid == 0) blk_taps[blk] = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
 }
 
+// The status into the host's pinned mailbox, `seq` last (one thread): a system-scope
+// release first, so the host sees the status only after every write before it.
+__device__ __forceinline__ void mailbox_post(Mailbox *mb, uint32_t seq, uint32_t flags, unsigned long long taps,
+                                             unsigned long long count)
+{
+    mb->flags = flags;
+    mb->taps = taps;
+    mb->count = count;
+    __threadfence_system();
+    __hip_atomic_store(&mb->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // The build's status and the sum of the resolve blocks' present counts, posted to the
 // host's mailbox by one block after the resolve has ended (so every write of the build
 // is visible device-wide when the host sees the post).  Counting the blocks inside the
@@ -558,11 +571,7 @@ __global__ __launch_bounds__(1024) void k_post_status(const DevStatus *st, const
     if (threadIdx.x == 0) {
         unsigned long long taps = st->taps;
         for (int w = 0; w < 16; ++w) taps += s_part[w];
-        mb->flags = st->flags;
-        mb->taps = taps;
-        mb->count = st->count;
-        __threadfence_system();
-        __hip_atomic_store(&mb->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        mailbox_post(mb, seq, st->flags, taps, st->count);
     }
 }
 
@@ -683,13 +692,16 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
 // small sets: one block
 // ---------------------------------------------------------------------------
 
+
 // End of a single-block build (every thread calls it, rows of all n sorted voxels in
 // s_rows): the rows go out as one run, the group windows are formed per 32 sorted
 // voxels in LDS, each tile's staging plan is computed by a team of 16 lanes, and the
-// status block is written whole (no clearing launch is needed for these builds).
+// status goes to the host's mailbox once every wave's stores have completed (they all
+// sit in this CU's L2, which the posting thread's system-scope release writes back),
+// so the call needs no copy and no stream synchronisation.
 __device__ void small_finish(const int32_t *s_rows, int n, int32_t *__restrict__ nbr_sp,
                              int32_t *__restrict__ plan, int32_t *s_gwin, int32_t *s_rec, uint32_t flags,
-                             uint32_t taps, DevStatus *st)
+                             uint32_t taps, Mailbox *mb, uint32_t seq)
 {
     const int tid = threadIdx.x;
     for (int e = tid; e < n * NBR_INTS; e += 1024) nbr_sp[e] = s_rows[e];
@@ -716,12 +728,9 @@ __device__ void small_finish(const int32_t *s_rows, int n, int32_t *__restrict__
     if (team < SMALL_N / WIN_TILE) plan_tile_team(lo, hi, q, WIN_CAP, s_rec + team * PLAN_INTS);
     __syncthreads();
     for (int e = tid; e < ntiles * PLAN_INTS; e += 1024) plan[e] = s_rec[e];
-    if (tid == 0) {
-        DevStatus v{};
-        v.flags = flags;
-        v.taps = taps;
-        *st = v;
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    __syncthreads();
+    if (tid == 0) mailbox_post(mb, seq, flags, taps, (unsigned long long)n);
 }
 
 // Key space of at most 2^16 bits: bitmap and prefix in LDS.
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
                                                          K *__restrict__ keys_out,
                                                          int32_t *__restrict__ perm_out,
                                                          int32_t *__restrict__ nbr_sp, int32_t *__restrict__ plan,
-                                                         DevStatus *st)
+                                                         Mailbox *mb, uint32_t seq)
 {
     constexpr int WORDS = (1 << SMALL_BITS) / 32;
     __shared__ uint32_t s_bm[WORDS];
@@ -786,12 +795,8 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
         if (w0 + 1 < words) s_pre[w0 + 1] = ex + a;
     }
     __syncthreads();
-    if (s_flags) {  // invalid set: report only
-        if (tid == 0) {
-            DevStatus v{};
-            v.flags = s_flags;
-            *st = v;
-        }
+    if (s_flags) {  // invalid set: report only (nothing was written)
+        if (tid == 0) mailbox_post(mb, seq, s_flags, 0ull, 0ull);
         return;
     }
     const K m = (K(1) << rb) - 1;
@@ -824,7 +829,7 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
     }
     if (present) atomicAdd(&s_taps, present);
     __syncthreads();
-    small_finish(s_rows, n, nbr_sp, plan, s_gwin, s_rec, 0u, s_taps, st);
+    small_finish(s_rows, n, nbr_sp, plan, s_gwin, s_rec, 0u, s_taps, mb, seq);
 }
 
 // Larger key space: bitonic sort of (key, row) in LDS, binary search in LDS.
@@ -834,7 +839,7 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
                                                       K *__restrict__ keys_out,
                                                       int32_t *__restrict__ perm_out,
                                                       int32_t *__restrict__ nbr_sp, int32_t *__restrict__ plan,
-                                                      DevStatus *st)
+                                                      Mailbox *mb, uint32_t seq)
 {
     __shared__ K s_key[SMALL_N];
     __shared__ int32_t s_row[SMALL_N];
@@ -914,7 +919,7 @@ __global__ __launch_bounds__(1024) void k_build_small(const int4 *__restrict__ c
     }
     if (present) atomicAdd(&s_red[0], present);
     __syncthreads();
-    small_finish(s_rows, n, nbr_sp, plan, s_gwin, s_rec, s_red[1], s_red[0], st);
+    small_finish(s_rows, n, nbr_sp, plan, s_gwin, s_rec, s_red[1], s_red[0], mb, seq);
 }
 
 // Group windows from a finished table (used after the single-block builds).
@@ -1034,14 +1039,15 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
                                0, stream, st, (unsigned long long *)(scratch + o_bm), clear_words,
                                (unsigned long long *)(scratch + o_aux), path == 2 ? stiles : int64_t(0));
         if (path == 0 || path == 1) {
+            if ((status = mailbox_acquire(&mb, &mb_seq)) != SUBMCONV_OK) break;
             if (path == 0)
                 hipLaunchKernelGGL(k_build_small_bm<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
                                    (int)n, rb->res, rb->batch, rb->rb, rb->nbits, (K *)rb->keys, rb->perm, rb->nbr_sp,
-                                   rb->plan, st);
+                                   rb->plan, mb, mb_seq);
             else
                 hipLaunchKernelGGL(k_build_small<K>, dim3(1), dim3(1024), 0, stream, (const int4 *)coords,
                                    (int)n, rb->res, rb->batch, rb->rb, (K *)rb->keys, rb->perm, rb->nbr_sp, rb->plan,
-                                   st);
+                                   mb, mb_seq);
         } else if (path == 2) {
             K *tmp = (K *)(scratch + o_keys);
             unsigned long long *bm = (unsigned long long *)(scratch + o_bm);
@@ -1092,8 +1098,8 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
         if (path == 3 && (status = win_plan_build(rb, blk_taps, (int64_t)grid, st, stream)) != SUBMCONV_OK) break;
         DevStatus h;
         uint64_t taps = 0;
-        if (path == 2) {
-            // the resolve's last block posts the status: no copy, no stream synchronisation
+        if (path <= 2) {
+            // the last kernel posts the status to the mailbox: no copy, no stream synchronisation
             if ((status = mailbox_wait(mb, mb_seq, &h, stream)) != SUBMCONV_OK) break;
         } else {
             if ((status = read_status_counts(st, 0, &h, &taps, stream)) != SUBMCONV_OK) break;
