@@ -21,6 +21,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "mailbox.h"
 
 namespace sc {
 
@@ -208,11 +209,11 @@ __global__ __launch_bounds__(256) void k_excl_to_seg(const uint32_t *__restrict_
     if (s < n) seg[s] = seg[s] + head[s] - 1;
 }
 
-__global__ void k_store_count(const uint32_t *__restrict__ total, DevStatus *st)
+// A helper call's status to the host's mailbox: the flags its kernels set in `st` (none
+// when st is null) and the output row count in *total.
+__global__ void k_post_count(const uint32_t *__restrict__ total, const DevStatus *st, Mailbox *mb, uint32_t seq)
 {
-    DevStatus v{};
-    v.count = *total;
-    *st = v;
+    mailbox_post(mb, seq, st ? st->flags : 0u, 0ull, (unsigned long long)*total);
 }
 
 // Coarse coordinates and the sorted position where each coarse voxel's children start.
@@ -448,7 +449,6 @@ static int coarse_group_bitmap(const int32_t *coords, const void *feats, int64_t
     DevStatus *st = (DevStatus *)(sc + o_st);
     uint32_t *total = (uint32_t *)&st->count;
     int status = SUBMCONV_OK;
-    bool synced = false;  // the status read has synchronised the stream
     do {
         if (hipMemsetAsync(bm, 0, (size_t)(words + 1) * 8, s) != hipSuccess ||
             hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) {
@@ -488,16 +488,18 @@ static int coarse_group_bitmap(const int32_t *coords, const void *feats, int64_t
                 hipLaunchKernelGGL((k_cg_pool<T, 1, false>), dim3(grid), dim3(256), 0, s, child, total, c,
                                    (const T *)feats, (T *)out_feats);
         }
+        Mailbox *mb = nullptr;
+        uint32_t seq = 0;
+        if ((status = mailbox_acquire(&mb, &seq)) != SUBMCONV_OK) break;
+        hipLaunchKernelGGL(k_post_count, dim3(1), dim3(1), 0, s, (const uint32_t *)total, (const DevStatus *)st, mb, seq);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in a coarse grouping failed"); break; }
         DevStatus h;
-        if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
-        synced = true;
+        if ((status = mailbox_wait(mb, seq, &h, s)) != SUBMCONV_OK) break;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
         else *out_m = (int64_t)h.count;
     } while (0);
-    if (synced) dev_free_idle(sc, s);
-    else dev_free(sc, s);
+    dev_free(sc, s);
     return status;
 }
 
@@ -531,7 +533,6 @@ static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, 
     uint32_t *tot = (uint32_t *)(sc + o_tot);
     DevStatus *st = (DevStatus *)(sc + o_st);
     int status = SUBMCONV_OK;
-    bool synced = false;  // the status read has synchronised the stream
     do {
         if (hipMemsetAsync(st, 0, sizeof(DevStatus), s) != hipSuccess) { status = fail(SUBMCONV_E_HIP, "status clear failed"); break; }
         const unsigned grid = (unsigned)((n + 255) / 256);
@@ -559,17 +560,18 @@ static int s2d_impl(const int32_t *coords, const void *feats, int64_t n, int c, 
                 hipLaunchKernelGGL((k_down_reduce<T, false>), dim3(cg_grid(total)), dim3(256), 0,
                                    s, va, seg, start, tot, n, c, (const T *)feats, (T *)out_feats);
         }
-        hipLaunchKernelGGL(k_store_count, dim3(1), dim3(1), 0, s, tot, st);
+        Mailbox *mb = nullptr;
+        uint32_t seq = 0;
+        if ((status = mailbox_acquire(&mb, &seq)) != SUBMCONV_OK) break;
+        hipLaunchKernelGGL(k_post_count, dim3(1), dim3(1), 0, s, (const uint32_t *)tot, (const DevStatus *)st, mb, seq);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in %s failed", op == COARSE_S2D ? "space_to_depth" : "downsample"); break; }
         DevStatus h;
-        if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
-        synced = true;
+        if ((status = mailbox_wait(mb, seq, &h, s)) != SUBMCONV_OK) break;
         if (h.flags & FLAG_RANGE) status = fail(SUBMCONV_E_COORD_RANGE, "a coordinate is outside [0,res) or its batch index outside [0,batch)");
         else if (h.flags & FLAG_DUPLICATE) status = fail(SUBMCONV_E_DUPLICATE, "the coordinate set holds a duplicate row");
         else *out_m = (int64_t)h.count;
     } while (0);
-    if (synced) dev_free_idle(sc, s);
-    else dev_free(sc, s);
+    dev_free(sc, s);
     return status;
 }
 
@@ -795,21 +797,21 @@ static int expand(const int32_t *cc, const void *cf, const uint8_t *mask, int64_
     const ExpandScratch L(m);
     char *sc = nullptr;
     SC_CHECK(dev_alloc((void **)&sc, L.bytes, s));
-    DevStatus *st = (DevStatus *)(sc + L.st);
     int status = SUBMCONV_OK;
-    bool synced = false;  // the status read has synchronised the stream
     do {
         if ((status = expand_masked_enqueue<REPL>(cc, cf, mask, m, c, dtype, out_coords, out_feats, sc, s)) !=
             SUBMCONV_OK) break;
-        hipLaunchKernelGGL(k_store_count, dim3(1), dim3(1), 0, s, (const uint32_t *)(sc + L.tot), st);
+        Mailbox *mb = nullptr;
+        uint32_t seq = 0;
+        if ((status = mailbox_acquire(&mb, &seq)) != SUBMCONV_OK) break;
+        hipLaunchKernelGGL(k_post_count, dim3(1), dim3(1), 0, s, (const uint32_t *)(sc + L.tot), (const DevStatus *)nullptr,
+                           mb, seq);
         if (hipGetLastError() != hipSuccess) { status = fail(SUBMCONV_E_HIP, "launch in a masked expansion failed"); break; }
         DevStatus h;
-        if ((status = read_status(st, &h, s)) != SUBMCONV_OK) break;
-        synced = true;
+        if ((status = mailbox_wait(mb, seq, &h, s)) != SUBMCONV_OK) break;
         *out_n = (int64_t)h.count;
     } while (0);
-    if (synced) dev_free_idle(sc, s);
-    else dev_free(sc, s);
+    dev_free(sc, s);
     return status;
 }
 

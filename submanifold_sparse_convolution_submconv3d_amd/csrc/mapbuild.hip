@@ -49,6 +49,7 @@
 // before packing and every neighbour coordinate is bounds-checked before its key
 // is formed, so a key never wraps into the next row, plane or batch entry.
 #include "common.h"
+#include "mailbox.h"
 #include "winplan.h"
 
 namespace sc {
@@ -534,17 +535,6 @@ __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, 
     if (tid == 0) blk_taps[blk] = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
 }
 
-// The status into the host's pinned mailbox, `seq` last (one thread): a system-scope
-// release first, so the host sees the status only after every write before it.
-__device__ __forceinline__ void mailbox_post(Mailbox *mb, uint32_t seq, uint32_t flags, unsigned long long taps,
-                                             unsigned long long count)
-{
-    mb->flags = flags;
-    mb->taps = taps;
-    mb->count = count;
-    __threadfence_system();
-    __hip_atomic_store(&mb->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-}
 
 // The build's status and the sum of the resolve blocks' present counts, posted to the
 // host's mailbox by one block after the resolve has ended (so every write of the build

@@ -656,15 +656,18 @@ def test_space_to_depth_and_back(dtype, n, res, batch, ch):
     np.testing.assert_array_equal(to_f64(af), eaf)
 
 
-def test_space_to_depth_errors():
-    note("s2d errors")
-    c = np.array([[0, 1, 1, 1], [0, 1, 1, 1]], np.int32)
-    f = torch.zeros((2, 4), device=DEV)
+@pytest.mark.parametrize("res", [4, 2048])
+def test_space_to_depth_errors(res):
+    """A duplicate row and an out-of-range row are reported on both groupings: the coarse
+    bitmap (res 4) and the sort (res 2048, a sparse coarse key space)."""
+    note("s2d errors res=%d" % res)
+    c = np.array([[0, 1, 1, 1], [0, 3, 2, 1], [0, 1, 1, 1]], np.int32)
+    f = torch.zeros((3, 4), device=DEV)
     with pytest.raises(sc.SubmconvError) as e:
-        sc.submconv_space_to_depth(coords_dev(c), f, 4, 1)
+        sc.submconv_space_to_depth(coords_dev(c), f, res, 1)
     assert e.value.status == -3
     with pytest.raises(sc.SubmconvError) as e:
-        sc.submconv_space_to_depth(coords_dev(np.array([[0, 9, 1, 1]], np.int32)), f[:1], 4, 1)
+        sc.submconv_space_to_depth(coords_dev(np.array([[0, 1, 1, 1], [0, res, 1, 1]], np.int32)), f[:2], res, 1)
     assert e.value.status == -2
 
 
@@ -712,14 +715,18 @@ def test_downsample(dtype, mode, n, res, batch, c):
         assert_close(to_f64(gf), ef, dtype, "downsample mean")
 
 
-def test_downsample_errors():
-    note("downsample errors")
-    f = torch.zeros((2, 4), device=DEV)
+@pytest.mark.parametrize("res", [4, 2048])
+def test_downsample_errors(res):
+    """As for space-to-depth: errors on the bitmap (res 4) and the sort (res 2048) groupings."""
+    note("downsample errors res=%d" % res)
+    f = torch.zeros((3, 4), device=DEV)
     with pytest.raises(sc.SubmconvError) as e:
-        sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1], [0, 1, 1, 1]], np.int32)), f, 4, 1, "max")
+        sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1], [0, 2, 3, 1], [0, 1, 1, 1]], np.int32)), f, res, 1,
+                               "max")
     assert e.value.status == -3
     with pytest.raises(sc.SubmconvError) as e:
-        sc.submconv_downsample(coords_dev(np.array([[0, 9, 1, 1]], np.int32)), f[:1], 4, 1, "mean")
+        sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1], [0, 1, res + 5, 1]], np.int32)), f[:2], res, 1,
+                               "mean")
     assert e.value.status == -2
     with pytest.raises(ValueError):
         sc.submconv_downsample(coords_dev(np.array([[0, 1, 1, 1]], np.int32)), f[:1], 4, 1, "sum")
