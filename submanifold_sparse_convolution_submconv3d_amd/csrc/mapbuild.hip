@@ -1022,7 +1022,7 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
     const unsigned grid = (unsigned)((n + 255) / 256);
     do {
         // one launch clears the status block and (dense path) the bitmap and the scan's flags;
-        // the single-block builds write their status block whole
+        // the single-block builds need no clearing (they post their status themselves)
         const int64_t clear_words = path == 2 ? words + 1 : 0;
         if (path >= 2)
             hipLaunchKernelGGL(k_clear, dim3((unsigned)(clear_words > 0 ? (clear_words + 4095) / 4096 : 1)), dim3(256),
