@@ -535,7 +535,6 @@ __global__ __launch_bounds__(256) void k_resolve_plan(const K *__restrict__ sk, 
     if (tid == 0) blk_taps[blk] = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
 }
 
-
 // The build's status and the sum of the resolve blocks' present counts, posted to the
 // host's mailbox by one block after the resolve has ended (so every write of the build
 // is visible device-wide when the host sees the post).  Counting the blocks inside the
@@ -681,7 +680,6 @@ __global__ __launch_bounds__(256) void k_resolve_win(const K *__restrict__ sk, i
 // ---------------------------------------------------------------------------
 // small sets: one block
 // ---------------------------------------------------------------------------
-
 
 // End of a single-block build (every thread calls it, rows of all n sorted voxels in
 // s_rows): the rows go out as one run, the group windows are formed per 32 sorted
@@ -1011,10 +1009,10 @@ static int build_map_impl(const int32_t *coords, submconv_rulebook *rb, hipStrea
         o_vals = off; off += up((size_t)n * 4);
         o_aux = off; off += up(sort_scratch_bytes(n));
     }
-    char *scratch = nullptr;
-    SC_CHECK(dev_alloc((void **)&scratch, off, stream));
+    char *scratch = nullptr;  // none for the single-block builds
+    if (path >= 2) SC_CHECK(dev_alloc((void **)&scratch, off, stream));
     DevStatus *st = (DevStatus *)scratch;
-    uint32_t *blk_taps = (uint32_t *)(scratch + sizeof(DevStatus));
+    uint32_t *blk_taps = scratch ? (uint32_t *)(scratch + sizeof(DevStatus)) : nullptr;
     int status = SUBMCONV_OK;
     bool synced = false;  // the status read has synchronised the stream
     Mailbox *mb = nullptr;
