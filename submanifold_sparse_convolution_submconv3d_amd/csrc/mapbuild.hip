@@ -797,16 +797,24 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
         perm_out[s] = i;
         const int x = (int)(key[q] & m), y = (int)((key[q] >> rb) & m), z = (int)((key[q] >> (2 * rb)) & m);
         const K bpart = (key[q] >> (3 * rb)) << (3 * rb);
+        // the 27 lookups without branches: every word and prefix is read (at key 0 for a
+        // neighbour off the grid, which is then masked), all reads issued together
         int32_t p[27];
+        uint32_t word[27], pre[27], bit[27];
+        bool on[27];
 #pragma unroll
         for (int k = 0; k < 27; ++k) {
             const int nz = z + k / 9 - 1, ny = y + (k / 3) % 3 - 1, nx = x + k % 3 - 1;
-            int32_t r = -1;
-            if (nz >= 0 && nz < res && ny >= 0 && ny < res && nx >= 0 && nx < res) {
-                const K t = bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)nx;
-                const uint32_t word = s_bm[t >> 5], b = (uint32_t)(t & 31);
-                if ((word >> b) & 1u) r = (int32_t)(s_pre[t >> 5] + __popc(word & ((1u << b) - 1u)));
-            }
+            on[k] = nz >= 0 && nz < res && ny >= 0 && ny < res && nx >= 0 && nx < res;
+            const K t = on[k] ? (bpart | ((K)nz << (2 * rb)) | ((K)ny << rb) | (K)nx) : K(0);
+            bit[k] = (uint32_t)(t & 31);
+            word[k] = s_bm[t >> 5];
+            pre[k] = s_pre[t >> 5];
+        }
+#pragma unroll
+        for (int k = 0; k < 27; ++k) {
+            const bool hit = on[k] && ((word[k] >> bit[k]) & 1u);
+            const int32_t r = hit ? (int32_t)(pre[k] + __popc(word[k] & ((1u << bit[k]) - 1u))) : -1;
             present += r >= 0;
             p[k] = r;
         }
