@@ -776,8 +776,9 @@ __global__ __launch_bounds__(1024) void k_build_small_bm(const int4 *__restrict_
         }
         if (lane == 63) s_wave[wave] = x;
         __syncthreads();
-        uint32_t before = 0;
-        for (int w = 0; w < (int)wave; ++w) before += s_wave[w];
+        uint32_t before = 0;  // the totals of the waves before this one (16 reads issued together)
+#pragma unroll
+        for (int w = 0; w < 16; ++w) before += w < (int)wave ? s_wave[w] : 0u;
         const uint32_t ex = x - v + before;
         if (w0 < words) s_pre[w0] = ex;
         if (w0 + 1 < words) s_pre[w0 + 1] = ex + a;
