@@ -540,25 +540,30 @@ def test_rulebook_cache_rebuilds_for_another_set_of_the_same_size():
     cache.clear()
 
 
-def test_builds_on_two_host_threads():
-    """Dense-path builds post their status to a mailbox of the calling host thread:
-    builds running on two threads at once, each on its own stream, return exact
-    tables and their own present counts."""
+def test_builds_on_several_host_threads():
+    """Bitmap-path and single-block builds post their status to a mailbox of the
+    calling host thread: builds running on four threads at once, each on its own
+    stream, return exact tables and their own present counts."""
     import threading
     w2, c2 = synth.workload(2)
     w3, c3 = synth.workload(3)
+    w1, c1 = synth.workload(1)
+    cs = synth.random_coords(1500, 64, 2, 9)   # single block, sort (19 key bits)
     e2 = dense.neighbor_table(c2, w2.res, 1)
     e3 = dense.neighbor_table(c3, w3.res, 1)
-    jobs = {"64^3": (c2, w2.res, e2), "128^3": (c3, w3.res, e3)}
+    e1 = dense.neighbor_table(c1, w1.res, 1)
+    es = dense.neighbor_table(cs, 64, 2)
+    jobs = {"64^3": (c2, w2.res, 1, e2), "128^3": (c3, w3.res, 1, e3), "16^3": (c1, w1.res, 1, e1),
+            "small sort": (cs, 64, 2, es)}
     got = {}
 
     def work(name):
-        c, res, e = jobs[name]
+        c, res, batch, e = jobs[name]
         s = torch.cuda.Stream()
         ok = True
         with torch.cuda.stream(s):
             for it in range(6):
-                rb = sc.submconv_build_map(coords_dev(c), res, 1)
+                rb = sc.submconv_build_map(coords_dev(c), res, batch)
                 table = rb.neighbors()
                 s.synchronize()
                 ok = ok and np.array_equal(table.cpu().numpy(), e) and rb.taps_present == int((e >= 0).sum())
@@ -566,7 +571,7 @@ def test_builds_on_two_host_threads():
         s.synchronize()
         got[name] = ok
 
-    note("builds on two host threads")
+    note("builds on four host threads")
     threads = [threading.Thread(target=work, args=(name,)) for name in jobs]
     for t in threads:
         t.start()
